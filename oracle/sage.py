@@ -1,0 +1,442 @@
+"""SageBwd INT8 attention, step by step, on the CPU.
+
+TEST INFRASTRUCTURE ONLY (see oracle/__init__.py): the tests, the smoke check
+and the benchmark's CPU-baseline leg may call this; the GPU library never does.
+
+What is computed, and where the pages define it
+-----------------------------------------------
+* SageBwd paper summary (paper.rainbus.top, "method step details"): the
+  forward steps (1)-(5) and backward steps (1)-(7) that this module follows
+  in order; K-smoothing on and Q-smoothing off by default.
+* SageBwd paper summary, prerequisites "INT8 quantisation": scale
+  delta_X = max|X| / 127 and codes round(X / delta_X); per-block granularity
+  aligned with the FlashAttention tiles.
+* SageAttention3 write-up, Eq. 1 (online softmax: running max m and running
+  sum l, initialised to -inf and 0, rescaled by exp(m_old - m_new)), Eq. 7
+  (INT8 per-block quantisation), Eq. 8 (INT8 logits and the per-token P scale
+  s_P = exp(rowmax(S_ij) - m_ij) / 127) and Eq. 9 with its INT8 backward
+  updates (dV, dP kept in 16-bit, dS = P o (dP - D), dQ, dK).
+* SageBwd paper summary, prerequisites "K-smoothing and Q-smoothing", and
+  paperlayer section 6: K is centred by its token mean at kernel entry with no
+  backward change; Q is centred per query block, the low-rank term
+  mu_Qi K^T is added to the logits in high precision and dK gains the bias
+  (dS^T 1) mu_Q^T.
+
+Numeric model (the readings taken where the pages leave a choice open)
+----------------------------------------------------------------------
+* Everything is float64 except where a value is stored by the method or
+  decides an integer code; there the kernel's precision, IEEE float32 with
+  round-to-nearest-even, is used:
+    - mu_K = f32(sum_n K[n] / N) (sum in float64); K_sm = f32(K - mu_K);
+      the same per query block for mu_Q and Q_sm;
+    - a block's scale s = f32(max|X| / 127) (correctly rounded float32
+      division), codes = clamp(rint(f32(X / s)), -127, 127), rint being
+      round-half-to-even; a block whose max is 0 gets s = 0 and zero codes;
+    - the forward P codes: s_P = f32(f32(exp(rm - m_new)) / 127) and
+      codes = clamp(rint(f32(f32(P~) / s_P)), 0, 127); a row with no visible
+      key in the tile gets s_P = 0 and zero codes;
+    - the backward P and dS codes: one scale per (query block, key block)
+      tile, computed as above from f32(P) and f32(dS);
+    - stored outputs: O rounded to the I/O dtype, L and delta to float32.
+* The logits carry the 1/sqrt(D) softmax scale (S = Q K^T / sqrt(d), as the
+  prerequisites state); by the chain rule dQ and dK are multiplied by it.
+* The running sum l adds the unquantised P~ (Eq. 1); the quantised codes only
+  feed the P V product.
+* L is the logsumexp of the logits the method forms, i.e. with K-smoothing
+  of Q (K - mu_K)^T * scale; it differs from the unsmoothed logsumexp by
+  -scale * q . mu_K per row, while O is unchanged.  The backward recomputes
+  P = exp(S - L) from the same smoothed logits.
+* Causal masking is top-left aligned (key n visible to query r iff n <= r);
+  tiles whose keys all lie after the block's last query are skipped.
+* delta = rowsum(dO o O) uses the stored (rounded) O.
+* dP = dO V^T uses the 16-bit input values exactly, summed in float64.
+
+Quantisation-off mode (quant=False): every quantise/dequantise pair becomes
+the identity (codes = values, scales = 1), nothing is rounded, and the result
+must equal full-precision attention (oracle.fpa) to float64 rounding.
+
+Tensors are per head, [N, D], as float arrays holding the exact input values.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, Iterable, Optional
+
+import numpy as np
+
+F32 = np.float32
+F64 = np.float64
+
+
+def r32(x):
+    """Round to IEEE float32 (round-to-nearest-even) and return as float64."""
+    return np.asarray(x, dtype=F64).astype(F32).astype(F64)
+
+
+def round_io(x, dtype: int):
+    """Round float64 values to the I/O dtype (0 = fp16, 1 = bf16) with
+    round-to-nearest-even, directly from float64 (no intermediate float32)."""
+    x = np.asarray(x, dtype=F64)
+    sig_bits, min_q, max_finite = (8, -133, 3.3895313892515355e38) if dtype == 1 else (11, -24, 65504.0)
+    out = np.zeros_like(x)
+    nz = x != 0
+    _, e = np.frexp(x[nz])                       # x = m * 2^e, 0.5 <= |m| < 1
+    q = np.maximum(e - sig_bits, min_q).astype(F64)
+    step = np.exp2(q)
+    out[nz] = np.rint(x[nz] / step) * step       # exact scaling by powers of two
+    big = np.abs(out) > max_finite
+    out[big] = np.sign(out[big]) * np.inf
+    return out
+
+
+@dataclasses.dataclass
+class Shape:
+    """The switches of one call: quantisation blocks and method options."""
+
+    N: int
+    D: int
+    bq: int
+    bkv: int
+    causal: bool = False
+    k_smooth: bool = True
+    q_smooth: bool = False
+    dtype: int = 1
+    sm_scale: Optional[float] = None
+
+    @property
+    def scale(self) -> float:
+        return float(1.0 / np.sqrt(self.D)) if self.sm_scale is None else float(self.sm_scale)
+
+    @property
+    def Tm(self) -> int:
+        return self.N // self.bq
+
+    @property
+    def Tn(self) -> int:
+        return self.N // self.bkv
+
+    @staticmethod
+    def of(cfg) -> "Shape":
+        """Build from a workload description (anything with the same fields)."""
+        return Shape(N=cfg.N, D=cfg.D, bq=cfg.bq, bkv=cfg.bkv, causal=bool(cfg.causal),
+                     k_smooth=bool(cfg.k_smooth), q_smooth=bool(cfg.q_smooth), dtype=int(cfg.dtype))
+
+
+# ---------------------------------------------------------------------------
+# Per-block INT8 quantisation (prerequisites "INT8 quantisation"; SA3 Eq. 7)
+# ---------------------------------------------------------------------------
+
+def quantize_block(X, quant=True):
+    """delta = max|X| / 127, codes = round(X / delta).
+
+    X holds float32-representable values.  Returns (codes as float64 integer
+    values, scale).  Quantisation off: (X, 1.0)."""
+    X = np.asarray(X, dtype=F64)
+    if not quant:
+        return X.copy(), 1.0
+    x32 = X.astype(F32)
+    a = np.max(np.abs(x32)) if x32.size else F32(0)
+    if a == 0:
+        return np.zeros_like(X), 0.0
+    s = F32(a) / F32(127)                          # float32 / float32: correctly rounded
+    codes = np.clip(np.rint(x32 / s), -127, 127)   # float32 division, then half-even rint
+    return codes.astype(F64), float(s)
+
+
+@dataclasses.dataclass
+class Quantized:
+    """Result of the preprocessing step for one head."""
+
+    Qc: np.ndarray      # [N, D] codes of Q_sm (integer-valued float64; values when quant off)
+    sQ: np.ndarray      # [Tm]
+    Kc: np.ndarray      # [N, D]
+    sK: np.ndarray      # [Tn]
+    Vc: np.ndarray      # [N, D]
+    sV: np.ndarray      # [Tn]
+    mu_k: np.ndarray    # [D]  (zeros when K-smoothing is off)
+    mu_q: np.ndarray    # [Tm, D] (zeros when Q-smoothing is off)
+    K_sm: np.ndarray    # [N, D] smoothed, unquantised K (for the Q-smoothing bias)
+
+
+def quantize(Q, K, V, sh: Shape, quant=True) -> Quantized:
+    """Forward steps (1)-(2): smoothing, then per-block quantisation of
+    Q (bq-row blocks), K and V (bkv-row blocks)."""
+    Q, K, V = (np.asarray(a, dtype=F64) for a in (Q, K, V))
+    N, D = Q.shape
+    rnd = r32 if quant else (lambda x: np.asarray(x, dtype=F64))
+
+    # K-smoothing: subtract the mean over all N tokens of the head.
+    if sh.k_smooth:
+        mu_k = rnd(np.sum(K, axis=0) / N)
+        K_sm = rnd(K - mu_k[None, :])
+    else:
+        mu_k = np.zeros(D)
+        K_sm = K.copy()
+
+    # Q-smoothing: subtract the mean of each bq-row query block.
+    mu_q = np.zeros((sh.Tm, D))
+    Q_sm = Q.copy()
+    if sh.q_smooth:
+        for i in range(sh.Tm):
+            rows = slice(i * sh.bq, (i + 1) * sh.bq)
+            mu_q[i] = rnd(np.sum(Q[rows], axis=0) / sh.bq)
+            Q_sm[rows] = rnd(Q[rows] - mu_q[i][None, :])
+
+    Qc = np.zeros((N, D)); sQ = np.zeros(sh.Tm)
+    Kc = np.zeros((N, D)); sK = np.zeros(sh.Tn)
+    Vc = np.zeros((N, D)); sV = np.zeros(sh.Tn)
+    for i in range(sh.Tm):
+        rows = slice(i * sh.bq, (i + 1) * sh.bq)
+        Qc[rows], sQ[i] = quantize_block(Q_sm[rows], quant)
+    for j in range(sh.Tn):
+        rows = slice(j * sh.bkv, (j + 1) * sh.bkv)
+        Kc[rows], sK[j] = quantize_block(K_sm[rows], quant)
+        Vc[rows], sV[j] = quantize_block(V[rows], quant)
+    return Quantized(Qc, sQ, Kc, sK, Vc, sV, mu_k, mu_q, K_sm)
+
+
+# ---------------------------------------------------------------------------
+# Tiles and logits (forward step (3); SA3 Eq. 8)
+# ---------------------------------------------------------------------------
+
+def tile_visible(i: int, j: int, sh: Shape) -> bool:
+    """False when every key of block j lies after the last query of block i."""
+    return (not sh.causal) or (j * sh.bkv <= (i + 1) * sh.bq - 1)
+
+
+def tile_mask(i: int, j: int, sh: Shape) -> np.ndarray:
+    """[bq, bkv] True where query (i*bq + r) sees key (j*bkv + n)."""
+    q = i * sh.bq + np.arange(sh.bq)[:, None]
+    k = j * sh.bkv + np.arange(sh.bkv)[None, :]
+    return np.ones((sh.bq, sh.bkv), bool) if not sh.causal else (k <= q)
+
+
+def qsmooth_bias(qz: Quantized, i: int, j: int, sh: Shape) -> np.ndarray:
+    """scale * mu_Qi K_sm,j^T, the low-rank logit term Q-smoothing moves out of
+    the INT8 product, kept in float64 ([bkv] row vector shared by the block)."""
+    keys = slice(j * sh.bkv, (j + 1) * sh.bkv)
+    return sh.scale * (qz.K_sm[keys] @ qz.mu_q[i])
+
+
+def logits(qz: Quantized, i: int, j: int, sh: Shape) -> np.ndarray:
+    """S_ij = M(Q^_i, K^_j) * s_Q * s_K * scale (+ Q-smoothing bias), masked
+    entries set to -inf."""
+    rows = slice(i * sh.bq, (i + 1) * sh.bq)
+    keys = slice(j * sh.bkv, (j + 1) * sh.bkv)
+    A = qz.Qc[rows] @ qz.Kc[keys].T                       # exact integer sums
+    S = A * (qz.sQ[i] * qz.sK[j] * sh.scale)
+    if sh.q_smooth:
+        S = S + qsmooth_bias(qz, i, j, sh)[None, :]
+    return np.where(tile_mask(i, j, sh), S, -np.inf)
+
+
+def _exp_shift(S, m):
+    """exp(S - m) row-wise with exp(-inf - anything) = 0 (no NaN for m = -inf)."""
+    with np.errstate(invalid="ignore"):
+        E = np.exp(S - m[:, None])
+    return np.where(np.isneginf(S), 0.0, E)
+
+
+def per_token_p_quant(P_tilde, rm, m_new, quant=True):
+    """Forward step (4), SA3 Eq. 8: s_P = exp(rowmax(S_ij) - m_ij) / 127,
+    P^_ij = P~_ij / s_P, rounded to integers in [0, 127]."""
+    if not quant:
+        return np.ones(P_tilde.shape[0]), P_tilde.copy()
+    with np.errstate(invalid="ignore"):
+        ex = np.where(np.isneginf(rm), 0.0, np.exp(rm - m_new))
+    sP = (np.asarray(ex).astype(F32) / F32(127)).astype(F32)   # float32 division
+    codes = np.zeros_like(P_tilde)
+    live = sP > 0
+    p32 = P_tilde[live].astype(F32)
+    codes[live] = np.clip(np.rint(p32 / sP[live][:, None]), 0, 127)
+    return sP.astype(F64), codes
+
+
+# ---------------------------------------------------------------------------
+# Forward (forward steps (3)-(5); SA3 Eq. 1 and Eq. 8)
+# ---------------------------------------------------------------------------
+
+def forward(qz: Quantized, sh: Shape, quant=True, q_blocks: Optional[Iterable[int]] = None):
+    """Online-softmax INT8 forward.  Returns (O [N, D], L [N]); rows of query
+    blocks not in ``q_blocks`` are left as NaN.  O is rounded to the I/O dtype
+    and L (natural-log logsumexp) to float32 when quant is on."""
+    N, D = qz.Qc.shape
+    O = np.full((N, D), np.nan)
+    L = np.full(N, np.nan)
+    blocks = range(sh.Tm) if q_blocks is None else q_blocks
+    for i in blocks:
+        rows = slice(i * sh.bq, (i + 1) * sh.bq)
+        m = np.full(sh.bq, -np.inf)
+        l = np.zeros(sh.bq)
+        acc = np.zeros((sh.bq, D))
+        for j in range(sh.Tn):
+            if not tile_visible(i, j, sh):
+                continue
+            keys = slice(j * sh.bkv, (j + 1) * sh.bkv)
+            S = logits(qz, i, j, sh)
+            rm = S.max(axis=1)
+            m_new = np.maximum(m, rm)
+            P_tilde = _exp_shift(S, m_new)
+            sP, P_hat = per_token_p_quant(P_tilde, rm, m_new, quant)
+            with np.errstate(invalid="ignore"):
+                alpha = np.where(np.isneginf(m), 0.0, np.exp(m - m_new))
+            l = alpha * l + P_tilde.sum(axis=1)
+            acc = alpha[:, None] * acc + (P_hat @ qz.Vc[keys]) * (sP[:, None] * qz.sV[j])
+            m = m_new
+        O[rows] = acc / l[:, None]
+        L[rows] = m + np.log(l)
+    if quant:
+        done = ~np.isnan(L)
+        O[done] = round_io(O[done], sh.dtype)
+        L[done] = r32(L[done])
+    return O, L
+
+
+def forward_two_pass(qz: Quantized, sh: Shape, quant=True):
+    """The same forward written without the streaming recurrence: the running
+    max after tile j is the prefix maximum of the tile row maxima, and every
+    tile is rescaled straight to the final row maximum.  Used only to check the
+    online recurrence (Eq. 1) of :func:`forward`."""
+    N, D = qz.Qc.shape
+    O = np.zeros((N, D)); L = np.zeros(N)
+    for i in range(sh.Tm):
+        rows = slice(i * sh.bq, (i + 1) * sh.bq)
+        tiles = [j for j in range(sh.Tn) if tile_visible(i, j, sh)]
+        S_all = [logits(qz, i, j, sh) for j in tiles]
+        rms = np.stack([S.max(axis=1) for S in S_all])            # [tiles, bq]
+        prefix = np.maximum.accumulate(rms, axis=0)
+        M = prefix[-1]
+        num = np.zeros((sh.bq, D)); den = np.zeros(sh.bq)
+        for t, j in enumerate(tiles):
+            keys = slice(j * sh.bkv, (j + 1) * sh.bkv)
+            P_tilde = _exp_shift(S_all[t], prefix[t])
+            sP, P_hat = per_token_p_quant(P_tilde, rms[t], prefix[t], quant)
+            to_final = np.exp(prefix[t] - M)
+            num += to_final[:, None] * ((P_hat @ qz.Vc[keys]) * (sP[:, None] * qz.sV[j]))
+            den += to_final * P_tilde.sum(axis=1)
+        O[rows] = num / den[:, None]
+        L[rows] = M + np.log(den)
+    if quant:
+        O = round_io(O, sh.dtype)
+        L = r32(L)
+    return O, L
+
+
+# ---------------------------------------------------------------------------
+# Backward pre-pass (backward step (1))
+# ---------------------------------------------------------------------------
+
+def backward_pre(O, dO, sh: Shape, quant=True):
+    """D_i = rowsum(dO o O) over the stored O, and the per-block (bq rows)
+    INT8 quantisation of dO.  Returns (delta [N], dOc [N, D], sdO [Tm])."""
+    O, dO = np.asarray(O, dtype=F64), np.asarray(dO, dtype=F64)
+    delta = np.sum(dO * O, axis=1)
+    if quant:
+        delta = r32(delta)
+    dOc = np.zeros_like(dO); sdO = np.zeros(sh.Tm)
+    for i in range(sh.Tm):
+        rows = slice(i * sh.bq, (i + 1) * sh.bq)
+        dOc[rows], sdO[i] = quantize_block(dO[rows], quant)
+    return delta, dOc, sdO
+
+
+# ---------------------------------------------------------------------------
+# Backward (backward steps (2)-(7); SA3 Eq. 9 INT8 updates)
+# ---------------------------------------------------------------------------
+
+def backward_tile(qz: Quantized, V, dO, dOc, sdO, L, delta, i: int, j: int, sh: Shape, quant=True):
+    """All contributions of tile (i, j).  Returns a dict with the tile's
+    dV_j, dK_j, dKbias_j, dQ_i terms and the intermediates P, dP, dS."""
+    rows = slice(i * sh.bq, (i + 1) * sh.bq)
+    keys = slice(j * sh.bkv, (j + 1) * sh.bkv)
+    # (2) recompute S_ij and P_ij = exp(S_ij - L_i)
+    S = logits(qz, i, j, sh)
+    P = _exp_shift(S, L[rows])
+    # (3) dV_j += M(P^_ij^T, dO^_i) * s_P * s_dO, P quantised per tile
+    P_hat, sPb = quantize_block(P, quant)
+    dV = (P_hat.T @ dOc[rows]) * (sPb * sdO[i])
+    # (4) dP_ij = dO_i V_j^T from the 16-bit values, no quantisation
+    dP = dO[rows] @ V[keys].T
+    # (5) dS_ij = P_ij o (dP_ij - D_i), then per-tile INT8 quantisation
+    dS = P * (dP - delta[rows][:, None])
+    dS_hat, sdS = quantize_block(dS, quant)
+    # (6) dQ_i += M(dS^_ij, K^_j) * s_dS * s_K
+    dQ = (dS_hat @ qz.Kc[keys]) * (sdS * qz.sK[j])
+    # (7) dK_j += M(dS^_ij^T, Q^_i) * s_dS * s_Q
+    dK = (dS_hat.T @ qz.Qc[rows]) * (sdS * qz.sQ[i])
+    # Q-smoothing bias gradient: (dS^T 1) mu_Qi^T from the unquantised dS
+    dKb = np.outer(dS.sum(axis=0), qz.mu_q[i]) if sh.q_smooth else np.zeros_like(dK)
+    return {"dV": dV, "dK": dK, "dKb": dKb, "dQ": dQ, "P": P, "dP": dP, "dS": dS,
+            "sPb": sPb, "sdS": sdS, "P_hat": P_hat, "dS_hat": dS_hat}
+
+
+def backward(qz: Quantized, V, dO, dOc, sdO, L, delta, sh: Shape, quant=True,
+             kv_blocks: Optional[Iterable[int]] = None, q_blocks: Optional[Iterable[int]] = None):
+    """KV blocks outer, query blocks inner (paperlayer A.1).  Returns (dQ, dK,
+    dV) as float64 [N, D]: dK/dV rows only for ``kv_blocks`` and dQ rows only
+    for ``q_blocks`` (NaN elsewhere; None = all).  dQ and dK carry the softmax
+    scale; dK includes the Q-smoothing bias term."""
+    V, dO = np.asarray(V, dtype=F64), np.asarray(dO, dtype=F64)
+    N, D = V.shape
+    kv_sel = set(range(sh.Tn) if kv_blocks is None else kv_blocks)
+    q_sel = set(range(sh.Tm) if q_blocks is None else q_blocks)
+    dQ = np.full((N, D), np.nan); dK = np.full((N, D), np.nan); dV = np.full((N, D), np.nan)
+    for i in q_sel:
+        dQ[i * sh.bq:(i + 1) * sh.bq] = 0.0
+    for j in kv_sel:
+        dK[j * sh.bkv:(j + 1) * sh.bkv] = 0.0
+        dV[j * sh.bkv:(j + 1) * sh.bkv] = 0.0
+    for j in range(sh.Tn):
+        for i in range(sh.Tm):
+            if not tile_visible(i, j, sh) or (j not in kv_sel and i not in q_sel):
+                continue
+            t = backward_tile(qz, V, dO, dOc, sdO, L, delta, i, j, sh, quant)
+            if j in kv_sel:
+                keys = slice(j * sh.bkv, (j + 1) * sh.bkv)
+                dV[keys] += t["dV"]
+                dK[keys] += t["dK"] + t["dKb"]
+            if i in q_sel:
+                dQ[i * sh.bq:(i + 1) * sh.bq] += t["dQ"]
+    return dQ * sh.scale, dK * sh.scale, dV
+
+
+# ---------------------------------------------------------------------------
+# Whole pass over all heads
+# ---------------------------------------------------------------------------
+
+def run_head(Q, K, V, dO, sh: Shape, quant=True) -> Dict[str, np.ndarray]:
+    """quantise -> forward -> backward pre-pass -> backward for one head."""
+    qz = quantize(Q, K, V, sh, quant)
+    O, L = forward(qz, sh, quant)
+    delta, dOc, sdO = backward_pre(O, dO, sh, quant)
+    dQ, dK, dV = backward(qz, V, dO, dOc, sdO, L, delta, sh, quant)
+    return {"qz": qz, "O": O, "L": L, "delta": delta, "dOc": dOc, "sdO": sdO,
+            "dQ": dQ, "dK": dK, "dV": dV}
+
+
+def run(inputs: Dict[str, np.ndarray], sh: Shape, quant=True) -> Dict[str, np.ndarray]:
+    """All heads of [B, H, N, D] float inputs ``q``, ``k``, ``v``, ``do``.
+    Returns stacked outputs; codes as int8, scales and means as float32 when
+    quant is on."""
+    Q, K, V, dO = (np.asarray(inputs[n], dtype=F64) for n in ("q", "k", "v", "do"))
+    B, H, N, D = Q.shape
+    names = ["Qc", "sQ", "Kc", "sK", "Vc", "sV", "mu_k", "mu_q", "O", "L", "delta", "dOc", "sdO",
+             "dQ", "dK", "dV"]
+    out = {n: [] for n in names}
+    for b in range(B):
+        for h in range(H):
+            r = run_head(Q[b, h], K[b, h], V[b, h], dO[b, h], sh, quant)
+            qz = r["qz"]
+            for n in ("Qc", "sQ", "Kc", "sK", "Vc", "sV", "mu_k", "mu_q"):
+                out[n].append(getattr(qz, n))
+            for n in ("O", "L", "delta", "dOc", "sdO", "dQ", "dK", "dV"):
+                out[n].append(r[n])
+    res = {}
+    for n, vals in out.items():
+        a = np.stack(vals).reshape((B, H) + np.shape(vals[0]))
+        if quant and n in ("Qc", "Kc", "Vc", "dOc"):
+            a = a.astype(np.int8)
+        elif quant and n in ("sQ", "sK", "sV", "mu_k", "mu_q", "L", "delta", "sdO"):
+            a = a.astype(F32)
+        res[n] = a
+    return res

@@ -1,0 +1,101 @@
+"""Plant plausible mistakes in a copy of the oracle and check the pins catch them.
+
+Each mutation edits one line of oracle/sage.py's source text, loads the edited
+copy as a separate module, swaps its functions into ``oracle.sage`` for the
+duration of the test, and runs a few pins, at least one of which must fail.
+Nothing here touches a GPU.
+"""
+import inspect
+import sys
+import types
+
+import numpy as np
+import pytest
+
+import oracle.sage as sage_mod
+from tests import test_oracle_bwd as tb
+from tests import test_oracle_fwd as tf
+from tests import test_oracle_quant as tq
+
+SRC = inspect.getsource(sage_mod)
+
+MUTATIONS = {
+    "drop_qsmooth_bias": ("S = S + qsmooth_bias(qz, i, j, sh)[None, :]", "S = S"),
+    "no_alpha_rescale": ("acc = alpha[:, None] * acc + ", "acc = acc + "),
+    "l_without_alpha": ("l = alpha * l + P_tilde.sum(axis=1)", "l = l + P_tilde.sum(axis=1)"),
+    "ds_sign": ("dS = P * (dP - delta[rows][:, None])", "dS = P * (delta[rows][:, None] - dP)"),
+    "dk_transposed": ("dK = (dS_hat.T @ qz.Qc[rows])", "dK = (dS_hat @ qz.Qc[rows])"),
+    "dq_wrong_scale_index": ("(sdS * qz.sK[j])", "(sdS * qz.sK[i])"),
+    "causal_strict": ("else (k <= q)", "else (k < q)"),
+    "missing_dq_scale": ("return dQ * sh.scale, dK * sh.scale, dV", "return dQ, dK * sh.scale, dV"),
+    "round_half_up": ("np.clip(np.rint(x32 / s), -127, 127)", "np.clip(np.floor(x32 / s + 0.5), -127, 127)"),
+    "drop_dk_bias": ("dK[keys] += t[\"dK\"] + t[\"dKb\"]", "dK[keys] += t[\"dK\"]"),
+    "kmean_over_block": ("mu_k = rnd(np.sum(K, axis=0) / N)", "mu_k = rnd(np.sum(K[:sh.bkv], axis=0) / sh.bkv)"),
+    "p_scale_wrong_max": ("np.exp(rm - m_new))", "np.exp(m_new - rm))"),
+    "dv_uses_p_not_codes": ("dV = (P_hat.T @ dOc[rows])", "dV = (P.T @ dOc[rows])"),
+    "lse_log2": ("L[rows] = m + np.log(l)", "L[rows] = m + np.log2(l)"),
+}
+
+
+def _mutated(name):
+    old, new = MUTATIONS[name]
+    assert SRC.count(old) == 1, name
+    return _load("oracle_sage_" + name, SRC.replace(old, new))
+
+
+def _load(modname, text):
+    mod = types.ModuleType(modname)
+    sys.modules[modname] = mod          # dataclasses look the module up by name
+    try:
+        exec(compile(text, "<" + modname + ">", "exec"), mod.__dict__)
+    finally:
+        del sys.modules[modname]
+    return mod
+
+
+PINS = [
+    lambda: [tf.test_quant_off_forward_is_exact_attention(s, c, f) for s in tf.SHAPES[:2]
+             for c in (False, True) for f in ((True, False), (True, True))],
+    lambda: [tb.test_quant_off_backward_is_exact_gradient(c, f, b) for c in (False, True)
+             for f in ((True, False), (True, True)) for b in ((64, 64), (32, 16))],
+    lambda: tf.test_uniform_logits_average_values(True),
+    lambda: tf.test_per_token_scale_is_static_value_at_row_max(),
+    lambda: tf.test_online_recurrence_matches_two_pass(True, True),
+    lambda: tb.test_uniform_probabilities_give_mean_dv(),
+    lambda: tb.test_q_smoothing_quantised_dk_close_to_exact(),
+    lambda: tb.test_q_smoothing_bias_restores_dk(),
+    lambda: [tq.test_quantize_block_golden(c) for c in tq._read_golden()],
+    lambda: tq.test_k_smoothing_centres_columns(),
+    lambda: tf.test_quantised_forward_close_to_exact(),
+    lambda: tf.test_per_token_codes_independent_of_running_max(),
+    lambda: [tb.test_quantised_gradients_with_uneven_block_scales(c) for c in (False, True)],
+]
+
+
+def _catches(mod):
+    saved = {k: getattr(sage_mod, k) for k in dir(sage_mod) if not k.startswith("__")}
+    try:
+        for k in saved:
+            if hasattr(mod, k):
+                setattr(sage_mod, k, getattr(mod, k))
+        caught = []
+        for idx, pin in enumerate(PINS):
+            try:
+                with np.errstate(all="ignore"):
+                    pin()
+            except (AssertionError, ValueError, FloatingPointError):
+                caught.append(idx)
+        return caught
+    finally:
+        for k, v in saved.items():
+            setattr(sage_mod, k, v)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name):
+    assert _catches(_mutated(name)), f"no pin caught the planted mistake {name!r}"
+
+
+def test_unmutated_copy_passes_all_pins():
+    assert _catches(_load("oracle_sage_clean", SRC)) == []
