@@ -1,0 +1,143 @@
+// C ABI of libsage.so: argument checking on the host, then the launches.
+// Every check runs before anything is queued, so a rejected call touches no
+// buffer and no device state, and the error paths run without a GPU.
+#include <cmath>
+#include <cstdint>
+
+#include "sage_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Validates the shape; fills d.  Returns SAGE_OK or an error code.
+int check_shape(const sage_shape* s, sage::Dims& d) {
+    if (s == nullptr) return SAGE_EINVAL;
+    if (s->B < 0 || s->H < 0 || s->N < 0) return SAGE_EINVAL;
+    if (s->causal < 0 || s->causal > 1 || s->k_smooth < 0 || s->k_smooth > 1 || s->q_smooth < 0 ||
+        s->q_smooth > 1)
+        return SAGE_EINVAL;
+    if (!(s->sm_scale >= 0.f) || !std::isfinite(s->sm_scale)) return SAGE_EINVAL;
+    if (s->D != 64 && s->D != 128) return SAGE_EUNSUPPORTED;
+    if (s->bq != 64 && s->bq != 128) return SAGE_EUNSUPPORTED;
+    if (s->bkv != 64) return SAGE_EUNSUPPORTED;
+    if (s->dtype != SAGE_FP16 && s->dtype != SAGE_BF16) return SAGE_EUNSUPPORTED;
+    if (s->N % s->bq != 0 || s->N % s->bkv != 0) return SAGE_EUNSUPPORTED;
+    // in-head offsets are 32-bit (16-bit element count fits), heads go on grid.y
+    if ((int64_t)s->N * s->D * 2 > INT32_MAX) return SAGE_EUNSUPPORTED;
+    if ((int64_t)s->B * s->H > 65535) return SAGE_EUNSUPPORTED;
+    d.B = s->B; d.H = s->H; d.N = s->N; d.D = s->D; d.bq = s->bq; d.bkv = s->bkv;
+    d.bf16 = s->dtype == SAGE_BF16;
+    d.causal = s->causal != 0;
+    d.k_smooth = s->k_smooth != 0;
+    d.q_smooth = s->q_smooth != 0;
+    d.scale = s->sm_scale > 0.f ? (double)s->sm_scale : 1.0 / std::sqrt((double)s->D);
+    return SAGE_OK;
+}
+
+bool empty(const sage::Dims& d) { return d.B == 0 || d.H == 0 || d.N == 0; }
+
+// Every listed pointer non-NULL and 16-byte aligned.
+template <typename... P>
+bool ptrs_ok(P... p) {
+    const void* ps[] = {static_cast<const void*>(p)...};
+    for (const void* x : ps)
+        if (x == nullptr || !aligned(x, 16)) return false;
+    return true;
+}
+
+int check_qtensors(const sage::Dims& d, const sage_qtensors* t) {
+    if (t == nullptr) return SAGE_EINVAL;
+    if (!ptrs_ok(t->q, t->qt, t->sq, t->k, t->kt, t->sk, t->vt, t->sv, t->vr)) return SAGE_EINVAL;
+    if (d.k_smooth && !ptrs_ok(t->mu_k)) return SAGE_EINVAL;
+    if (d.q_smooth && !ptrs_ok(t->mu_q, t->qk_bias)) return SAGE_EINVAL;
+    return SAGE_OK;
+}
+
+int check_dotensors(const sage_dotensors* t) {
+    if (t == nullptr) return SAGE_EINVAL;
+    if (!ptrs_ok(t->delta, t->dot, t->sdo, t->dor)) return SAGE_EINVAL;
+    return SAGE_OK;
+}
+
+int finish(hipError_t e) {
+    if (e != hipSuccess) {
+        g_last_hip_error = (int)e;
+        return SAGE_EHIP;
+    }
+    return SAGE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sage_quantize_workspace_bytes(const sage_shape* shape) {
+    sage::Dims d;
+    if (check_shape(shape, d) != SAGE_OK) return 0;
+    return (size_t)d.B * d.H * d.D * sizeof(double);
+}
+
+int sage_quantize(const sage_shape* shape, const void* Q, const void* K, const void* V,
+                  const sage_qtensors* out, void* workspace, sage_stream_t stream) {
+    sage::Dims d;
+    int st = check_shape(shape, d);
+    if (st != SAGE_OK) return st;
+    if (empty(d)) return SAGE_OK;
+    if (!ptrs_ok(Q, K, V)) return SAGE_EINVAL;
+    if ((st = check_qtensors(d, out)) != SAGE_OK) return st;
+    if (d.k_smooth && (workspace == nullptr || !aligned(workspace, 8))) return SAGE_EINVAL;
+    return finish(sage::launch_quantize(d, Q, K, V, *out, static_cast<double*>(workspace),
+                                        reinterpret_cast<hipStream_t>(stream)));
+}
+
+int sage_fwd(const sage_shape* shape, const sage_qtensors* qk, void* O, float* L, sage_stream_t stream) {
+    sage::Dims d;
+    int st = check_shape(shape, d);
+    if (st != SAGE_OK) return st;
+    if (empty(d)) return SAGE_OK;
+    if ((st = check_qtensors(d, qk)) != SAGE_OK) return st;
+    if (!ptrs_ok(O, L)) return SAGE_EINVAL;
+    return finish(sage::launch_fwd(d, *qk, O, L, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int sage_bwd_pre(const sage_shape* shape, const void* O, const void* dO, const sage_dotensors* out,
+                 sage_stream_t stream) {
+    sage::Dims d;
+    int st = check_shape(shape, d);
+    if (st != SAGE_OK) return st;
+    if (empty(d)) return SAGE_OK;
+    if (!ptrs_ok(O, dO)) return SAGE_EINVAL;
+    if ((st = check_dotensors(out)) != SAGE_OK) return st;
+    return finish(sage::launch_bwd_pre(d, O, dO, *out, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int sage_bwd(const sage_shape* shape, const sage_qtensors* qk, const sage_dotensors* dos,
+             const float* L, float* dQ, float* dK, float* dV, sage_stream_t stream) {
+    sage::Dims d;
+    int st = check_shape(shape, d);
+    if (st != SAGE_OK) return st;
+    if (empty(d)) return SAGE_OK;
+    if ((st = check_qtensors(d, qk)) != SAGE_OK) return st;
+    if ((st = check_dotensors(dos)) != SAGE_OK) return st;
+    if (!ptrs_ok(L, dQ, dK, dV)) return SAGE_EINVAL;
+    return finish(sage::launch_bwd(d, *qk, *dos, L, dQ, dK, dV, reinterpret_cast<hipStream_t>(stream)));
+}
+
+const char* sage_status_str(int status) {
+    switch (status) {
+        case SAGE_OK: return "ok";
+        case SAGE_EINVAL: return "invalid argument (NULL or misaligned pointer, negative size, bad flag)";
+        case SAGE_EUNSUPPORTED: return "unsupported shape (D, block sizes, dtype, or N not a multiple of the blocks)";
+        case SAGE_EHIP: return "HIP launch failed (see sage_last_hip_error)";
+        default: return "unknown status";
+    }
+}
+
+int sage_last_hip_error(void) { return g_last_hip_error; }
+
+const char* sage_version(void) { return "sage-mi355x 0.1 (gfx950)"; }
+
+}  // extern "C"

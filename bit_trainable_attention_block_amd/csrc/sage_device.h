@@ -1,0 +1,127 @@
+// Device-side helpers shared by the SageBwd kernels (gfx950 only).
+//
+// Matrix-instruction operand orders used throughout (wave64, lane l):
+//   v_mfma_i32_32x32x32_i8 / v_mfma_f32_32x32x16_*: A row m = l%32, B column
+//     n = l%32; both carry the contraction index in lane half h = l/32 and
+//     register byte/element e; result register j holds row 8*(j/4)+4*h+j%4,
+//     column l%32.
+//   v_mfma_i32_16x16x64_i8 / v_mfma_f32_16x16x32_*: A row m = l%16, B column
+//     n = l%16; lane group g = l/16 and byte/element e carry the contraction
+//     index; result register j holds row 4*g+j, column l%16.
+// A and B only have to agree on which (h|g, e) carries which contraction
+// index, so a result tile can feed the next product straight from registers
+// once the other operand is stored in the matching permuted order (the
+// C32P / C64P layouts of sage.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sage {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef uint16_t u16;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr double kLog2e_d = 1.4426950408889634074;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLog2_127 = 6.988684686772166f;  // log2(127)
+
+// ---------------------------------------------------------------- dtypes
+template <bool BF16>
+__device__ __forceinline__ float to_f32(u16 b) {
+    if constexpr (BF16) {
+        return __uint_as_float((uint32_t)b << 16);
+    } else {
+        return (float)__builtin_bit_cast(_Float16, b);
+    }
+}
+
+template <bool BF16>
+__device__ __forceinline__ u16 from_f32(float x) {
+    if constexpr (BF16) {
+        uint32_t u = __float_as_uint(x);
+        if ((u & 0x7f800000u) == 0x7f800000u) return (u16)((u >> 16) | ((u & 0xffff) ? 0x40 : 0));
+        u += 0x7fffu + ((u >> 16) & 1u);  // round to nearest even
+        return (u16)(u >> 16);
+    } else {
+        return __builtin_bit_cast(u16, (_Float16)x);  // v_cvt_f16_f32: nearest even
+    }
+}
+
+// ---------------------------------------------------------------- layouts
+// Byte offset of element (row, col) inside a head for each code layout of
+// sage.h.  D is the head dimension.
+__device__ __forceinline__ int off_r32(int row, int col, int D) {
+    return (row >> 5) * (32 * D) + (((col >> 4) * 32 + (row & 31)) << 4) + (col & 15);
+}
+// C32P: 32-row group, (h, e) -> in-group row 8*(e/4) + 4*h + e%4.
+__device__ __forceinline__ int off_c32p(int row, int col, int D) {
+    int r = row & 31;
+    int h = (r >> 2) & 1;
+    int e = ((r >> 3) << 2) | (r & 3);
+    return (row >> 5) * (32 * D) + ((h * D + col) << 4) + e;
+}
+// C64P: 64-row group, (g, e) -> in-group row 16*(e/4) + 4*g + e%4.
+__device__ __forceinline__ int off_c64p(int row, int col, int D) {
+    int r = row & 63;
+    int g = (r >> 2) & 3;
+    int e = ((r >> 4) << 2) | (r & 3);
+    return (row >> 6) * (64 * D) + ((g * D + col) << 4) + e;
+}
+// C64N: 64-row group, (g, e) -> in-group row 16*g + e.
+__device__ __forceinline__ int off_c64n(int row, int col, int D) {
+    int r = row & 63;
+    return (row >> 6) * (64 * D) + ((((r >> 4) * D) + col) << 4) + (r & 15);
+}
+// R16H: element offset of 16-bit element (row, col).
+__device__ __forceinline__ int off_r16h(int row, int col, int D) {
+    return (row >> 4) * (16 * D) + ((((col >> 3) << 4) + (row & 15)) << 3) + (col & 7);
+}
+
+// ---------------------------------------------------------------- reductions
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+__device__ __forceinline__ double wave_sum_d(double v, int width) {
+    for (int o = width >> 1; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// Round-half-even float -> int8 code in [-127, 127] (v is already scaled).
+__device__ __forceinline__ int code_i8(float v) {
+    float r = rintf(v);
+    r = fminf(fmaxf(r, -127.f), 127.f);
+    return (int)r;
+}
+__device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
+    return (uint32_t)(a & 255) | ((uint32_t)(b & 255) << 8) | ((uint32_t)(c & 255) << 16) |
+           ((uint32_t)(d & 255) << 24);
+}
+
+// ---------------------------------------------------------------- MFMA
+__device__ __forceinline__ v16i mfma32_i8(v4i a, v4i b, v16i c) {
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ v4i mfma16_i8(v4i a, v4i b, v4i c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+template <bool BF16>
+__device__ __forceinline__ v4f mfma16_h(v4i a, v4i b, v4f c) {
+    if constexpr (BF16) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a),
+                                                       __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+    } else {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a),
+                                                      __builtin_bit_cast(v8h, b), c, 0, 0, 0);
+    }
+}
+
+}  // namespace sage

@@ -1,0 +1,234 @@
+// SageBwd INT8 forward (SageBwd method summary, forward steps (3)-(5);
+// SageAttention3 write-up Eq. 1 and Eq. 8).
+//
+// One workgroup = 4 waves = 128 queries of one head; wave w owns 32 queries.
+// Key/value tiles of 64 keys (one K/V quantisation block) stream through a
+// double-buffered LDS stage: the K codes (R32 row tiles) and the V codes (C32P
+// column tiles) are contiguous 64*D-byte runs in HBM, so a stage is a plain
+// coalesced copy and every operand read is a conflict-free 16-byte LDS read.
+//
+// Per tile and wave, on the matrix cores (v_mfma_i32_32x32x32_i8):
+//   S^T (64 keys x 32 queries) = K^_j Q^_i^T            int32
+// so each lane holds 32 logits of ONE query (lane % 32) and row statistics
+// are in-lane plus one exchange between the two lane halves.  Then, in
+// float32 on the vector units and in log2 units (x = S * log2 e):
+//   rm = rowmax, m_new = max(m, rm),
+//   P^ codes = rint(127 * 2^(x - rm))         (= P~ / s_P, independent of m)
+//   s_P = 2^(rm - m_new) / 127,  l = l * 2^(m - m_new) + s_P * sum(codes-domain)
+// and the codes feed the second product straight from registers:
+//   O^T (D x 32 queries) += V^_j^T P^^T  (int32) -> O = O * alpha + f32 * s_P s_V.
+// The result register order of S^T is the operand order of P^ once the V
+// codes are stored permuted (C32P), so no shuffle or LDS round trip is needed.
+#include "sage_device.h"
+#include "sage_internal.h"
+
+namespace sage {
+namespace {
+
+struct FwdArgs {
+    const int8_t* q;
+    const float* sq;
+    const int8_t* k;
+    const float* sk;
+    const int8_t* vt;
+    const float* sv;
+    const float* qk_bias;
+    void* O;
+    float* L;
+    int N, bq;
+    double scale2;  // softmax scale * log2(e)
+};
+
+constexpr int kQTile = 128;  // queries per workgroup
+constexpr int kKTile = 64;   // keys per stage (= the K/V quantisation block)
+
+template <bool BF16, int D, bool CAUSAL, bool QSMOOTH>
+__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
+    constexpr int TILE_BYTES = kKTile * D;           // K or V codes of one tile
+    constexpr int CHUNKS = 2 * TILE_BYTES / 16;      // 16-byte chunks per stage (K + V)
+    constexpr int CPT = CHUNKS / 256;                // chunks per thread
+    constexpr int KS = D / 32;                       // contraction steps over d
+    constexpr int DB = D / 32;                       // 32-wide blocks of d
+    __shared__ __align__(16) int8_t stage[2][2 * TILE_BYTES];
+
+    const int N = a.N;
+    const int Tn = N / kKTile;
+    const int Tm = N / a.bq;
+    const int ntiles = (N + kQTile - 1) / kQTile;
+    const int qt = CAUSAL ? (ntiles - 1 - (int)blockIdx.x) : (int)blockIdx.x;  // heavy tiles first
+    const int bh = blockIdx.y;
+    const size_t head = (size_t)bh * N * D;
+
+    const int tid = threadIdx.x;
+    const int w = tid >> 6, lane = tid & 63, n = lane & 31, hh = lane >> 5;
+    const int q0 = qt * kQTile + w * 32;
+    const bool active = q0 < N;
+    const int query = q0 + n;
+
+    int jend = Tn;
+    if (CAUSAL) jend = min(Tn, (qt * kQTile + kQTile) / kKTile);
+
+    // Q codes as the B operand of S^T: lane = query, 16 bytes of d per step.
+    v4i qop[KS];
+    float sqv = 0.f;
+    if (active) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qop[ks] = *reinterpret_cast<const v4i*>(a.q + head + off_r32(query, 32 * ks + 16 * hh, D));
+        sqv = a.sq[(size_t)bh * Tm + q0 / a.bq];
+    }
+    const float* bias_row = nullptr;
+    if (QSMOOTH && active) bias_row = a.qk_bias + ((size_t)bh * Tm + q0 / a.bq) * N;
+
+    float m = -INFINITY, l = 0.f;
+    float o[DB][16];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+
+    // stage loader: chunk c < CHUNKS/2 from K, the rest from V
+    auto load_chunks = [&](int j, v4i (&buf)[CPT]) {
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) {
+            const int c = tid + u * 256;
+            const int half = c / (CHUNKS / 2), cc = c % (CHUNKS / 2);
+            const int8_t* src = (half == 0 ? a.k : a.vt) + head + (size_t)j * TILE_BYTES + cc * 16;
+            buf[u] = *reinterpret_cast<const v4i*>(src);
+        }
+    };
+    auto store_chunks = [&](int sidx, const v4i (&buf)[CPT]) {
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) {
+            const int c = tid + u * 256;
+            *reinterpret_cast<v4i*>(&stage[sidx][c * 16]) = buf[u];
+        }
+    };
+
+    v4i pre[CPT];
+    if (jend > 0) {
+        load_chunks(0, pre);
+        store_chunks(0, pre);
+    }
+    __syncthreads();
+
+    for (int j = 0; j < jend; ++j) {
+        const int sidx = j & 1;
+        const bool more = j + 1 < jend;
+        if (more) load_chunks(j + 1, pre);
+
+        const int k0 = j * kKTile;
+        const bool wave_on = active && (!CAUSAL || k0 <= q0 + 31);
+        if (wave_on) {
+            const v4i* lk = reinterpret_cast<const v4i*>(&stage[sidx][0]);
+            const v4i* lv = reinterpret_cast<const v4i*>(&stage[sidx][TILE_BYTES]);
+            v16i s[2];
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+                s[mb] = v16i{0};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    v4i av = lk[mb * 2 * D + (2 * ks + hh) * 32 + n];
+                    s[mb] = mfma32_i8(av, qop[ks], s[mb]);
+                }
+            }
+            // one rounding from the exact product of the scales (keeps the
+            // logits within an ulp of the definition)
+            const float c2 = (float)((double)sqv * (double)a.sk[(size_t)bh * Tn + j] * a.scale2);
+            const bool need_mask = CAUSAL && (k0 + kKTile - 1 > q0);
+            float x[2][16];
+            float rm = -INFINITY;
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = k0 + 32 * mb + 8 * (r >> 2) + 4 * hh + (r & 3);
+                    float v = (float)s[mb][r] * c2;
+                    if (QSMOOTH) v += (float)((double)bias_row[key] * kLog2e_d);
+                    if (need_mask && key > query) v = -INFINITY;
+                    x[mb][r] = v;
+                    rm = fmaxf(rm, v);
+                }
+            rm = fmaxf(rm, __shfl_xor(rm, 32));
+            const float m_new = fmaxf(m, rm);
+            const float alpha = exp2f(m - m_new);
+            const float shift = rm - kLog2_127;
+            float sum = 0.f;
+            v4i pc[2];
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+                int c[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float e = exp2f(x[mb][r] - shift);  // 127 * 2^(x - rm)
+                    sum += e;
+                    c[r] = (int)rintf(e);
+                }
+#pragma unroll
+                for (int qd = 0; qd < 4; ++qd)
+                    pc[mb][qd] = (int)pack4(c[4 * qd], c[4 * qd + 1], c[4 * qd + 2], c[4 * qd + 3]);
+            }
+            sum += __shfl_xor(sum, 32);
+            const float sP = __fdiv_rn(exp2f(rm - m_new), 127.f);
+            l = fmaf(l, alpha, sum * sP);
+            m = m_new;
+            const float beta = sP * a.sv[(size_t)bh * Tn + j];
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                v16i acc = v16i{0};
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb) {
+                    v4i av = lv[(mb * 2 + hh) * D + 32 * db + n];
+                    acc = mfma32_i8(av, pc[mb], acc);
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[db][r] = fmaf(o[db][r], alpha, (float)acc[r] * beta);
+            }
+        }
+        if (more) {
+            __syncthreads();  // everyone is done reading the other stage
+            store_chunks(sidx ^ 1, pre);
+            __syncthreads();
+        }
+    }
+
+    if (active) {
+        u16* O = reinterpret_cast<u16*>(a.O) + head + (size_t)query * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) {
+                u16 h[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) h[r] = from_f32<BF16>(__fdiv_rn(o[db][4 * qd + r], l));
+                uint2 pk;
+                pk.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+                pk.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+                *reinterpret_cast<uint2*>(O + 32 * db + 8 * qd + 4 * hh) = pk;
+            }
+        if (hh == 0) a.L[(size_t)bh * N + query] = (m + log2f(l)) * kLn2;
+    }
+}
+
+template <bool BF16, int D>
+hipError_t fwd_dispatch(const Dims& d, const FwdArgs& a, hipStream_t s) {
+    dim3 grid((d.N + kQTile - 1) / kQTile, d.BH());
+    if (d.causal) {
+        if (d.q_smooth) fwd_kernel<BF16, D, true, true><<<grid, 256, 0, s>>>(a);
+        else fwd_kernel<BF16, D, true, false><<<grid, 256, 0, s>>>(a);
+    } else {
+        if (d.q_smooth) fwd_kernel<BF16, D, false, true><<<grid, 256, 0, s>>>(a);
+        else fwd_kernel<BF16, D, false, false><<<grid, 256, 0, s>>>(a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const Dims& d, const sage_qtensors& qk, void* O, float* L, hipStream_t s) {
+    FwdArgs a{qk.q, qk.sq, qk.k, qk.sk, qk.vt, qk.sv, qk.qk_bias, O, L, d.N, d.bq, d.scale * kLog2e_d};
+    if (d.bf16) return d.D == 128 ? fwd_dispatch<true, 128>(d, a, s) : fwd_dispatch<true, 64>(d, a, s);
+    return d.D == 128 ? fwd_dispatch<false, 128>(d, a, s) : fwd_dispatch<false, 64>(d, a, s);
+}
+
+}  // namespace sage

@@ -1,0 +1,32 @@
+// Host-side declarations shared by the translation units of libsage.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/sage.h"
+
+namespace sage {
+
+// Validated, derived view of a sage_shape.
+struct Dims {
+    int B, H, N, D, bq, bkv;
+    bool bf16, causal, k_smooth, q_smooth;
+    double scale;  // softmax scale; 1/sqrt(D) in double unless given
+    int BH() const { return B * H; }
+    int Tm() const { return N / bq; }
+    int Tn() const { return N / bkv; }
+    size_t head_elems() const { return (size_t)N * D; }
+};
+
+// Launchers; each returns hipSuccess or the launch error.
+hipError_t launch_quantize(const Dims& d, const void* Q, const void* K, const void* V,
+                           const sage_qtensors& out, double* ws, hipStream_t s);
+hipError_t launch_bwd_pre(const Dims& d, const void* O, const void* dO, const sage_dotensors& out,
+                          hipStream_t s);
+hipError_t launch_fwd(const Dims& d, const sage_qtensors& qk, void* O, float* L, hipStream_t s);
+hipError_t launch_bwd(const Dims& d, const sage_qtensors& qk, const sage_dotensors& dos,
+                      const float* L, float* dQ, float* dK, float* dV, hipStream_t s);
+
+}  // namespace sage

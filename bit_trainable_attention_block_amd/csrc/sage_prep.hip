@@ -1,0 +1,451 @@
+// Preprocessing kernels of the SageBwd path: K/Q smoothing, per-block INT8
+// quantisation of Q, K, V (SageBwd method summary, forward steps (1)-(2);
+// SageAttention3 write-up Eq. 7) and the backward pre-pass
+// D = rowsum(dO o O) plus dO quantisation (backward step (1)).
+//
+// All of it is HBM-bound streaming: each workgroup owns one quantisation
+// block (64 or 128 rows x D columns of one head), reads it once with 16-byte
+// loads, reduces max|x| in registers / DPP / LDS, and writes the INT8 codes in
+// the operand layouts the attention kernels consume (see sage.h), staged
+// through LDS so every global store is a coalesced 16-byte store.
+//
+// Codes and scales must equal the definition bit for bit:
+//   s = f32(max|x| / 127) with a correctly rounded division, and
+//   code = clamp(rint(f32(x / s)), -127, 127), ties to even.
+// Hence __fdiv_rn / __fsub_rn and no fast-math anywhere in this file.
+#include "sage_device.h"
+#include "sage_internal.h"
+
+namespace sage {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <int R, int D>
+struct Blk {
+    static constexpr int CPR = D / 8;                 // 16-byte input chunks per row
+    static constexpr int PER_T = R * CPR / kThreads;  // chunks per thread
+    static constexpr int RSTEP = kThreads / CPR;      // rows between a thread's chunks
+    static_assert(PER_T >= 1 && R * CPR % kThreads == 0, "block shape");
+};
+
+// Load a block of 16-bit values: thread t gets the chunks (row, cc) with
+// cc = t % CPR and rows t / CPR + k * RSTEP.
+template <int R, int D>
+__device__ __forceinline__ void load_block(const u16* __restrict__ src, v4i (&raw)[Blk<R, D>::PER_T]) {
+    using B = Blk<R, D>;
+    const int t = threadIdx.x;
+    const int cc = t % B::CPR;
+#pragma unroll
+    for (int k = 0; k < B::PER_T; ++k) {
+        int row = t / B::CPR + k * B::RSTEP;
+        raw[k] = *reinterpret_cast<const v4i*>(src + (size_t)row * D + cc * 8);
+    }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void unpack8(v4i r, float (&x)[8]) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        uint32_t u = (uint32_t)r[w];
+        x[2 * w] = to_f32<BF16>((u16)(u & 0xffff));
+        x[2 * w + 1] = to_f32<BF16>((u16)(u >> 16));
+    }
+}
+
+__device__ __forceinline__ float block_max(float m, float* red) {
+    m = wave_max(m);
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[w] = m;
+    __syncthreads();
+    float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+    return r;
+}
+
+// Column sums in float64 over the thread's rows, reduced across the RSTEP
+// threads sharing a column chunk; result for column c in dsum[c].
+template <int R, int D>
+__device__ __forceinline__ void block_colsum(const double (&part)[8], double* red, double* dsum) {
+    using B = Blk<R, D>;
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) red[c * kThreads + t] = part[c];
+    __syncthreads();
+    if (t < D) {
+        const int cc = t / 8, c = t % 8;
+        double s = 0.0;
+        for (int r = 0; r < B::RSTEP; ++r) s += red[c * kThreads + r * B::CPR + cc];
+        dsum[t] = s;
+    }
+    __syncthreads();
+}
+
+// Quantise x (values of the block held per thread) with scale s and store
+// the codes row-major into LDS codes[R][D].
+template <int R, int D>
+__device__ __forceinline__ void codes_to_lds(const float (&x)[Blk<R, D>::PER_T][8], float s,
+                                             uint8_t* codes) {
+    using B = Blk<R, D>;
+    const int t = threadIdx.x;
+    const int cc = t % B::CPR;
+#pragma unroll
+    for (int k = 0; k < B::PER_T; ++k) {
+        int row = t / B::CPR + k * B::RSTEP;
+        int c[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) c[e] = s > 0.f ? code_i8(__fdiv_rn(x[k][e], s)) : 0;
+        uint2 w;
+        w.x = pack4(c[0], c[1], c[2], c[3]);
+        w.y = pack4(c[4], c[5], c[6], c[7]);
+        *reinterpret_cast<uint2*>(codes + row * D + cc * 8) = w;
+    }
+}
+
+enum Layout { R32, C32P, C64P, C64N };
+
+// In-block row of byte e of output chunk (h|g) for the column layouts.
+template <Layout L>
+__device__ __forceinline__ int col_layout_row(int grp_part, int e) {
+    if constexpr (L == C32P) return 8 * (e >> 2) + 4 * grp_part + (e & 3);
+    if constexpr (L == C64P) return 16 * (e >> 2) + 4 * grp_part + (e & 3);
+    return 16 * grp_part + e;  // C64N
+}
+
+// Write the R x D codes held in LDS to dst (the block's region of the head,
+// laid out as L) with coalesced 16-byte stores.
+template <Layout L, int R, int D>
+__device__ __forceinline__ void store_codes(const uint8_t* codes, int8_t* __restrict__ dst) {
+    constexpr int CHUNKS = R * D / 16;
+    for (int oc = threadIdx.x; oc < CHUNKS; oc += kThreads) {
+        v4i out;
+        if constexpr (L == R32) {
+            const int g = oc / (2 * D), rem = oc % (2 * D);
+            const int col16 = rem / 32, r = rem % 32;
+            out = *reinterpret_cast<const v4i*>(codes + (32 * g + r) * D + col16 * 16);
+        } else {
+            constexpr int GR = (L == C32P) ? 32 : 64;  // rows per group
+            constexpr int PARTS = GR / 16;             // h or g values
+            const int grp = oc / (PARTS * D), rem = oc % (PARTS * D);
+            const int part = rem / D, col = rem % D;
+            uint32_t w[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uint32_t acc = 0;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int row = grp * GR + col_layout_row<L>(part, 4 * q + b);
+                    acc |= (uint32_t)codes[row * D + col] << (8 * b);
+                }
+                w[q] = acc;
+            }
+            out = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+        }
+        *reinterpret_cast<v4i*>(dst + (size_t)oc * 16) = out;
+    }
+}
+
+// Copy the raw 16-bit block into the R16H row-tile layout.
+template <int R, int D>
+__device__ __forceinline__ void store_r16h(const v4i (&raw)[Blk<R, D>::PER_T], u16* __restrict__ head,
+                                           int row0) {
+    using B = Blk<R, D>;
+    const int t = threadIdx.x;
+    const int cc = t % B::CPR;
+#pragma unroll
+    for (int k = 0; k < B::PER_T; ++k) {
+        int row = row0 + t / B::CPR + k * B::RSTEP;
+        *reinterpret_cast<v4i*>(head + off_r16h(row, cc * 8, D)) = raw[k];
+    }
+}
+
+// ------------------------------------------------------------------ kernels
+
+__global__ void zero_f64_kernel(double* p, int n) {
+    int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0.0;
+}
+
+// V blocks (64 rows): codes -> vt (C32P), scale -> sv, raw copy -> vr (R16H).
+// K blocks (same rows): float64 column sums accumulated into ws[bh][D]
+// (exact: sums of 16-bit values fit float64 without rounding, so the order of
+// the atomic additions does not change the result).
+template <bool BF16, int D>
+__global__ __launch_bounds__(kThreads) void quant_v_ksum_kernel(
+    const u16* __restrict__ K, const u16* __restrict__ V, int N, int8_t* __restrict__ vt,
+    float* __restrict__ sv, u16* __restrict__ vr, double* __restrict__ ws, int k_smooth) {
+    constexpr int R = 64;
+    using B = Blk<R, D>;
+    __shared__ float red[4];
+    __shared__ __align__(16) uint8_t codes[R * D];
+    __shared__ double dred[8 * kThreads];
+    __shared__ double dsum[D];
+    const int j = blockIdx.x, bh = blockIdx.y;
+    const size_t head = (size_t)bh * N * D;
+    const int row0 = j * R;
+
+    v4i raw[B::PER_T];
+    float x[B::PER_T][8];
+    load_block<R, D>(V + head + (size_t)row0 * D, raw);
+    float m = 0.f;
+#pragma unroll
+    for (int k = 0; k < B::PER_T; ++k) {
+        unpack8<BF16>(raw[k], x[k]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[k][e]));
+    }
+    store_r16h<R, D>(raw, vr + head, row0);
+    const float a = block_max(m, red);
+    const float s = __fdiv_rn(a, 127.f);
+    codes_to_lds<R, D>(x, s, codes);
+    if (threadIdx.x == 0) sv[(size_t)bh * (N / R) + j] = s;
+    __syncthreads();
+    store_codes<C32P, R, D>(codes, vt + head + (size_t)row0 * D);
+
+    if (k_smooth) {
+        load_block<R, D>(K + head + (size_t)row0 * D, raw);
+        double part[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int k = 0; k < B::PER_T; ++k) {
+            float y[8];
+            unpack8<BF16>(raw[k], y);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) part[e] += (double)y[e];
+        }
+        block_colsum<R, D>(part, dred, dsum);
+        if (threadIdx.x < D) atomicAdd(ws + (size_t)bh * D + threadIdx.x, dsum[threadIdx.x]);
+    }
+}
+
+// Q blocks (BQ rows): optional Q-smoothing, codes -> q (R32) and qt (C64P).
+template <bool BF16, int D, int BQ>
+__global__ __launch_bounds__(kThreads) void quant_q_kernel(const u16* __restrict__ Q, int N,
+                                                           int8_t* __restrict__ q,
+                                                           int8_t* __restrict__ qt,
+                                                           float* __restrict__ sq,
+                                                           float* __restrict__ mu_q) {
+    using B = Blk<BQ, D>;
+    __shared__ float red[4];
+    __shared__ __align__(16) uint8_t codes[BQ * D];
+    __shared__ double dred[8 * kThreads];
+    __shared__ double dsum[D];
+    __shared__ float mu[D];
+    const int i = blockIdx.x, bh = blockIdx.y;
+    const size_t head = (size_t)bh * N * D;
+    const int row0 = i * BQ;
+    const int Tm = N / BQ;
+
+    v4i raw[B::PER_T];
+    float x[B::PER_T][8];
+    load_block<BQ, D>(Q + head + (size_t)row0 * D, raw);
+#pragma unroll
+    for (int k = 0; k < B::PER_T; ++k) unpack8<BF16>(raw[k], x[k]);
+
+    if (mu_q != nullptr) {
+        double part[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int k = 0; k < B::PER_T; ++k)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) part[e] += (double)x[k][e];
+        block_colsum<BQ, D>(part, dred, dsum);
+        if (threadIdx.x < D) {
+            const float mv = (float)(dsum[threadIdx.x] / (double)BQ);
+            mu[threadIdx.x] = mv;
+            mu_q[((size_t)bh * Tm + i) * D + threadIdx.x] = mv;
+        }
+        __syncthreads();
+        const int cc = threadIdx.x % B::CPR;
+#pragma unroll
+        for (int k = 0; k < B::PER_T; ++k)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[k][e] = __fsub_rn(x[k][e], mu[cc * 8 + e]);
+    }
+    float m = 0.f;
+#pragma unroll
+    for (int k = 0; k < B::PER_T; ++k)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[k][e]));
+    const float a = block_max(m, red);
+    const float s = __fdiv_rn(a, 127.f);
+    codes_to_lds<BQ, D>(x, s, codes);
+    if (threadIdx.x == 0) sq[(size_t)bh * Tm + i] = s;
+    __syncthreads();
+    store_codes<R32, BQ, D>(codes, q + head + (size_t)row0 * D);
+    store_codes<C64P, BQ, D>(codes, qt + head + (size_t)row0 * D);
+}
+
+// K blocks (64 rows): mu_K = f32(sum / N); K_sm = f32(K - mu_K); codes -> k
+// (R32) and kt (C64N).  With Q-smoothing, also the logit bias of these keys
+// for every query block: bias[i][n] = scale * sum_c mu_Q[i][c] * K_sm[n][c]
+// (float64 accumulation, rounded once).
+template <bool BF16, int D>
+__global__ __launch_bounds__(kThreads) void quant_k_kernel(
+    const u16* __restrict__ K, int N, int8_t* __restrict__ k, int8_t* __restrict__ kt,
+    float* __restrict__ sk, float* __restrict__ mu_k, const double* __restrict__ ws, int k_smooth,
+    const float* __restrict__ mu_q, float* __restrict__ qk_bias, int Tm, double scale) {
+    constexpr int R = 64;
+    using B = Blk<R, D>;
+    __shared__ float red[4];
+    __shared__ __align__(16) uint8_t codes[R * D];
+    __shared__ float mu[D];
+    __shared__ float ksm[R][D + 1];
+    const int j = blockIdx.x, bh = blockIdx.y;
+    const size_t head = (size_t)bh * N * D;
+    const int row0 = j * R;
+
+    if (threadIdx.x < D) {
+        float mv = 0.f;
+        if (k_smooth) {
+            mv = (float)(ws[(size_t)bh * D + threadIdx.x] / (double)N);
+            if (j == 0) mu_k[(size_t)bh * D + threadIdx.x] = mv;
+        }
+        mu[threadIdx.x] = mv;
+    }
+    __syncthreads();
+
+    v4i raw[B::PER_T];
+    float x[B::PER_T][8];
+    load_block<R, D>(K + head + (size_t)row0 * D, raw);
+    const int cc = threadIdx.x % B::CPR;
+    float m = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < B::PER_T; ++kk) {
+        unpack8<BF16>(raw[kk], x[kk]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if (k_smooth) x[kk][e] = __fsub_rn(x[kk][e], mu[cc * 8 + e]);
+            m = fmaxf(m, fabsf(x[kk][e]));
+        }
+    }
+    const float a = block_max(m, red);
+    const float s = __fdiv_rn(a, 127.f);
+    codes_to_lds<R, D>(x, s, codes);
+    if (threadIdx.x == 0) sk[(size_t)bh * (N / R) + j] = s;
+    if (qk_bias != nullptr) {
+#pragma unroll
+        for (int kk = 0; kk < B::PER_T; ++kk) {
+            int row = threadIdx.x / B::CPR + kk * B::RSTEP;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ksm[row][cc * 8 + e] = x[kk][e];
+        }
+    }
+    __syncthreads();
+    store_codes<R32, R, D>(codes, k + head + (size_t)row0 * D);
+    store_codes<C64N, R, D>(codes, kt + head + (size_t)row0 * D);
+
+    if (qk_bias != nullptr) {
+        // thread -> (key n = t % 64, query blocks i = t / 64 + 4 * step)
+        const int n = threadIdx.x & 63;
+        for (int i = threadIdx.x >> 6; i < Tm; i += 4) {
+            const float* mq = mu_q + ((size_t)bh * Tm + i) * D;
+            double acc = 0.0;
+            for (int c = 0; c < D; ++c) acc += (double)mq[c] * (double)ksm[n][c];
+            qk_bias[((size_t)bh * Tm + i) * N + row0 + n] = (float)(acc * scale);
+        }
+    }
+}
+
+// Backward pre-pass on one BQ-row block: delta = rowsum(dO o O) (float64,
+// rounded once), dO codes -> dot (C64P), scale -> sdo, raw dO -> dor (R16H).
+template <bool BF16, int D, int BQ>
+__global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const u16* __restrict__ O,
+                                                           const u16* __restrict__ dO, int N,
+                                                           float* __restrict__ delta,
+                                                           int8_t* __restrict__ dot,
+                                                           float* __restrict__ sdo,
+                                                           u16* __restrict__ dor) {
+    using B = Blk<BQ, D>;
+    __shared__ float red[4];
+    __shared__ __align__(16) uint8_t codes[BQ * D];
+    const int i = blockIdx.x, bh = blockIdx.y;
+    const size_t head = (size_t)bh * N * D;
+    const int row0 = i * BQ;
+    const int Tm = N / BQ;
+    const int cc = threadIdx.x % B::CPR;
+
+    v4i raw[B::PER_T], rawo[B::PER_T];
+    float x[B::PER_T][8];
+    load_block<BQ, D>(dO + head + (size_t)row0 * D, raw);
+    load_block<BQ, D>(O + head + (size_t)row0 * D, rawo);
+    store_r16h<BQ, D>(raw, dor + head, row0);
+    float m = 0.f;
+#pragma unroll
+    for (int k = 0; k < B::PER_T; ++k) {
+        float o[8];
+        unpack8<BF16>(raw[k], x[k]);
+        unpack8<BF16>(rawo[k], o);
+        double acc = 0.0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            acc += (double)x[k][e] * (double)o[e];
+            m = fmaxf(m, fabsf(x[k][e]));
+        }
+        // the CPR threads of a row are consecutive lanes of one wave
+        acc = wave_sum_d(acc, B::CPR);
+        if (cc == 0) delta[(size_t)bh * N + row0 + threadIdx.x / B::CPR + k * B::RSTEP] = (float)acc;
+    }
+    const float a = block_max(m, red);
+    const float s = __fdiv_rn(a, 127.f);
+    codes_to_lds<BQ, D>(x, s, codes);
+    if (threadIdx.x == 0) sdo[(size_t)bh * Tm + i] = s;
+    __syncthreads();
+    store_codes<C64P, BQ, D>(codes, dot + head + (size_t)row0 * D);
+}
+
+template <bool BF16, int D>
+hipError_t quantize_impl(const Dims& d, const void* Q, const void* K, const void* V,
+                         const sage_qtensors& out, double* ws, hipStream_t s) {
+    const int BH = d.BH();
+    dim3 blk(kThreads);
+    if (d.k_smooth) {
+        int n = BH * d.D;
+        zero_f64_kernel<<<(n + 255) / 256, 256, 0, s>>>(ws, n);
+    }
+    quant_v_ksum_kernel<BF16, D><<<dim3(d.Tn(), BH), blk, 0, s>>>(
+        (const u16*)K, (const u16*)V, d.N, out.vt, out.sv, out.vr, ws, d.k_smooth ? 1 : 0);
+    if (d.bq == 128)
+        quant_q_kernel<BF16, D, 128><<<dim3(d.Tm(), BH), blk, 0, s>>>((const u16*)Q, d.N, out.q, out.qt,
+                                                                      out.sq, d.q_smooth ? out.mu_q : nullptr);
+    else
+        quant_q_kernel<BF16, D, 64><<<dim3(d.Tm(), BH), blk, 0, s>>>((const u16*)Q, d.N, out.q, out.qt,
+                                                                     out.sq, d.q_smooth ? out.mu_q : nullptr);
+    quant_k_kernel<BF16, D><<<dim3(d.Tn(), BH), blk, 0, s>>>(
+        (const u16*)K, d.N, out.k, out.kt, out.sk, out.mu_k, ws, d.k_smooth ? 1 : 0,
+        d.q_smooth ? out.mu_q : nullptr, d.q_smooth ? out.qk_bias : nullptr, d.Tm(), d.scale);
+    return hipGetLastError();
+}
+
+template <bool BF16, int D>
+hipError_t bwd_pre_impl(const Dims& d, const void* O, const void* dO, const sage_dotensors& out,
+                        hipStream_t s) {
+    dim3 grid(d.Tm(), d.BH());
+    if (d.bq == 128)
+        bwd_pre_kernel<BF16, D, 128><<<grid, kThreads, 0, s>>>((const u16*)O, (const u16*)dO, d.N,
+                                                               out.delta, out.dot, out.sdo, out.dor);
+    else
+        bwd_pre_kernel<BF16, D, 64><<<grid, kThreads, 0, s>>>((const u16*)O, (const u16*)dO, d.N,
+                                                              out.delta, out.dot, out.sdo, out.dor);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const Dims& d, const void* Q, const void* K, const void* V,
+                           const sage_qtensors& out, double* ws, hipStream_t s) {
+    if (d.bf16) {
+        return d.D == 128 ? quantize_impl<true, 128>(d, Q, K, V, out, ws, s)
+                          : quantize_impl<true, 64>(d, Q, K, V, out, ws, s);
+    }
+    return d.D == 128 ? quantize_impl<false, 128>(d, Q, K, V, out, ws, s)
+                      : quantize_impl<false, 64>(d, Q, K, V, out, ws, s);
+}
+
+hipError_t launch_bwd_pre(const Dims& d, const void* O, const void* dO, const sage_dotensors& out,
+                          hipStream_t s) {
+    if (d.bf16) {
+        return d.D == 128 ? bwd_pre_impl<true, 128>(d, O, dO, out, s) : bwd_pre_impl<true, 64>(d, O, dO, out, s);
+    }
+    return d.D == 128 ? bwd_pre_impl<false, 128>(d, O, dO, out, s) : bwd_pre_impl<false, 64>(d, O, dO, out, s);
+}
+
+}  // namespace sage

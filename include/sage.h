@@ -1,0 +1,177 @@
+/*
+ * sage.h — C ABI of libsage.so: SageBwd INT8 attention (forward and backward)
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The method: "SageBwd: A Trainable Low-bit Attention" (arXiv 2603.02170) and
+ * the SageBwd part of "SageAttention3" (arXiv 2505.11594).  Six of the seven
+ * attention products run on INT8 matrix cores with one float32 scale per
+ * block; dP = dO V^T stays in 16-bit floating point.
+ *
+ * Calls, in the order a training step makes them:
+ *   sage_quantize  smoothing + per-block INT8 quantisation of Q, K, V
+ *   sage_fwd       INT8 forward with online softmax -> O and logsumexp L
+ *   sage_bwd_pre   delta = rowsum(dO o O) and INT8 quantisation of dO
+ *   sage_bwd       recompute S and P, dP in 16-bit, dS, INT8 dV, dQ, dK
+ *
+ * Conventions shared by every call
+ *   - Every pointer is a device pointer unless stated otherwise.  The caller
+ *     allocates and owns every buffer, including the workspace; the library
+ *     allocates nothing and keeps no pointer after a call returns.
+ *   - Calls are asynchronous on the given HIP stream (NULL = the default
+ *     stream) and never synchronise the host.  Buffers must stay valid until
+ *     the stream's work is done.  Calls on one stream run in order; calls on
+ *     different streams that share buffers must be ordered by the caller.
+ *   - All 16-bit tensors (Q, K, V, O, dO) are contiguous [B, H, N, D],
+ *     row-major, in the dtype the shape names.  Every base pointer must be
+ *     16-byte aligned.
+ *   - Return value 0 (SAGE_OK) on success, a negative SAGE_E* code otherwise.
+ *     Arguments are checked on the host before anything is launched; on an
+ *     argument error nothing is launched and no buffer is touched.  An empty
+ *     problem (B, H or N equal to 0) launches nothing and returns SAGE_OK.
+ *   - No exception, abort or exit crosses this interface.
+ *
+ * Quantised-tensor layouts (element (row, col) of a [N, D] head; a "group"
+ * is 16, 32 or 64 consecutive rows; each layout is [B, H, N/group, ...]):
+ *   R32   row tiles:  byte (row, col) at group row/32, offset
+ *         ((col/16) * 32 + row%32) * 16 + col%16.
+ *   C32P  column tiles, 32-row groups, permuted: byte (row, col) at group
+ *         row/32, offset (h * D + col) * 16 + e, where the in-group row
+ *         r = 8*(e/4) + 4*h + e%4  (h in {0,1}, e in [0,16)).
+ *   C64P  column tiles, 64-row groups, permuted: offset (g * D + col) * 16 + e,
+ *         with in-group row r = 16*(e/4) + 4*g + e%4  (g in [0,4)).
+ *   C64N  column tiles, 64-row groups, natural order: offset
+ *         (g * D + col) * 16 + e with r = 16*g + e.
+ *   R16H  16-bit row tiles: element (row, col) at group row/16, element
+ *         offset ((col/8) * 16 + row%16) * 8 + col%8.
+ * These orders are the operand orders of the gfx950 INT8 / 16-bit matrix
+ * instructions the kernels use, so tiles move into LDS as plain copies.
+ */
+#ifndef SAGE_H
+#define SAGE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as hipStream_t. */
+typedef struct ihipStream_t* sage_stream_t;
+
+enum {
+    SAGE_OK = 0,
+    SAGE_EINVAL = -1,       /* NULL pointer, negative size, misaligned pointer */
+    SAGE_EUNSUPPORTED = -2, /* D, block sizes, dtype or N outside what is built */
+    SAGE_EHIP = -3          /* a HIP launch failed; see sage_last_hip_error() */
+};
+
+enum { SAGE_FP16 = 0, SAGE_BF16 = 1 };
+
+/* Problem description shared by all calls. */
+typedef struct sage_shape {
+    int32_t B, H, N, D; /* batch, heads, sequence length, head dim (64 or 128) */
+    int32_t bq;         /* rows per Q / dO quantisation block: 64 or 128 */
+    int32_t bkv;        /* rows per K / V quantisation block: 64 */
+    int32_t dtype;      /* SAGE_FP16 or SAGE_BF16, for Q, K, V, O, dO */
+    int32_t causal;     /* 1 = key n visible to query r iff n <= r */
+    int32_t k_smooth;   /* 1 = subtract the per-head token mean of K */
+    int32_t q_smooth;   /* 1 = subtract the mean of each Q block */
+    float sm_scale;     /* softmax scale; 0 selects 1/sqrt(D) */
+} sage_shape;
+/* Supported: D in {64, 128}; bq in {64, 128}; bkv = 64; N a multiple of bq
+ * and of bkv (the pages define T_m = N / B_q blocks; a ragged block is
+ * reported as SAGE_EUNSUPPORTED, not padded). */
+
+/* Output of sage_quantize, input of sage_fwd / sage_bwd.  Sizes in bytes
+ * for one head, T_m = N/bq, T_n = N/bkv. */
+typedef struct sage_qtensors {
+    int8_t* q;        /* R32,  N*D:   codes of Q (of Q - mu_Q with q_smooth) */
+    int8_t* qt;       /* C64P, N*D:   the same codes, column tiles */
+    float* sq;        /* T_m floats:  Q block scales */
+    int8_t* k;        /* R32,  N*D:   codes of K - mu_K (K if !k_smooth) */
+    int8_t* kt;       /* C64N, N*D:   the same codes, column tiles */
+    float* sk;        /* T_n floats:  K block scales */
+    int8_t* vt;       /* C32P, N*D:   codes of V, column tiles */
+    float* sv;        /* T_n floats:  V block scales */
+    uint16_t* vr;     /* R16H, N*D*2: V re-laid as 16-bit row tiles */
+    float* mu_k;      /* D floats:    K token mean (written if k_smooth) */
+    float* mu_q;      /* T_m*D floats: Q block means (q_smooth; else NULL) */
+    float* qk_bias;   /* T_m*N floats: sm_scale * mu_Qi . (K_n - mu_K)
+                         (q_smooth; else NULL) */
+} sage_qtensors;
+
+/* Output of sage_bwd_pre. */
+typedef struct sage_dotensors {
+    float* delta;     /* N floats per head: rowsum(dO o O) */
+    int8_t* dot;      /* C64P, N*D: codes of dO, bq-row blocks */
+    float* sdo;       /* T_m floats: dO block scales */
+    uint16_t* dor;    /* R16H, N*D*2: dO re-laid as 16-bit row tiles */
+} sage_dotensors;
+
+/* Bytes of workspace sage_quantize needs (float64 column sums of K). */
+size_t sage_quantize_workspace_bytes(const sage_shape* shape);
+
+/*
+ * sage_quantize — forward steps (1)-(2) of the SageBwd method summary
+ * (paper.rainbus.top, "method step details"): K-smoothing (prerequisites,
+ * "K-smoothing and Q-smoothing"), optional Q-smoothing, and per-block INT8
+ * quantisation with scale max|X|/127 (prerequisites "INT8 quantisation";
+ * SageAttention3 write-up Eq. 7).
+ *   mu_K = f32(sum_n K[n] / N), the sum exact in float64; K_sm = f32(K - mu_K)
+ *   mu_Q,i likewise over the bq rows of block i; Q_sm = f32(Q - mu_Q,i)
+ *   per block: s = f32(max|X| / 127); code = clamp(rint(f32(x / s)), +-127),
+ *   half-to-even; a block of zeros gets s = 0 and zero codes.
+ * Codes and scales are bit-identical to that definition.
+ * Q, K, V: [B,H,N,D] 16-bit inputs.  out: every pointer must be set, except
+ * mu_q and qk_bias, which must be NULL unless q_smooth (and set if it is).
+ * workspace: sage_quantize_workspace_bytes() bytes, 8-byte aligned, any
+ * content (it is cleared on the stream first).
+ */
+int sage_quantize(const sage_shape* shape, const void* Q, const void* K, const void* V,
+                  const sage_qtensors* out, void* workspace, sage_stream_t stream);
+
+/*
+ * sage_fwd — forward steps (3)-(5): for each query block, the INT8 logits
+ * S_ij = M(Q^_i, K^_j) s_Q s_K * sm_scale (+ the Q-smoothing bias), online
+ * softmax (SageAttention3 Eq. 1), per-token P codes with
+ * s_P = exp(rowmax(S_ij) - m_ij) / 127 and the INT8 product M(P^_ij, V^_j)
+ * (Eq. 8).  The running sum l adds the unquantised probabilities.
+ * O: [B,H,N,D] in the shape's dtype (round-to-nearest-even from float32).
+ * L: [B,H,N] float32, natural-log logsumexp of the (smoothed) logits.
+ */
+int sage_fwd(const sage_shape* shape, const sage_qtensors* qk, void* O, float* L,
+             sage_stream_t stream);
+
+/*
+ * sage_bwd_pre — backward step (1): D_i = rowsum(dO o O) over the stored O
+ * (summed exactly in float64, rounded once to float32), and per-block (bq
+ * rows) INT8 quantisation of dO exactly as in sage_quantize.
+ */
+int sage_bwd_pre(const sage_shape* shape, const void* O, const void* dO,
+                 const sage_dotensors* out, sage_stream_t stream);
+
+/*
+ * sage_bwd — backward steps (2)-(7) (SageAttention3 Eq. 9 INT8 updates), key
+ * blocks outer and query blocks inner: recompute S and P = exp(S - L);
+ * quantise P per (bq x bkv) tile; dV += M(P^T, dO^) s_P s_dO; dP = dO V^T
+ * from the 16-bit values with float32 accumulation; dS = P o (dP - D);
+ * quantise dS per tile; dQ += M(dS^, K^) s_dS s_K; dK += M(dS^T, Q^) s_dS s_Q
+ * (+ (dS^T 1) mu_Q^T with q_smooth).  dQ and dK include sm_scale.
+ * dQ, dK, dV: [B,H,N,D] float32 outputs; dQ is accumulated with atomics and
+ * is cleared on the stream first.  L is sage_fwd's output.
+ */
+int sage_bwd(const sage_shape* shape, const sage_qtensors* qk, const sage_dotensors* dos,
+             const float* L, float* dQ, float* dK, float* dV, sage_stream_t stream);
+
+/* Text for a status code (static storage). */
+const char* sage_status_str(int status);
+/* HIP error code of the most recent SAGE_EHIP in this thread (0 if none). */
+int sage_last_hip_error(void);
+/* Library version string. */
+const char* sage_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SAGE_H */

