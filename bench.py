@@ -1,0 +1,199 @@
+"""Throughput of the SageBwd INT8 attention path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input that
+is already resident in HBM:  sage_quantize -> sage_fwd -> sage_bwd_pre ->
+sage_bwd, through the C ABI, on the workload with d = 128 and N = 8192
+(B = 2, H = 16, causal, bf16, QK-normed Q/K with a per-channel K offset).
+
+Throughput is attention operations per second in the FlashAttention
+convention (forward 4*B*H*N^2*d, backward 10*B*H*N^2*d, halved for causal).
+Besides the one JSON line the driver reads, the line carries per-call times
+(HIP events on the launch stream), the roofline of the dominant kernel and a
+CPU baseline: the oracle timed on this machine's host cores on a bounded
+sample (two whole heads of the same workload).
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "SageBwd fwd+bwd TOPS at d=128,N=8K (1 GPU) + % of INT8 MFMA peak"
+INT8_PEAK_TOPS = 5000.0      # MI355X dense INT8 MFMA, published
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense BF16 MFMA, published
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources: traffic counters are only valid for this code."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "bit_trainable_attention_block_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or
+    None when absent or taken on different kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        if t.get("source_hash") != kernel_source_hash():
+            return None
+        return t["kernels"][kernel]["bytes_per_launch"]
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(cfg, heads=((0, 0), (1, 15))):
+    """The oracle as it stands, single BLAS thread, on whole heads."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from bit_trainable_attention_block_amd import workloads as wl
+    from oracle import sage
+
+    sh = sage.Shape.of(cfg)
+    per_head_ops = sum(cfg.attention_ops()) / (cfg.B * cfg.H)
+    inputs = [wl.generate(cfg, heads=hd) for hd in heads]
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        for x in inputs:
+            Q, K, V, dO = (x[n]["f32"][0, 0].astype(np.float64) for n in ("q", "k", "v", "do"))
+            sage.run_head(Q, K, V, dO, sh)
+        dt = time.perf_counter() - t0
+    ops = per_head_ops * len(heads)
+    return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": 1, "kind": "oracle",
+            "sample": f"{len(heads)} of {cfg.B * cfg.H} heads of the same workload, whole chain "
+                      f"(quantize, fwd, bwd_pre, bwd), {dt:.1f} s on 1 host core"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
+              "(heads shard across GPUs with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from bit_trainable_attention_block_amd import binding as bd
+    from bit_trainable_attention_block_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    bd.load()
+    cfg = wl.C3
+    sh = bd.Shape.of(cfg)
+    x = wl.generate(cfg)
+    dt = sh.torch_dtype
+    Q, K, V, dO = (torch.from_numpy(x[n]["bits"].view(np.int16)).to("cuda").view(dt) for n in ("q", "k", "v", "do"))
+    del x
+    qt = bd.alloc_qtensors(sh)
+    dot = bd.alloc_dotensors(sh)
+    O = torch.empty(Q.shape, dtype=dt, device="cuda")
+    L = torch.empty(Q.shape[:3], dtype=torch.float32, device="cuda")
+    dQ, dK, dV = (torch.empty(Q.shape, dtype=torch.float32, device="cuda") for _ in range(3))
+    bws = bd.bwd_workspace(sh)
+    stream = torch.cuda.current_stream()
+
+    calls = ("sage_quantize", "sage_fwd", "sage_bwd_pre", "sage_bwd")
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        bd.quantize(sh, Q, K, V, out=qt)
+        if ev is not None:
+            ev[1].record(stream)
+        bd.fwd(sh, qt, O, L)
+        if ev is not None:
+            ev[2].record(stream)
+        bd.bwd_pre(sh, O, dO, out=dot)
+        if ev is not None:
+            ev[3].record(stream)
+        bd.bwd(sh, qt, dot, L, dQ, dK, dV, ws=bws)
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per_call = {c: [] for c in calls}
+    for ev in events:
+        for i, c in enumerate(calls):
+            per_call[c].append(ev[i].elapsed_time(ev[i + 1]))
+    call_ms = {c: float(np.mean(v)) for c, v in per_call.items()}
+    ms_per_step = wall * 1e3 / args.steps
+    fwd_ops, bwd_ops = cfg.attention_ops()
+    total_ops = fwd_ops + bwd_ops
+    tops = total_ops / (ms_per_step * 1e-3) / 1e12
+
+    # dominant kernel: the backward (MFMA-bound).  Algorithmic work per launch:
+    # 10*D INT8-equivalent ops per unmasked (query, key) pair of the B*H heads
+    # (S, dV, dK, dQ in INT8 and dP in bf16 counted as ops), halved for causal.
+    bwd_ms = call_ms["sage_bwd"]
+    bwd_tops = bwd_ops / (bwd_ms * 1e-3) / 1e12
+    traffic = measured_traffic("sage_bwd")
+    roofline = {"bound": "mfma", "kernel": "sage_bwd", "achieved": round(bwd_tops, 2), "peak": INT8_PEAK_TOPS,
+                "unit": "TFLOP/s", "frac": round(bwd_tops / INT8_PEAK_TOPS, 4),
+                "traffic": traffic,
+                "mixed_ceiling": round(5.0 / (4.0 / INT8_PEAK_TOPS + 1.0 / BF16_PEAK_TFLOPS), 1)}
+
+    fwd_path_ms = call_ms["sage_quantize"] + call_ms["sage_fwd"]
+    bwd_path_ms = call_ms["sage_bwd_pre"] + call_ms["sage_bwd"]
+    breakdown = {
+        "call_ms": {c: round(v, 4) for c, v in call_ms.items()},
+        "fwd_kernel_tops": round(fwd_ops / (call_ms["sage_fwd"] * 1e-3) / 1e12, 1),
+        "bwd_kernel_tops": round(bwd_tops, 1),
+        "fwd_path_tops": round(fwd_ops / (fwd_path_ms * 1e-3) / 1e12, 1),
+        "bwd_path_tops": round(bwd_ops / (bwd_path_ms * 1e-3) / 1e12, 1),
+        "pct_int8_peak_fwd_bwd": round(100 * tops / INT8_PEAK_TOPS, 2),
+        "pct_int8_peak_fwd_kernel": round(100 * fwd_ops / (call_ms["sage_fwd"] * 1e-3) / 1e12 / INT8_PEAK_TOPS, 2),
+    }
+
+    out = {
+        "metric": METRIC, "value": round(tops, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int8+bf16",
+        "data": "synthetic (seeded Gaussian, QK-normed Q/K, per-channel K offset), resident in HBM",
+        "config": {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "N": cfg.N, "D": cfg.D, "causal": cfg.causal,
+                   "io_dtype": "bf16", "bq": cfg.bq, "bkv": cfg.bkv, "k_smooth": cfg.k_smooth,
+                   "q_smooth": cfg.q_smooth, "parallelism": "single GPU"},
+        "roofline": roofline,
+        "breakdown": breakdown,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -9,7 +9,6 @@ from __future__ import annotations
 
 import ctypes
 import dataclasses
-import math
 import os
 from typing import Dict, Optional
 
@@ -54,8 +53,9 @@ SIGNATURES = {
     "sage_quantize": (ctypes.c_int, [ctypes.POINTER(c_shape), _P, _P, _P, ctypes.POINTER(c_qtensors), _P, _P]),
     "sage_fwd": (ctypes.c_int, [ctypes.POINTER(c_shape), ctypes.POINTER(c_qtensors), _P, _P, _P]),
     "sage_bwd_pre": (ctypes.c_int, [ctypes.POINTER(c_shape), _P, _P, ctypes.POINTER(c_dotensors), _P]),
+    "sage_bwd_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(c_shape)]),
     "sage_bwd": (ctypes.c_int, [ctypes.POINTER(c_shape), ctypes.POINTER(c_qtensors), ctypes.POINTER(c_dotensors),
-                                _P, _P, _P, _P, _P]),
+                                _P, _P, _P, _P, _P, _P]),
     "sage_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "sage_last_hip_error": (ctypes.c_int, []),
     "sage_version": (ctypes.c_char_p, []),
@@ -206,16 +206,22 @@ def bwd_pre(sh: Shape, O, dO, out=None, stream=None):
     return out
 
 
-def bwd(sh: Shape, qt, dot, L, dQ=None, dK=None, dV=None, stream=None):
+def bwd_workspace(sh: Shape, device="cuda") -> torch.Tensor:
+    n = load().sage_bwd_workspace_bytes(ctypes.byref(sh.c()))
+    return torch.empty((max(n, 16),), dtype=torch.uint8, device=device)
+
+
+def bwd(sh: Shape, qt, dot, L, dQ=None, dK=None, dV=None, ws=None, stream=None):
     lib = load()
     dev = L.device
+    ws = bwd_workspace(sh, dev) if ws is None else ws
     shape = (sh.B, sh.H, sh.N, sh.D)
     dQ = torch.empty(shape, dtype=torch.float32, device=dev) if dQ is None else dQ
     dK = torch.empty(shape, dtype=torch.float32, device=dev) if dK is None else dK
     dV = torch.empty(shape, dtype=torch.float32, device=dev) if dV is None else dV
     cs = sh.c()
     _check(lib.sage_bwd(ctypes.byref(cs), ctypes.byref(_qstruct(qt)), ctypes.byref(_dostruct(dot)), _ptr(L),
-                        _ptr(dQ), _ptr(dK), _ptr(dV), _stream(stream)), "sage_bwd")
+                        _ptr(ws), _ptr(dQ), _ptr(dK), _ptr(dV), _stream(stream)), "sage_bwd")
     return dQ, dK, dV
 
 

@@ -114,16 +114,22 @@ int sage_bwd_pre(const sage_shape* shape, const void* O, const void* dO, const s
     return finish(sage::launch_bwd_pre(d, O, dO, *out, reinterpret_cast<hipStream_t>(stream)));
 }
 
+size_t sage_bwd_workspace_bytes(const sage_shape* shape) {
+    sage::Dims d;
+    if (check_shape(shape, d) != SAGE_OK) return 0;
+    return sage::bwd_workspace_bytes(d);
+}
+
 int sage_bwd(const sage_shape* shape, const sage_qtensors* qk, const sage_dotensors* dos,
-             const float* L, float* dQ, float* dK, float* dV, sage_stream_t stream) {
+             const float* L, void* workspace, float* dQ, float* dK, float* dV, sage_stream_t stream) {
     sage::Dims d;
     int st = check_shape(shape, d);
     if (st != SAGE_OK) return st;
     if (empty(d)) return SAGE_OK;
     if ((st = check_qtensors(d, qk)) != SAGE_OK) return st;
     if ((st = check_dotensors(dos)) != SAGE_OK) return st;
-    if (!ptrs_ok(L, dQ, dK, dV)) return SAGE_EINVAL;
-    return finish(sage::launch_bwd(d, *qk, *dos, L, dQ, dK, dV, reinterpret_cast<hipStream_t>(stream)));
+    if (!ptrs_ok(L, workspace, dQ, dK, dV)) return SAGE_EINVAL;
+    return finish(sage::launch_bwd(d, *qk, *dos, L, workspace, dQ, dK, dV, reinterpret_cast<hipStream_t>(stream)));
 }
 
 const char* sage_status_str(int status) {

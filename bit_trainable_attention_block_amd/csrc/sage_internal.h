@@ -26,7 +26,8 @@ hipError_t launch_quantize(const Dims& d, const void* Q, const void* K, const vo
 hipError_t launch_bwd_pre(const Dims& d, const void* O, const void* dO, const sage_dotensors& out,
                           hipStream_t s);
 hipError_t launch_fwd(const Dims& d, const sage_qtensors& qk, void* O, float* L, hipStream_t s);
+size_t bwd_workspace_bytes(const Dims& d);
 hipError_t launch_bwd(const Dims& d, const sage_qtensors& qk, const sage_dotensors& dos,
-                      const float* L, float* dQ, float* dK, float* dV, hipStream_t s);
+                      const float* L, void* workspace, float* dQ, float* dK, float* dV, hipStream_t s);
 
 }  // namespace sage

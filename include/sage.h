@@ -151,18 +151,27 @@ int sage_fwd(const sage_shape* shape, const sage_qtensors* qk, void* O, float* L
 int sage_bwd_pre(const sage_shape* shape, const void* O, const void* dO,
                  const sage_dotensors* out, sage_stream_t stream);
 
+/* Bytes of workspace sage_bwd needs: the INT8 dS codes of every (visible)
+ * bq x bkv tile plus one float32 scale per tile, handed from the key-outer
+ * backward kernel to the query-outer dQ kernel (about N^2/2 bytes per head
+ * when causal, N^2 otherwise). */
+size_t sage_bwd_workspace_bytes(const sage_shape* shape);
+
 /*
- * sage_bwd — backward steps (2)-(7) (SageAttention3 Eq. 9 INT8 updates), key
- * blocks outer and query blocks inner: recompute S and P = exp(S - L);
- * quantise P per (bq x bkv) tile; dV += M(P^T, dO^) s_P s_dO; dP = dO V^T
- * from the 16-bit values with float32 accumulation; dS = P o (dP - D);
- * quantise dS per tile; dQ += M(dS^, K^) s_dS s_K; dK += M(dS^T, Q^) s_dS s_Q
- * (+ (dS^T 1) mu_Q^T with q_smooth).  dQ and dK include sm_scale.
- * dQ, dK, dV: [B,H,N,D] float32 outputs; dQ is accumulated with atomics and
- * is cleared on the stream first.  L is sage_fwd's output.
+ * sage_bwd — backward steps (2)-(7) (SageAttention3 write-up Eq. 9 INT8
+ * updates), key blocks outer and query blocks inner: recompute S and
+ * P = exp(S - L); quantise P per (bq x bkv) tile; dV += M(P^T, dO^) s_P s_dO;
+ * dP = dO V^T from the 16-bit values with float32 accumulation;
+ * dS = P o (dP - D); quantise dS per tile; dK += M(dS^T, Q^) s_dS s_Q
+ * (+ (dS^T 1) mu_Q^T with q_smooth); then, in a second query-outer pass over
+ * the stored dS codes, dQ += M(dS^, K^) s_dS s_K.  dQ and dK include
+ * sm_scale.  dQ, dK, dV: [B,H,N,D] float32 outputs, each written exactly
+ * once (no atomics, no clearing).  L is sage_fwd's output; dos is
+ * sage_bwd_pre's.  workspace: sage_bwd_workspace_bytes() bytes, 16-byte
+ * aligned, any content.
  */
 int sage_bwd(const sage_shape* shape, const sage_qtensors* qk, const sage_dotensors* dos,
-             const float* L, float* dQ, float* dK, float* dV, sage_stream_t stream);
+             const float* L, void* workspace, float* dQ, float* dK, float* dV, sage_stream_t stream);
 
 /* Text for a status code (static storage). */
 const char* sage_status_str(int status);

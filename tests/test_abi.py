@@ -85,8 +85,9 @@ def test_bad_shapes_rejected_by_every_call(lib, kw, code):
     assert lib.sage_quantize(ctypes.byref(s), FAKE, FAKE, FAKE, ctypes.byref(qt), FAKE, None) == code
     assert lib.sage_fwd(ctypes.byref(s), ctypes.byref(qt), FAKE, FAKE, None) == code
     assert lib.sage_bwd_pre(ctypes.byref(s), FAKE, FAKE, ctypes.byref(dot), None) == code
-    assert lib.sage_bwd(ctypes.byref(s), ctypes.byref(qt), ctypes.byref(dot), FAKE, FAKE, FAKE, FAKE, None) == code
+    assert lib.sage_bwd(ctypes.byref(s), ctypes.byref(qt), ctypes.byref(dot), FAKE, FAKE, FAKE, FAKE, FAKE, None) == code
     assert lib.sage_quantize_workspace_bytes(ctypes.byref(s)) == 0
+    assert lib.sage_bwd_workspace_bytes(ctypes.byref(s)) == 0
 
 
 def test_null_shape(lib):
@@ -115,7 +116,7 @@ def test_missing_dotensor(lib, field):
     s = _shape()
     dot = _dot(**{field: None})
     assert lib.sage_bwd_pre(ctypes.byref(s), FAKE, FAKE, ctypes.byref(dot), None) == bd.SAGE_EINVAL
-    assert lib.sage_bwd(ctypes.byref(s), ctypes.byref(_qt()), ctypes.byref(dot), FAKE, FAKE, FAKE, FAKE,
+    assert lib.sage_bwd(ctypes.byref(s), ctypes.byref(_qt()), ctypes.byref(dot), FAKE, FAKE, FAKE, FAKE, FAKE,
                         None) == bd.SAGE_EINVAL
 
 
@@ -127,7 +128,8 @@ def test_io_pointers_checked(lib):
     assert lib.sage_quantize(ctypes.byref(s), FAKE, FAKE, FAKE, qt, FAKE + 4, None) == bd.SAGE_EINVAL
     assert lib.sage_fwd(ctypes.byref(s), qt, FAKE + 2, FAKE, None) == bd.SAGE_EINVAL
     assert lib.sage_fwd(ctypes.byref(s), qt, FAKE, None, None) == bd.SAGE_EINVAL
-    assert lib.sage_bwd(ctypes.byref(s), qt, ctypes.byref(_dot()), FAKE, None, FAKE, FAKE, None) == bd.SAGE_EINVAL
+    assert lib.sage_bwd(ctypes.byref(s), qt, ctypes.byref(_dot()), FAKE, None, FAKE, FAKE, FAKE, None) == bd.SAGE_EINVAL
+    assert lib.sage_bwd(ctypes.byref(s), qt, ctypes.byref(_dot()), FAKE, FAKE, None, FAKE, FAKE, None) == bd.SAGE_EINVAL
 
 
 def test_empty_problem_is_a_no_op(lib):
@@ -137,12 +139,18 @@ def test_empty_problem_is_a_no_op(lib):
         assert lib.sage_quantize(ctypes.byref(s), None, None, None, None, None, None) == bd.SAGE_OK
         assert lib.sage_fwd(ctypes.byref(s), None, None, None, None) == bd.SAGE_OK
         assert lib.sage_bwd_pre(ctypes.byref(s), None, None, None, None) == bd.SAGE_OK
-        assert lib.sage_bwd(ctypes.byref(s), None, None, None, None, None, None, None) == bd.SAGE_OK
+        assert lib.sage_bwd(ctypes.byref(s), None, None, None, None, None, None, None, None) == bd.SAGE_OK
 
 
 def test_workspace_size_and_strings(lib):
     s = _shape(B=2, H=3, D=64)
     assert lib.sage_quantize_workspace_bytes(ctypes.byref(s)) == 2 * 3 * 64 * 8
+    # N = 256, bq = 128, bkv = 64: 2 x 4 tiles of 128 x 64 codes + a float each, per head
+    tiles = 2 * 3 * 2 * 4
+    codes = -(-tiles * 128 * 64 // 256) * 256
+    assert lib.sage_bwd_workspace_bytes(ctypes.byref(s)) == codes + tiles * 4
+    c = _shape(B=1, H=1, N=512, causal=1)      # causal: only the visible tiles (2 + 4 + 6 + 8)
+    assert lib.sage_bwd_workspace_bytes(ctypes.byref(c)) == 20 * 128 * 64 + 20 * 4
     for code in (0, -1, -2, -3, 7):
         assert lib.sage_status_str(code)
     assert b"gfx950" in lib.sage_version()
