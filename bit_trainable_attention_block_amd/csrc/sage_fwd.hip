@@ -12,13 +12,16 @@
 // so each lane holds 32 logits of ONE query (lane % 32) and row statistics
 // are in-lane plus one exchange between the two lane halves.  Then, in
 // float32 on the vector units and in log2 units (x = S * log2 e):
-//   rm = rowmax, m_new = max(m, rm),
+//   rm = rowmax, m = reference maximum (moved lazily, see below),
 //   P^ codes = rint(127 * 2^(x - rm))         (= P~ / s_P, independent of m)
-//   s_P = 2^(rm - m_new) / 127,  l = l * 2^(m - m_new) + s_P * sum(codes-domain)
+//   s_P = 2^(rm - m) / 127,  l += s_P * sum(127 * 2^(x - rm))
 // and the codes feed the second product straight from registers:
 //   O^T (D x 32 queries) += V^_j^T P^^T  (int32) -> O = O * alpha + f32 * s_P s_V.
 // The result register order of S^T is the operand order of P^ once the V
 // codes are stored permuted (C32P), so no shuffle or LDS round trip is needed.
+#include <climits>
+#include <type_traits>
+
 #include "sage_device.h"
 #include "sage_internal.h"
 
@@ -41,6 +44,15 @@ struct FwdArgs {
 
 constexpr int kQTile = 128;  // queries per workgroup
 constexpr int kKTile = 64;   // keys per stage (= the K/V quantisation block)
+constexpr float kLazy = 8.f; // log2 slack before the reference maximum moves
+constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23: x + kMagic holds rint(x) in its low byte
+
+// Byte 0 of four magic-rounded floats -> one dword.
+__device__ __forceinline__ int pack_magic(float a, float b, float c, float d) {
+    const uint32_t lo = __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x0c0c0400u);
+    const uint32_t hi = __builtin_amdgcn_perm(__float_as_uint(d), __float_as_uint(c), 0x04000c0cu);
+    return (int)(lo | hi);
+}
 
 template <bool BF16, int D, bool CAUSAL, bool QSMOOTH>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
@@ -135,55 +147,100 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
             // one rounding from the exact product of the scales (keeps the
             // logits within an ulp of the definition)
             const float c2 = (float)((double)sqv * (double)a.sk[(size_t)bh * Tn + j] * a.scale2);
-            const bool need_mask = CAUSAL && (k0 + kKTile - 1 > q0);
-            float x[2][16];
-            float rm = -INFINITY;
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = k0 + 32 * mb + 8 * (r >> 2) + 4 * hh + (r & 3);
-                    float v = (float)s[mb][r] * c2;
-                    if (QSMOOTH) v += (float)((double)bias_row[key] * kLog2e_d);
-                    if (need_mask && key > query) v = -INFINITY;
-                    x[mb][r] = v;
-                    rm = fmaxf(rm, v);
+            // Diagonal tiles (some key after some query) take the masked
+            // instantiation; every other tile runs without a compare.
+            auto tile = [&](auto mask_tag) {
+                constexpr bool MASK = decltype(mask_tag)::value;
+                // Row maximum of this tile (log2 units).  Without Q-smoothing the
+                // logits are one positive scale times the int32 sums, so the max
+                // is taken on the integers; masked keys never win it.
+                float rm;
+                float bias2[2][16];
+                if (QSMOOTH) {
+                    rm = -INFINITY;
+    #pragma unroll
+                    for (int mb = 0; mb < 2; ++mb)
+    #pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int key = k0 + 32 * mb + 8 * (r >> 2) + 4 * hh + (r & 3);
+                            bias2[mb][r] = (float)((double)bias_row[key] * kLog2e_d);
+                            const float v = fmaf((float)s[mb][r], c2, bias2[mb][r]);
+                            if (!(MASK && key > query)) rm = fmaxf(rm, v);
+                        }
+                } else {
+                    int im = INT_MIN;
+                    if (MASK) {
+    #pragma unroll
+                        for (int mb = 0; mb < 2; ++mb)
+    #pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                const int key = k0 + 32 * mb + 8 * (r >> 2) + 4 * hh + (r & 3);
+                                im = max(im, key > query ? INT_MIN : s[mb][r]);
+                            }
+                    } else {
+    #pragma unroll
+                        for (int mb = 0; mb < 2; ++mb)
+    #pragma unroll
+                            for (int r = 0; r < 16; r += 2) im = max(im, max(s[mb][r], s[mb][r + 1]));
+                    }
+                    rm = (float)im * c2;
                 }
-            rm = fmaxf(rm, __shfl_xor(rm, 32));
-            const float m_new = fmaxf(m, rm);
-            const float alpha = exp2f(m - m_new);
-            const float shift = rm - kLog2_127;
-            float sum = 0.f;
-            v4i pc[2];
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-                int c[16];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float e = exp2f(x[mb][r] - shift);  // 127 * 2^(x - rm)
-                    sum += e;
-                    c[r] = (int)rintf(e);
-                }
-#pragma unroll
-                for (int qd = 0; qd < 4; ++qd)
-                    pc[mb][qd] = (int)pack4(c[4 * qd], c[4 * qd + 1], c[4 * qd + 2], c[4 * qd + 3]);
-            }
-            sum += __shfl_xor(sum, 32);
-            const float sP = __fdiv_rn(exp2f(rm - m_new), 127.f);
-            l = fmaf(l, alpha, sum * sP);
-            m = m_new;
-            const float beta = sP * a.sv[(size_t)bh * Tn + j];
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                v16i acc = v16i{0};
-#pragma unroll
+                rm = fmaxf(rm, __shfl_xor(rm, 32));
+                // Reference maximum: moves only when the row max exceeds it by
+                // more than 2^8, so the rescale below is rare.  The codes
+                // 127 * 2^(x - rm) do not depend on it, only l and O's common
+                // factor do, and those use it consistently.
+                const float m_new = (rm > m + kLazy) ? rm : m;
+                const float shift = rm - kLog2_127;
+                float sum = 0.f;
+                v4i pc[2];
+    #pragma unroll
                 for (int mb = 0; mb < 2; ++mb) {
-                    v4i av = lv[(mb * 2 + hh) * D + 32 * db + n];
-                    acc = mfma32_i8(av, pc[mb], acc);
+                    float c[16];
+    #pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        float x = QSMOOTH ? fmaf((float)s[mb][r], c2, bias2[mb][r] - shift)
+                                          : fmaf((float)s[mb][r], c2, -shift);
+                        if (MASK) {
+                            const int key = k0 + 32 * mb + 8 * (r >> 2) + 4 * hh + (r & 3);
+                            if (key > query) x = -INFINITY;
+                        }
+                        const float e = __builtin_amdgcn_exp2f(x);  // 127 * 2^(x - rm), in [0, 127]
+                        sum += e;
+                        c[r] = e + kMagic;                           // rint(e) in the low byte
+                    }
+    #pragma unroll
+                    for (int qd = 0; qd < 4; ++qd)
+                        pc[mb][qd] = pack_magic(c[4 * qd], c[4 * qd + 1], c[4 * qd + 2], c[4 * qd + 3]);
                 }
-#pragma unroll
-                for (int r = 0; r < 16; ++r) o[db][r] = fmaf(o[db][r], alpha, (float)acc[r] * beta);
-            }
+                sum += __shfl_xor(sum, 32);
+                const float sP = __fdiv_rn(__builtin_amdgcn_exp2f(rm - m_new), 127.f);
+                if (__builtin_expect(__any(m_new != m), 0)) {
+                    // rare: a row's reference maximum moved; rescale l and O
+                    const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 0 on the first tile
+                    l *= alpha;
+    #pragma unroll
+                    for (int db = 0; db < DB; ++db)
+    #pragma unroll
+                        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+                }
+                l = fmaf(sum, sP, l);
+                m = m_new;
+                const float beta = sP * a.sv[(size_t)bh * Tn + j];
+    #pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    v16i acc = v16i{0};
+    #pragma unroll
+                    for (int mb = 0; mb < 2; ++mb) {
+                        v4i av = lv[(mb * 2 + hh) * D + 32 * db + n];
+                        acc = mfma32_i8(av, pc[mb], acc);
+                    }
+    #pragma unroll
+                    for (int r = 0; r < 16; ++r) o[db][r] = fmaf((float)acc[r], beta, o[db][r]);
+                }
+            };
+            if (CAUSAL && (k0 + kKTile - 1 > q0)) tile(std::true_type{});
+            else tile(std::false_type{});
         }
         if (more) {
             __syncthreads();  // everyone is done reading the other stage
