@@ -10,7 +10,7 @@ convention (forward 4*B*H*N^2*d, backward 10*B*H*N^2*d, halved for causal).
 Besides the one JSON line the driver reads, the line carries per-call times
 (HIP events on the launch stream), the roofline of the dominant kernel and a
 CPU baseline: the oracle timed on this machine's host cores on a bounded
-sample (two whole heads of the same workload).
+sample (ten whole heads of the same workload).
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -57,7 +57,11 @@ def measured_traffic(kernel: str):
         return None
 
 
-def cpu_baseline(cfg, heads=((0, 0), (1, 15))):
+# whole heads timed for the CPU baseline: about 10-15 s of single-core work
+CPU_HEADS = ((0, 0), (0, 5), (0, 10), (0, 15), (1, 0), (1, 3), (1, 7), (1, 9), (1, 12), (1, 15))
+
+
+def cpu_baseline(cfg, heads=CPU_HEADS):
     """The oracle as it stands, single BLAS thread, on whole heads."""
     import numpy as np
     from threadpoolctl import threadpool_limits
