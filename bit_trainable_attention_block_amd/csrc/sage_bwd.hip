@@ -4,27 +4,36 @@
 //
 // 1. bwd_kernel — one workgroup = 8 waves = two 64-key blocks of one head;
 //    wave w owns 16 keys of block 2*jj + w/4 and keeps their dV and dK in
-//    float32 registers for the whole sweep over query tiles.  Per query tile
-//    (BQ rows, the dO/Q quantisation block) the Q codes, dO (16-bit), the
-//    transposed Q and dO codes and the per-row L and delta are staged in LDS
-//    once for both key blocks, and each wave computes, on the matrix cores
-//    (16x16 tiles, lane = key):
+//    float32 registers for the whole sweep over query tiles.  The query tile
+//    (BQ rows, the dO/Q quantisation block: Q codes, dO codes in the
+//    transposed operand order, dO in 16-bit) streams through a double-buffered
+//    LDS stage filled by asynchronous global->LDS copies one tile ahead.  Per
+//    tile each wave computes, on the matrix cores (16x16 tiles, lane = key):
 //      S  = Q^ K^T     v_mfma_i32_16x16x64_i8            (recompute)
 //      dP = dO V^T     v_mfma_f32_16x16x32_{bf16,f16}    (kept in 16-bit)
 //    then on the vector units P = 2^(S log2e - L log2e), dS = P (dP - delta);
-//    the per-tile maxima of P and |dS| (one scale per BQ x 64 tile) go
-//    through LDS once, and the codes feed, straight from registers,
+//    the tile maxima of P and |dS| (one scale per BQ x 64 tile) are reduced
+//    in-wave with DPP and across the block's four waves through LDS, and the
+//    codes feed, straight from registers,
 //      dV^T += dO^^T P^   and   dK^T += Q^^T dS^        (16x16x64 i8)
-//    because S's result order is the operand order once the transposed codes
-//    are stored permuted (C64P).  The dS codes of each tile (BQ x 64 bytes)
-//    and its scale go to the workspace, already in the dQ product's operand
-//    order.
+//    because S's result order is the operand order of the transposed codes
+//    (C64P for dO; Q's transposed operand is read from its row tiles with
+//    the LDS transpose read).  The dS codes of each tile go to the workspace
+//    key-major, two 16-byte stores per lane, and its scale beside them.
 // 2. dq_kernel — one workgroup per query tile: dQ_i = sum_j dS^_ij K^_j
-//    s_dS,ij s_K,j (INT8 products, int32 per tile, float32 across tiles),
-//    written once: no atomics and no clearing pass.
+//    s_dS,ij s_K,j (INT8 products, float32 across tiles), the dS codes read
+//    back transposed by the LDS transpose read.  dQ is written once: no
+//    atomics and no clearing pass.
 //
-// Codes are rounded to nearest-even by one fma with 1.5 * 2^23, which leaves
-// the integer in the low mantissa byte, and packed with v_perm.
+// Integer products start from the accumulator 1.5 * 2^23 so that their
+// float value is one exact subtraction away (see unmagic).  Codes are
+// rounded to nearest-even by one fma with 1.5 * 2^23 and packed with v_perm.
+//
+// dS workspace layout, per tile (BQ queries x 64 keys, BQ * 64 bytes): key
+// row kr (0..63) holds BQ bytes; query q = 16 mb + 4 g + r of the tile sits
+// at position p = (BQ/4) g + 4 mb + r, and the 16-byte chunk c of a row is
+// stored at chunk slot c ^ (kr mod BQ/16), which spreads the transpose reads
+// of eight consecutive rows over distinct LDS banks.
 #include <algorithm>
 
 #include "sage_device.h"
@@ -35,10 +44,8 @@ namespace {
 
 struct BwdArgs {
     const int8_t* q;
-    const int8_t* qt;
     const float* sq;
     const int8_t* k;
-    const int8_t* kt;
     const float* sk;
     const u16* vr;
     const float* mu_q;
@@ -48,12 +55,11 @@ struct BwdArgs {
     const float* sdo;
     const u16* dor;
     const float* L;
-    int8_t* dsw;   // dS codes per tile, [bh][tile][4][BQ][16]
+    int8_t* dsw;   // dS codes per tile (layout above)
     float* sds;    // dS scale per tile, [bh][tile]
-    float* dQ;
     float* dK;
     float* dV;
-    int N;
+    int N, BH;
     double scale;  // softmax scale
 };
 
@@ -79,39 +85,85 @@ __device__ __forceinline__ int pack_magic(float a, float b, float c, float d) {
     return (int)(lo | hi);
 }
 
+// Workgroup -> (unit, head).  Blocks are dealt to the eight XCDs round-robin;
+// when the heads divide evenly, each XCD takes whole heads one after another
+// (so a head's streamed tiles stay in that XCD's L2), units in order within
+// a head; `units` is the number of units per head.
+__device__ __forceinline__ void xcd_coords(int units, int BH, int& unit, int& bh) {
+    const int id = blockIdx.x;
+    if ((BH & 7) == 0) {
+        const int xcd = id & 7, k = id >> 3;
+        bh = xcd + 8 * (k / units);
+        unit = k % units;
+    } else {
+        bh = id / units;
+        unit = id % units;
+    }
+}
+
 template <int BQ, int D>
 struct BwdSmem {
-    int8_t q[BQ * D];            // Q codes, R32
-    int8_t qt[BQ * D];           // Q codes, C64P
-    int8_t dot[BQ * D];          // dO codes, C64P
-    u16 dor[BQ * D];             // dO, R16H
-    int8_t ds[2][4 * BQ * 16];   // dS codes of the two key blocks, [key/16][query][16]
-    float l2[BQ];                // L * log2 e
-    float delta[BQ];
-    float red[2][2][4];          // [key block][P | dS][wave]
-    float sds[2];                // dS scale of the two key blocks
+    int8_t q[2][BQ * D];     // Q codes, R32
+    int8_t dot[2][BQ * D];   // dO codes, C64P
+    u16 dor[2][BQ * D];      // dO, R16H
+    float l2[2][BQ];         // L * log2 e
+    float delta[2][BQ];
+    float red[2][2][4];      // [key block][P | dS][key group]
 };
+
+// Asynchronous copy of query tile qbase (Q codes, dO codes, dO) into stage b.
+// The three regions are contiguous BQ*D, BQ*D and 2*BQ*D byte runs; each
+// wave instruction moves 1 KiB.
+template <int BQ, int D>
+__device__ __forceinline__ void stage_query_tile(BwdSmem<BQ, D>& sm, int b, const BwdArgs& a, size_t head,
+                                                 int qbase) {
+    constexpr int QB = BQ * D, TOT = 4 * QB, ROUNDS = TOT / (8 * 1024);
+    static_assert(TOT % (8 * 1024) == 0 && QB % 1024 == 0, "stage shape");
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int8_t* q = a.q + head + (size_t)qbase * D;
+    const int8_t* dot = a.dot + head + (size_t)qbase * D;
+    const int8_t* dor = reinterpret_cast<const int8_t*>(a.dor + head + (size_t)qbase * D);
+#pragma unroll
+    for (int u = 0; u < ROUNDS; ++u) {
+        const int c0 = u * 8 * 1024 + w * 1024;
+        const int8_t* src;
+        int8_t* dst;
+        if (c0 < QB) {
+            src = q + c0;
+            dst = sm.q[b] + c0;
+        } else if (c0 < 2 * QB) {
+            src = dot + (c0 - QB);
+            dst = sm.dot[b] + (c0 - QB);
+        } else {
+            src = dor + (c0 - 2 * QB);
+            dst = reinterpret_cast<int8_t*>(sm.dor[b]) + (c0 - 2 * QB);
+        }
+        copy16_to_lds(src + lane * 16, dst);
+    }
+}
 
 template <bool BF16, int D, int BQ, bool CAUSAL, bool QSMOOTH>
 __global__ __launch_bounds__(512, 1) void bwd_kernel(BwdArgs a) {
-    constexpr int NT = 512;
     constexpr int MB = BQ / 16;   // 16-query blocks per tile
     constexpr int KQ = BQ / 64;   // i8 contraction steps over queries
     constexpr int KS8 = D / 64;   // i8 contraction steps over d
     constexpr int KSH = D / 32;   // 16-bit contraction steps over d
     constexpr int DB = D / 16;    // 16-wide blocks of d
+    constexpr int CH = BQ / 16;   // 16-byte chunks per dS key row
     __shared__ __align__(16) BwdSmem<BQ, D> sm;
 
     const int N = a.N;
     const int Tn = N / 64, Tm = N / BQ;
-    const int jj = blockIdx.x, bh = blockIdx.y;
+    int jj, bh;
+    xcd_coords((Tn + 1) / 2, a.BH, jj, bh);
     const size_t head = (size_t)bh * N * D;
     const int tid = threadIdx.x;
     const int w = tid >> 6, lane = tid & 63, n16 = lane & 15, g = lane >> 4;
     const int kb = w >> 2, kg = w & 3;
     const int j = 2 * jj + kb;        // this wave's key block
     const bool kv_on = j < Tn;        // the second block of a ragged tail may not exist
-    const int key = j * 64 + 16 * kg + n16;
+    const int kr = 16 * kg + n16;     // key row inside the block
+    const int key = j * 64 + kr;
 
     v4i kop[KS8], vop[KSH];
     float skj = 0.f;
@@ -131,35 +183,39 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(BwdArgs a) {
         dvt[db] = v4f{0, 0, 0, 0};
         dkt[db] = v4f{0, 0, 0, 0};
     }
+    const v4i magic4 = v4i{kMagicBits, kMagicBits, kMagicBits, kMagicBits};
 
     const size_t tph = tiles_per_head<BQ, CAUSAL>(Tm, Tn);
     const int istart = CAUSAL ? (2 * jj * 64) / BQ : 0;
+    const float* Lh = a.L + (size_t)bh * N;
+    const float* dlh = a.delta + (size_t)bh * N;
+
+    // ---- prologue: first query tile
+    stage_query_tile<BQ, D>(sm, 0, a, head, istart * BQ);
+    if (tid < BQ) {
+        sm.l2[0][tid] = (float)((double)Lh[istart * BQ + tid] * kLog2e_d);
+        sm.delta[0][tid] = dlh[istart * BQ + tid];
+    }
+    wait_vmem();
+    __syncthreads();
+
     for (int i = istart; i < Tm; ++i) {
+        const int b = (i - istart) & 1;
         const int qbase = i * BQ;
-        // ---- stage the query tile (read by the waves of both key blocks)
-        {
-            const v4i* src_q = reinterpret_cast<const v4i*>(a.q + head + (size_t)qbase * D);
-            const v4i* src_qt = reinterpret_cast<const v4i*>(a.qt + head + (size_t)qbase * D);
-            const v4i* src_dot = reinterpret_cast<const v4i*>(a.dot + head + (size_t)qbase * D);
-            const v4i* src_dor = reinterpret_cast<const v4i*>(a.dor + head + (size_t)qbase * D);
-            v4i* dq_ = reinterpret_cast<v4i*>(sm.q);
-            v4i* dqt = reinterpret_cast<v4i*>(sm.qt);
-            v4i* ddot = reinterpret_cast<v4i*>(sm.dot);
-            v4i* ddor = reinterpret_cast<v4i*>(sm.dor);
-#pragma unroll
-            for (int c = tid; c < BQ * D / 16; c += NT) {
-                dq_[c] = src_q[c];
-                dqt[c] = src_qt[c];
-                ddot[c] = src_dot[c];
-            }
-#pragma unroll
-            for (int c = tid; c < BQ * D / 8; c += NT) ddor[c] = src_dor[c];
+        const bool more = i + 1 < Tm;
+        // ---- next tile: asynchronous copy into the other stage (last read
+        // before the previous iteration's closing barrier)
+        float nL = 0.f, nd = 0.f;
+        if (more) {
+            stage_query_tile<BQ, D>(sm, b ^ 1, a, head, qbase + BQ);
             if (tid < BQ) {
-                sm.l2[tid] = (float)((double)a.L[(size_t)bh * N + qbase + tid] * kLog2e_d);
-                sm.delta[tid] = a.delta[(size_t)bh * N + qbase + tid];
+                nL = Lh[qbase + BQ + tid];
+                nd = dlh[qbase + BQ + tid];
             }
         }
-        __syncthreads();
+        const int8_t* sq = sm.q[b];
+        const int8_t* sdot = sm.dot[b];
+        const u16* sdor = sm.dor[b];
 
         const bool tile_on = kv_on && (!CAUSAL || j * 64 <= qbase + BQ - 1);
         const float sqi = a.sq[(size_t)bh * Tm + i];
@@ -171,30 +227,41 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(BwdArgs a) {
             if (QSMOOTH) bias2 = (float)((double)a.qk_bias[((size_t)bh * Tm + i) * N + key] * kLog2e_d);
             const bool need_mask = CAUSAL && (j * 64 + 63 > qbase);
             // ---- S and dP for this wave's 16 keys and all BQ queries
+            v4i s[MB];
+            v4f dp[MB];
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
                 const int row = 16 * mb + n16;  // query row (in tile) this lane supplies
-                v4i s = v4i{0, 0, 0, 0};
+                s[mb] = magic4;
 #pragma unroll
                 for (int ks = 0; ks < KS8; ++ks) {
-                    const v4i av = *reinterpret_cast<const v4i*>(sm.q + off_r32(row, 64 * ks + 16 * g, D));
-                    s = mfma16_i8(av, kop[ks], s);
+                    const v4i av = *reinterpret_cast<const v4i*>(sq + off_r32(row, 64 * ks + 16 * g, D));
+                    s[mb] = mfma16_i8(av, kop[ks], s[mb]);
                 }
-                v4f dp = v4f{0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                const int row = 16 * mb + n16;
+                dp[mb] = v4f{0, 0, 0, 0};
 #pragma unroll
                 for (int ks = 0; ks < KSH; ++ks) {
-                    const v4i av = *reinterpret_cast<const v4i*>(sm.dor + off_r16h(row, 32 * ks + 8 * g, D));
-                    dp = mfma16_h<BF16>(av, vop[ks], dp);
+                    const v4i av = *reinterpret_cast<const v4i*>(sdor + off_r16h(row, 32 * ks + 8 * g, D));
+                    dp[mb] = mfma16_h<BF16>(av, vop[ks], dp[mb]);
                 }
-                const v4f l2 = *reinterpret_cast<const v4f*>(&sm.l2[16 * mb + 4 * g]);
-                const v4f dl = *reinterpret_cast<const v4f*>(&sm.delta[16 * mb + 4 * g]);
+            }
+            const float* sl2 = sm.l2[b];
+            const float* sdl = sm.delta[b];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                const v4f l2 = *reinterpret_cast<const v4f*>(&sl2[16 * mb + 4 * g]);
+                const v4f dl = *reinterpret_cast<const v4f*>(&sdl[16 * mb + 4 * g]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    float x = fmaf((float)s[r], c2, -l2[r]);
+                    float x = fmaf(unmagic(s[mb][r]), c2, -l2[r]);
                     if (QSMOOTH) x += bias2;
                     float pv = __builtin_amdgcn_exp2f(x);
                     if (need_mask && key > qbase + 16 * mb + 4 * g + r) pv = 0.f;
-                    const float dsv = pv * (dp[r] - dl[r]);
+                    const float dsv = pv * (dp[mb][r] - dl[r]);
                     p[mb][r] = pv;
                     ds[mb][r] = dsv;
                     pmax = fmaxf(pmax, pv);
@@ -202,9 +269,9 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(BwdArgs a) {
                 }
             }
         }
-        // ---- per-tile maxima over the key block's four waves
-        pmax = wave_max(pmax);
-        dsmax = wave_max(dsmax);
+        // ---- tile maxima over the key block's four waves
+        pmax = wave_max_nonneg(pmax);
+        dsmax = wave_max_nonneg(dsmax);
         if (lane == 0) {
             sm.red[kb][0][kg] = pmax;
             sm.red[kb][1][kg] = dsmax;
@@ -214,14 +281,12 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(BwdArgs a) {
         dsmax = fmaxf(fmaxf(sm.red[kb][1][0], sm.red[kb][1][1]), fmaxf(sm.red[kb][1][2], sm.red[kb][1][3]));
         const float sP = __fdiv_rn(pmax, 127.f);
         const float sS = __fdiv_rn(dsmax, 127.f);
-        if (tid == 256 * kb) sm.sds[kb] = sS;
 
         if (tile_on) {
             const float invP = sP > 0.f ? 1.f / sP : 0.f;
             const float invS = sS > 0.f ? 1.f / sS : 0.f;
-            // ---- codes; dS codes also to LDS (query on the lane, for dQ)
+            // ---- codes, query-contiguous per lane (4 queries per dword)
             v4i pop[KQ], dsop[KQ];
-            int8_t* dsl = sm.ds[kb] + kg * BQ * 16;
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
                 float pc[4], sc[4];
@@ -231,11 +296,17 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(BwdArgs a) {
                     sc[r] = fmaf(ds[mb][r], invS, kMagic);
                 }
                 pop[mb >> 2][mb & 3] = pack_magic(pc[0], pc[1], pc[2], pc[3]);
-                const int sw = pack_magic(sc[0], sc[1], sc[2], sc[3]);
-                dsop[mb >> 2][mb & 3] = sw;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) dsl[(16 * mb + 4 * g + r) * 16 + n16] = (int8_t)(sw >> (8 * r));
+                dsop[mb >> 2][mb & 3] = pack_magic(sc[0], sc[1], sc[2], sc[3]);
             }
+            // ---- dS codes and scale to the workspace (key-major, swizzled)
+            const size_t t = (size_t)bh * tph + tile_index<BQ, CAUSAL>(i, j, Tn);
+            int8_t* drow = a.dsw + t * (BQ * 64) + kr * BQ;
+#pragma unroll
+            for (int kq = 0; kq < KQ; ++kq) {
+                const int slot = (KQ * g + kq) ^ (kr & (CH - 1));
+                *reinterpret_cast<v4i*>(drow + slot * 16) = dsop[kq];
+            }
+            if (kg == 0 && lane == 0) a.sds[t] = sS;
             if (QSMOOTH) {
                 // dK bias (dS^T 1) mu_Q^T from the unquantised dS
                 float cs = 0.f;
@@ -256,39 +327,34 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(BwdArgs a) {
             // ---- dV^T += dO^^T P^,  dK^T += Q^^T dS^
             const float fv = sP * a.sdo[(size_t)bh * Tm + i];
             const float fk = sS * sqi;
+            const int kk = n16 >> 1, hf = n16 & 1;
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                v4i accv = v4i{0, 0, 0, 0}, acck = v4i{0, 0, 0, 0};
+                v4i accv = magic4, acck = magic4;
 #pragma unroll
                 for (int kq = 0; kq < KQ; ++kq) {
-                    const int chunk = kq * 4 * D + g * D + 16 * db + n16;
-                    const v4i av = reinterpret_cast<const v4i*>(sm.dot)[chunk];
-                    const v4i ak = reinterpret_cast<const v4i*>(sm.qt)[chunk];
+                    const v4i av = reinterpret_cast<const v4i*>(sdot)[kq * 4 * D + g * D + 16 * db + n16];
+                    // Q^ transposed: rows = d (lane), k = queries 64 kq + 16 (e/4) + 4 g + e%4
+                    const int qa = 64 * kq + 16 * (kk >> 2) + 4 * g + (kk & 3);
+                    const v2i r1 = lds_read_tr8(sq + off_r32(qa, 16 * db, D) + 8 * hf);
+                    const v2i r2 = lds_read_tr8(sq + off_r32(qa + 32, 16 * db, D) + 8 * hf);
+                    const v4i ak = v4i{r1[0], r1[1], r2[0], r2[1]};
                     accv = mfma16_i8(av, pop[kq], accv);
                     acck = mfma16_i8(ak, dsop[kq], acck);
                 }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    dvt[db][r] = fmaf((float)accv[r], fv, dvt[db][r]);
-                    dkt[db][r] = fmaf((float)acck[r], fk, dkt[db][r]);
+                    dvt[db][r] = fmaf(unmagic(accv[r]), fv, dvt[db][r]);
+                    dkt[db][r] = fmaf(unmagic(acck[r]), fk, dkt[db][r]);
                 }
             }
         }
-        __syncthreads();  // dS tiles complete in LDS; the staged tile is no longer read
-
-        // ---- dS codes and scales of the visible tiles to the workspace
-#pragma unroll
-        for (int b2 = 0; b2 < 2; ++b2) {
-            const int jb = 2 * jj + b2;
-            if (jb < Tn && (!CAUSAL || jb * 64 <= qbase + BQ - 1)) {
-                const size_t t = (size_t)bh * tph + tile_index<BQ, CAUSAL>(i, jb, Tn);
-                const v4i* src = reinterpret_cast<const v4i*>(sm.ds[b2]);
-                v4i* dst = reinterpret_cast<v4i*>(a.dsw + t * (BQ * 64));
-                for (int c = tid; c < BQ * 64 / 16; c += NT) dst[c] = src[c];
-                if (tid == 0) a.sds[t] = sm.sds[b2];
-            }
+        if (more && tid < BQ) {
+            sm.l2[b ^ 1][tid] = (float)((double)nL * kLog2e_d);
+            sm.delta[b ^ 1][tid] = nd;
         }
-        __syncthreads();  // LDS reused by the next tile
+        wait_vmem();       // the next tile has landed in LDS
+        __syncthreads();   // ... for every wave; this stage may be overwritten
     }
 
     // ---- write dV and dK (lane = key, 4 consecutive d per block)
@@ -307,45 +373,42 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(BwdArgs a) {
 }
 
 // dQ_i = scale * sum_j s_dS,ij s_K,j M(dS^_ij, K^_j), one workgroup per query
-// tile; wave w owns BQ/4 queries and all D columns.
+// tile; wave w owns the BQ/4 dS positions [w BQ/4, (w+1) BQ/4) (queries
+// 16 mb + 4 w + r) and all D columns.
 template <int D, int BQ, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void dq_kernel(const int8_t* __restrict__ dsw, const float* __restrict__ sds,
                                                    const int8_t* __restrict__ kt, const float* __restrict__ sk,
-                                                   float* __restrict__ dQ, int N, double scale) {
-    constexpr int QPW = BQ / 4;           // queries per wave
+                                                   float* __restrict__ dQ, int N, int BH, double scale) {
+    constexpr int QPW = BQ / 4;           // positions per wave
     constexpr int MBq = QPW / 16;
     constexpr int NB = D / 16;
+    constexpr int CH = BQ / 16;
     constexpr int DS_BYTES = BQ * 64;
     constexpr int K_BYTES = 64 * D;
-    constexpr int CH = (DS_BYTES + K_BYTES) / 16;   // 16-byte chunks per stage
-    constexpr int CPT = (CH + 255) / 256;
-    __shared__ __align__(16) int8_t stage[2][DS_BYTES + K_BYTES];
+    constexpr int ST = DS_BYTES + K_BYTES;
+    constexpr int ROUNDS = ST / 4096;
+    static_assert(ST % 4096 == 0 && DS_BYTES % 1024 == 0, "stage shape");
+    __shared__ __align__(16) int8_t stage[2][ST];
 
     const int Tn = N / 64, Tm = N / BQ;
-    const int i = CAUSAL ? (Tm - 1 - (int)blockIdx.x) : (int)blockIdx.x;  // heavy tiles first
-    const int bh = blockIdx.y;
+    int unit, bh;
+    xcd_coords(Tm, BH, unit, bh);
+    const int i = CAUSAL ? (Tm - 1 - unit) : unit;  // heavy tiles first
     const size_t head = (size_t)bh * N * D;
     const size_t tph = tiles_per_head<BQ, CAUSAL>(Tm, Tn);
     const int tid = threadIdx.x;
     const int w = tid >> 6, lane = tid & 63, n16 = lane & 15, g = lane >> 4;
     const int jend = CAUSAL ? (i + 1) * BQ / 64 : Tn;
 
-    auto load = [&](int j, v4i (&buf)[CPT]) {
+    auto load = [&](int j, int b) {
         const size_t t = (size_t)bh * tph + tile_index<BQ, CAUSAL>(i, j, Tn);
+        const int8_t* s1 = dsw + t * DS_BYTES;
+        const int8_t* s2 = kt + head + (size_t)j * K_BYTES;
 #pragma unroll
-        for (int u = 0; u < CPT; ++u) {
-            const int c = tid + u * 256;
-            if (c < DS_BYTES / 16)
-                buf[u] = reinterpret_cast<const v4i*>(dsw + t * DS_BYTES)[c];
-            else if (c < CH)
-                buf[u] = reinterpret_cast<const v4i*>(kt + head + (size_t)j * K_BYTES)[c - DS_BYTES / 16];
-        }
-    };
-    auto store = [&](int sidx, const v4i (&buf)[CPT]) {
-#pragma unroll
-        for (int u = 0; u < CPT; ++u) {
-            const int c = tid + u * 256;
-            if (c < CH) reinterpret_cast<v4i*>(stage[sidx])[c] = buf[u];
+        for (int u = 0; u < ROUNDS; ++u) {
+            const int c0 = u * 4096 + w * 1024;
+            const int8_t* src = c0 < DS_BYTES ? s1 + c0 : s2 + (c0 - DS_BYTES);
+            copy16_to_lds(src + lane * 16, stage[b] + c0);
         }
     };
 
@@ -354,61 +417,76 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const int8_t* __restrict__ d
     for (int mb = 0; mb < MBq; ++mb)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = v4f{0, 0, 0, 0};
+    const v4i magic4 = v4i{kMagicBits, kMagicBits, kMagicBits, kMagicBits};
 
-    v4i pre[CPT];
-    load(0, pre);
-    store(0, pre);
+    load(0, 0);
+    wait_vmem();
     __syncthreads();
     for (int j = 0; j < jend; ++j) {
-        const int sidx = j & 1;
-        const bool more = j + 1 < jend;
-        if (more) load(j + 1, pre);
+        const int b = j & 1;
+        if (j + 1 < jend) load(j + 1, b ^ 1);
         const size_t t = (size_t)bh * tph + tile_index<BQ, CAUSAL>(i, j, Tn);
         const float cj = (float)((double)sds[t] * (double)sk[(size_t)bh * Tn + j] * scale);
-        const v4i* lds = reinterpret_cast<const v4i*>(stage[sidx]);
-        const v4i* lk = reinterpret_cast<const v4i*>(stage[sidx] + DS_BYTES);
+        const int8_t* lds = stage[b];
+        const v4i* lk = reinterpret_cast<const v4i*>(stage[b] + DS_BYTES);
+        // A = dS^ rows (positions), k = keys 16 g + e, read transposed from the
+        // key-major rows: two transpose reads of eight keys each
         v4i av[MBq];
 #pragma unroll
-        for (int mb = 0; mb < MBq; ++mb) av[mb] = lds[g * BQ + QPW * w + 16 * mb + n16];
+        for (int mb = 0; mb < MBq; ++mb) {
+            const int c = (QPW * w + 16 * mb) >> 4;
+            v2i r[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int krow = 16 * g + 8 * h + (n16 >> 1);
+                const int slot = c ^ (krow & (CH - 1));
+                r[h] = lds_read_tr8(lds + krow * BQ + slot * 16 + 8 * (n16 & 1));
+            }
+            av[mb] = v4i{r[0][0], r[0][1], r[1][0], r[1][1]};
+        }
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            const v4i bv = lk[g * D + 16 * nb + n16];
+            const v4i bv = lk[g * D + 16 * nb + n16];   // K^ C64N: column d, k = key 16 g + e
 #pragma unroll
             for (int mb = 0; mb < MBq; ++mb) {
-                const v4i x = mfma16_i8(av[mb], bv, v4i{0, 0, 0, 0});
+                const v4i x = mfma16_i8(av[mb], bv, magic4);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[mb][nb][r] = fmaf((float)x[r], cj, acc[mb][nb][r]);
+                for (int r = 0; r < 4; ++r) acc[mb][nb][r] = fmaf(unmagic(x[r]), cj, acc[mb][nb][r]);
             }
         }
-        if (more) {
-            __syncthreads();
-            store(sidx ^ 1, pre);
-            __syncthreads();
-        }
+        wait_vmem();
+        __syncthreads();
     }
-    float* out = dQ + head + (size_t)(i * BQ + QPW * w) * D;
+    // position p = QPW w + 16 mb + 4 g + r  ->  query 64 mb + 16 g + 4 w + r
+    float* out = dQ + head + (size_t)(i * BQ) * D;
 #pragma unroll
     for (int mb = 0; mb < MBq; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+        for (int r = 0; r < 4; ++r) {
+            const int qrow = 64 * mb + 16 * g + 4 * w + r;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) out[(size_t)(16 * mb + 4 * g + r) * D + 16 * nb + n16] = acc[mb][nb][r];
+            for (int nb = 0; nb < NB; ++nb) out[(size_t)qrow * D + 16 * nb + n16] = acc[mb][nb][r];
+        }
 }
 
 template <bool BF16, int D, int BQ, bool CAUSAL>
-hipError_t bwd_dispatch(const Dims& d, const BwdArgs& a, hipStream_t s) {
-    const dim3 grid((d.Tn() + 1) / 2, d.BH());
+hipError_t bwd_dispatch(const Dims& d, const BwdArgs& a, const int8_t* kt, float* dQ, hipStream_t s) {
+    const int gx = (d.Tn() + 1) / 2;
+    const dim3 grid(gx * d.BH());
     if (d.q_smooth) bwd_kernel<BF16, D, BQ, CAUSAL, true><<<grid, 512, 0, s>>>(a);
     else bwd_kernel<BF16, D, BQ, CAUSAL, false><<<grid, 512, 0, s>>>(a);
-    dq_kernel<D, BQ, CAUSAL><<<dim3(d.Tm(), d.BH()), 256, 0, s>>>(a.dsw, a.sds, a.kt, a.sk, a.dQ, d.N, d.scale);
+    dq_kernel<D, BQ, CAUSAL><<<dim3(d.Tm() * d.BH()), 256, 0, s>>>(a.dsw, a.sds, kt, a.sk, dQ, d.N, d.BH(),
+                                                                   d.scale);
     return hipGetLastError();
 }
 
 template <bool BF16, int D>
-hipError_t bwd_dispatch_bq(const Dims& d, const BwdArgs& a, hipStream_t s) {
+hipError_t bwd_dispatch_bq(const Dims& d, const BwdArgs& a, const int8_t* kt, float* dQ, hipStream_t s) {
     if (d.bq == 128)
-        return d.causal ? bwd_dispatch<BF16, D, 128, true>(d, a, s) : bwd_dispatch<BF16, D, 128, false>(d, a, s);
-    return d.causal ? bwd_dispatch<BF16, D, 64, true>(d, a, s) : bwd_dispatch<BF16, D, 64, false>(d, a, s);
+        return d.causal ? bwd_dispatch<BF16, D, 128, true>(d, a, kt, dQ, s)
+                        : bwd_dispatch<BF16, D, 128, false>(d, a, kt, dQ, s);
+    return d.causal ? bwd_dispatch<BF16, D, 64, true>(d, a, kt, dQ, s)
+                    : bwd_dispatch<BF16, D, 64, false>(d, a, kt, dQ, s);
 }
 
 size_t total_tiles(const Dims& d) {
@@ -427,10 +505,11 @@ hipError_t launch_bwd(const Dims& d, const sage_qtensors& qk, const sage_dotenso
                       void* workspace, float* dQ, float* dK, float* dV, hipStream_t s) {
     int8_t* dsw = static_cast<int8_t*>(workspace);
     float* sds = reinterpret_cast<float*>(dsw + codes_bytes(d));
-    const BwdArgs a{qk.q,  qk.qt, qk.sq, qk.k, qk.kt, qk.sk, qk.vr, qk.mu_q, qk.qk_bias, dos.delta, dos.dot,
-                    dos.sdo, dos.dor, L, dsw, sds, dQ, dK, dV, d.N, d.scale};
-    if (d.bf16) return d.D == 128 ? bwd_dispatch_bq<true, 128>(d, a, s) : bwd_dispatch_bq<true, 64>(d, a, s);
-    return d.D == 128 ? bwd_dispatch_bq<false, 128>(d, a, s) : bwd_dispatch_bq<false, 64>(d, a, s);
+    const BwdArgs a{qk.q,  qk.sq,    qk.k,    qk.sk,   qk.vr, qk.mu_q, qk.qk_bias, dos.delta, dos.dot,
+                    dos.sdo, dos.dor, L, dsw, sds, dK, dV, d.N, d.BH(), d.scale};
+    if (d.bf16)
+        return d.D == 128 ? bwd_dispatch_bq<true, 128>(d, a, qk.kt, dQ, s) : bwd_dispatch_bq<true, 64>(d, a, qk.kt, dQ, s);
+    return d.D == 128 ? bwd_dispatch_bq<false, 128>(d, a, qk.kt, dQ, s) : bwd_dispatch_bq<false, 64>(d, a, qk.kt, dQ, s);
 }
 
 }  // namespace sage

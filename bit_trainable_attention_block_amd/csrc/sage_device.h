@@ -90,6 +90,19 @@ __device__ __forceinline__ float wave_max(float v) {
     for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
     return v;
 }
+// Maximum over the wave of non-negative floats, without LDS: the float bits
+// of non-negative values order like integers, so rows of 16 lanes reduce by
+// DPP rotations and the four row results by readlane.  Uniform result.
+__device__ __forceinline__ float wave_max_nonneg(float v) {
+    int x = __float_as_int(v);
+    x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x128, 0xf, 0xf, false));  // row_ror:8
+    x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x124, 0xf, 0xf, false));  // row_ror:4
+    x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x122, 0xf, 0xf, false));  // row_ror:2
+    x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x121, 0xf, 0xf, false));  // row_ror:1
+    const int a = max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16));
+    const int b = max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48));
+    return __int_as_float(max(a, b));
+}
 __device__ __forceinline__ double wave_sum_d(double v, int width) {
     for (int o = width >> 1; o >= 1; o >>= 1) v += __shfl_xor(v, o);
     return v;
@@ -106,7 +119,35 @@ __device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
            ((uint32_t)(d & 255) << 24);
 }
 
+// ---------------------------------------------------------------- LDS
+typedef int v2i __attribute__((ext_vector_type(2)));
+#define SAGE_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// ds_read_b64_tr_b8: the 16 lanes of each lane group supply eight bytes each;
+// lanes 2k and 2k+1 together name row k (16 bytes) of an 8 x 16 byte matrix,
+// and lane i receives column i (byte k of the result = row k, byte i).
+__device__ __forceinline__ v2i lds_read_tr8(const int8_t* p) {
+    return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (__attribute__((address_space(3))) v2i*)(const_cast<int8_t*>(p)));
+}
+
+// Asynchronous 16-byte copy global -> LDS: lane l's 16 bytes from src land at
+// dst_wave + 16 * l (dst_wave must be the same for the whole wave).  Tracked
+// by vmcnt; wait with wait_vmem() before a barrier that publishes the data.
+__device__ __forceinline__ void copy16_to_lds(const void* src, void* dst_wave) {
+    __builtin_amdgcn_global_load_lds(src, SAGE_LDS(dst_wave), 16, 0, 0);
+}
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // ---------------------------------------------------------------- MFMA
+// Integer products with a float conversion for free: an int32 accumulator
+// started at the bits of 1.5 * 2^23 holds, read as a float, exactly
+// 1.5 * 2^23 + sum while |sum| < 2^22 (every product here has
+// |sum| <= 127 * 127 * 128 < 2^21), so one exact subtraction recovers it.
+constexpr int kMagicBits = 0x4B400000;
+constexpr float kMagicF = 12582912.0f;
+__device__ __forceinline__ float unmagic(int x) { return __int_as_float(x) - kMagicF; }
+
 __device__ __forceinline__ v16i mfma32_i8(v4i a, v4i b, v16i c) {
     return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
 }
