@@ -35,33 +35,13 @@
 // stored at chunk slot c ^ (kr mod BQ/16), which spreads the transpose reads
 // of eight consecutive rows over distinct LDS banks.
 #include <algorithm>
+#include <type_traits>
 
 #include "sage_device.h"
 #include "sage_internal.h"
 
 namespace sage {
 namespace {
-
-struct BwdArgs {
-    const int8_t* q;
-    const float* sq;
-    const int8_t* k;
-    const float* sk;
-    const u16* vr;
-    const float* mu_q;
-    const float* qk_bias;
-    const float* delta;
-    const int8_t* dot;
-    const float* sdo;
-    const u16* dor;
-    const float* L;
-    int8_t* dsw;   // dS codes per tile (layout above)
-    float* sds;    // dS scale per tile, [bh][tile]
-    float* dK;
-    float* dV;
-    int N, BH;
-    double scale;  // softmax scale
-};
 
 constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
 
@@ -102,27 +82,23 @@ __device__ __forceinline__ void xcd_coords(int units, int BH, int& unit, int& bh
 }
 
 template <int BQ, int D>
-struct BwdSmem {
-    int8_t q[2][BQ * D];     // Q codes, R32
-    int8_t dot[2][BQ * D];   // dO codes, C64P
-    u16 dor[2][BQ * D];      // dO, R16H
-    float l2[2][BQ];         // L * log2 e
-    float delta[2][BQ];
-    float red[2][2][4];      // [key block][P | dS][key group]
+struct BwdStage {
+    int8_t q[BQ * D];     // Q codes, R32
+    int8_t dot[BQ * D];   // dO codes, C64P
+    u16 dor[BQ * D];      // dO, R16H
+    float l2[BQ];         // L * log2 e
+    float delta[BQ];
 };
 
-// Asynchronous copy of query tile qbase (Q codes, dO codes, dO) into stage b.
+// Asynchronous copy of query tile qbase (Q codes, dO codes, dO) into a stage.
 // The three regions are contiguous BQ*D, BQ*D and 2*BQ*D byte runs; each
 // wave instruction moves 1 KiB.
 template <int BQ, int D>
-__device__ __forceinline__ void stage_query_tile(BwdSmem<BQ, D>& sm, int b, const BwdArgs& a, size_t head,
-                                                 int qbase) {
+__device__ __forceinline__ void stage_query_tile(BwdStage<BQ, D>& st, const int8_t* q, const int8_t* dot,
+                                                 const u16* dor, int w, int lane) {
     constexpr int QB = BQ * D, TOT = 4 * QB, ROUNDS = TOT / (8 * 1024);
     static_assert(TOT % (8 * 1024) == 0 && QB % 1024 == 0, "stage shape");
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int8_t* q = a.q + head + (size_t)qbase * D;
-    const int8_t* dot = a.dot + head + (size_t)qbase * D;
-    const int8_t* dor = reinterpret_cast<const int8_t*>(a.dor + head + (size_t)qbase * D);
+    const int8_t* dorb = reinterpret_cast<const int8_t*>(dor);
 #pragma unroll
     for (int u = 0; u < ROUNDS; ++u) {
         const int c0 = u * 8 * 1024 + w * 1024;
@@ -130,35 +106,46 @@ __device__ __forceinline__ void stage_query_tile(BwdSmem<BQ, D>& sm, int b, cons
         int8_t* dst;
         if (c0 < QB) {
             src = q + c0;
-            dst = sm.q[b] + c0;
+            dst = st.q + c0;
         } else if (c0 < 2 * QB) {
             src = dot + (c0 - QB);
-            dst = sm.dot[b] + (c0 - QB);
+            dst = st.dot + (c0 - QB);
         } else {
-            src = dor + (c0 - 2 * QB);
-            dst = reinterpret_cast<int8_t*>(sm.dor[b]) + (c0 - 2 * QB);
+            src = dorb + (c0 - 2 * QB);
+            dst = reinterpret_cast<int8_t*>(st.dor) + (c0 - 2 * QB);
         }
         copy16_to_lds(src + lane * 16, dst);
     }
 }
 
+// The two stages are separate LDS objects and the tile loop is unrolled by
+// two, so the compiler sees that the asynchronous copy into one stage never
+// aliases the reads of the other and does not wait for it.
 template <bool BF16, int D, int BQ, bool CAUSAL, bool QSMOOTH>
-__global__ __launch_bounds__(512, 1) void bwd_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512, 1) void bwd_kernel(
+    const int8_t* __restrict__ q, const float* __restrict__ sq, const int8_t* __restrict__ k,
+    const float* __restrict__ sk, const u16* __restrict__ vr, const float* __restrict__ mu_q,
+    const float* __restrict__ qk_bias, const float* __restrict__ delta, const int8_t* __restrict__ dot,
+    const float* __restrict__ sdo, const u16* __restrict__ dor, const float* __restrict__ L,
+    int8_t* __restrict__ dsw, float* __restrict__ sds, float* __restrict__ dK, float* __restrict__ dV, int N,
+    int BH, double scale) {
     constexpr int MB = BQ / 16;   // 16-query blocks per tile
     constexpr int KQ = BQ / 64;   // i8 contraction steps over queries
     constexpr int KS8 = D / 64;   // i8 contraction steps over d
     constexpr int KSH = D / 32;   // 16-bit contraction steps over d
     constexpr int DB = D / 16;    // 16-wide blocks of d
     constexpr int CH = BQ / 16;   // 16-byte chunks per dS key row
-    __shared__ __align__(16) BwdSmem<BQ, D> sm;
+    __shared__ __align__(16) BwdStage<BQ, D> st0;
+    __shared__ __align__(16) BwdStage<BQ, D> st1;
+    __shared__ float red[2][2][4];   // [key block][P | dS][key group]
 
-    const int N = a.N;
     const int Tn = N / 64, Tm = N / BQ;
     int jj, bh;
-    xcd_coords((Tn + 1) / 2, a.BH, jj, bh);
+    xcd_coords((Tn + 1) / 2, BH, jj, bh);
     const size_t head = (size_t)bh * N * D;
     const int tid = threadIdx.x;
-    const int w = tid >> 6, lane = tid & 63, n16 = lane & 15, g = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    const int lane = tid & 63, n16 = lane & 15, g = lane >> 4;
     const int kb = w >> 2, kg = w & 3;
     const int j = 2 * jj + kb;        // this wave's key block
     const bool kv_on = j < Tn;        // the second block of a ragged tail may not exist
@@ -170,11 +157,11 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(BwdArgs a) {
     if (kv_on) {
 #pragma unroll
         for (int ks = 0; ks < KS8; ++ks)
-            kop[ks] = *reinterpret_cast<const v4i*>(a.k + head + off_r32(key, 64 * ks + 16 * g, D));
+            kop[ks] = *reinterpret_cast<const v4i*>(k + head + off_r32(key, 64 * ks + 16 * g, D));
 #pragma unroll
         for (int ks = 0; ks < KSH; ++ks)
-            vop[ks] = *reinterpret_cast<const v4i*>(a.vr + head + off_r16h(key, 32 * ks + 8 * g, D));
-        skj = a.sk[(size_t)bh * Tn + j];
+            vop[ks] = *reinterpret_cast<const v4i*>(vr + head + off_r16h(key, 32 * ks + 8 * g, D));
+        skj = sk[(size_t)bh * Tn + j];
     }
 
     v4f dvt[DB], dkt[DB];
@@ -187,45 +174,36 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(BwdArgs a) {
 
     const size_t tph = tiles_per_head<BQ, CAUSAL>(Tm, Tn);
     const int istart = CAUSAL ? (2 * jj * 64) / BQ : 0;
-    const float* Lh = a.L + (size_t)bh * N;
-    const float* dlh = a.delta + (size_t)bh * N;
+    const float* Lh = L + (size_t)bh * N;
+    const float* dlh = delta + (size_t)bh * N;
+    const int8_t* qh = q + head;
+    const int8_t* doth = dot + head;
+    const u16* dorh = dor + head;
 
-    // ---- prologue: first query tile
-    stage_query_tile<BQ, D>(sm, 0, a, head, istart * BQ);
-    if (tid < BQ) {
-        sm.l2[0][tid] = (float)((double)Lh[istart * BQ + tid] * kLog2e_d);
-        sm.delta[0][tid] = dlh[istart * BQ + tid];
-    }
-    wait_vmem();
-    __syncthreads();
-
-    for (int i = istart; i < Tm; ++i) {
-        const int b = (i - istart) & 1;
+    // One query tile, read from `cur`; the next one is copied into `nxt`.
+    auto step = [&](int i, BwdStage<BQ, D>& cur, BwdStage<BQ, D>& nxt) __attribute__((always_inline)) {
         const int qbase = i * BQ;
         const bool more = i + 1 < Tm;
-        // ---- next tile: asynchronous copy into the other stage (last read
-        // before the previous iteration's closing barrier)
+        // small loads of the next tile first: waiting for them never waits
+        // for the copies issued after them
         float nL = 0.f, nd = 0.f;
-        if (more) {
-            stage_query_tile<BQ, D>(sm, b ^ 1, a, head, qbase + BQ);
-            if (tid < BQ) {
-                nL = Lh[qbase + BQ + tid];
-                nd = dlh[qbase + BQ + tid];
-            }
+        if (more && tid < BQ) {
+            nL = Lh[qbase + BQ + tid];
+            nd = dlh[qbase + BQ + tid];
         }
-        const int8_t* sq = sm.q[b];
-        const int8_t* sdot = sm.dot[b];
-        const u16* sdor = sm.dor[b];
+        if (more)
+            stage_query_tile<BQ, D>(nxt, qh + (size_t)(qbase + BQ) * D, doth + (size_t)(qbase + BQ) * D,
+                                    dorh + (size_t)(qbase + BQ) * D, w, lane);
 
         const bool tile_on = kv_on && (!CAUSAL || j * 64 <= qbase + BQ - 1);
-        const float sqi = a.sq[(size_t)bh * Tm + i];
+        const float sqi = sq[(size_t)bh * Tm + i];
+        const float sdoi = sdo[(size_t)bh * Tm + i];
         float p[MB][4], ds[MB][4];
         float pmax = 0.f, dsmax = 0.f;
         if (tile_on) {
-            const float c2 = (float)((double)sqi * (double)skj * a.scale * kLog2e_d);  // one rounding
+            const float c2 = (float)((double)sqi * (double)skj * scale * kLog2e_d);  // one rounding
             float bias2 = 0.f;
-            if (QSMOOTH) bias2 = (float)((double)a.qk_bias[((size_t)bh * Tm + i) * N + key] * kLog2e_d);
-            const bool need_mask = CAUSAL && (j * 64 + 63 > qbase);
+            if (QSMOOTH) bias2 = (float)((double)qk_bias[((size_t)bh * Tm + i) * N + key] * kLog2e_d);
             // ---- S and dP for this wave's 16 keys and all BQ queries
             v4i s[MB];
             v4f dp[MB];
@@ -235,7 +213,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(BwdArgs a) {
                 s[mb] = magic4;
 #pragma unroll
                 for (int ks = 0; ks < KS8; ++ks) {
-                    const v4i av = *reinterpret_cast<const v4i*>(sq + off_r32(row, 64 * ks + 16 * g, D));
+                    const v4i av = *reinterpret_cast<const v4i*>(cur.q + off_r32(row, 64 * ks + 16 * g, D));
                     s[mb] = mfma16_i8(av, kop[ks], s[mb]);
                 }
             }
@@ -245,22 +223,19 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(BwdArgs a) {
                 dp[mb] = v4f{0, 0, 0, 0};
 #pragma unroll
                 for (int ks = 0; ks < KSH; ++ks) {
-                    const v4i av = *reinterpret_cast<const v4i*>(sdor + off_r16h(row, 32 * ks + 8 * g, D));
+                    const v4i av = *reinterpret_cast<const v4i*>(cur.dor + off_r16h(row, 32 * ks + 8 * g, D));
                     dp[mb] = mfma16_h<BF16>(av, vop[ks], dp[mb]);
                 }
             }
-            const float* sl2 = sm.l2[b];
-            const float* sdl = sm.delta[b];
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
-                const v4f l2 = *reinterpret_cast<const v4f*>(&sl2[16 * mb + 4 * g]);
-                const v4f dl = *reinterpret_cast<const v4f*>(&sdl[16 * mb + 4 * g]);
+                const v4f l2 = *reinterpret_cast<const v4f*>(&cur.l2[16 * mb + 4 * g]);
+                const v4f dl = *reinterpret_cast<const v4f*>(&cur.delta[16 * mb + 4 * g]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     float x = fmaf(unmagic(s[mb][r]), c2, -l2[r]);
                     if (QSMOOTH) x += bias2;
-                    float pv = __builtin_amdgcn_exp2f(x);
-                    if (need_mask && key > qbase + 16 * mb + 4 * g + r) pv = 0.f;
+                    const float pv = __builtin_amdgcn_exp2f(x);
                     const float dsv = pv * (dp[mb][r] - dl[r]);
                     p[mb][r] = pv;
                     ds[mb][r] = dsv;
@@ -268,17 +243,37 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(BwdArgs a) {
                     dsmax = fmaxf(dsmax, fabsf(dsv));
                 }
             }
+            if (CAUSAL && (j * 64 + 63 > qbase)) {
+                // diagonal tile: zero the keys after each query (by selection,
+                // so an overflowed exp there never reaches a product) and take
+                // the maxima again
+                pmax = 0.f;
+                dsmax = 0.f;
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const bool vis = key <= qbase + 16 * mb + 4 * g + r;
+                        p[mb][r] = vis ? p[mb][r] : 0.f;
+                        ds[mb][r] = vis ? ds[mb][r] : 0.f;
+                        pmax = fmaxf(pmax, p[mb][r]);
+                        dsmax = fmaxf(dsmax, fabsf(ds[mb][r]));
+                    }
+            }
         }
-        // ---- tile maxima over the key block's four waves
+        // ---- tile maxima over the key block's four waves (raw barrier: the
+        // copy of the next tile stays in flight)
         pmax = wave_max_nonneg(pmax);
         dsmax = wave_max_nonneg(dsmax);
         if (lane == 0) {
-            sm.red[kb][0][kg] = pmax;
-            sm.red[kb][1][kg] = dsmax;
+            red[kb][0][kg] = pmax;
+            red[kb][1][kg] = dsmax;
         }
-        __syncthreads();
-        pmax = fmaxf(fmaxf(sm.red[kb][0][0], sm.red[kb][0][1]), fmaxf(sm.red[kb][0][2], sm.red[kb][0][3]));
-        dsmax = fmaxf(fmaxf(sm.red[kb][1][0], sm.red[kb][1][1]), fmaxf(sm.red[kb][1][2], sm.red[kb][1][3]));
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        pmax = fmaxf(fmaxf(red[kb][0][0], red[kb][0][1]), fmaxf(red[kb][0][2], red[kb][0][3]));
+        dsmax = fmaxf(fmaxf(red[kb][1][0], red[kb][1][1]), fmaxf(red[kb][1][2], red[kb][1][3]));
         const float sP = __fdiv_rn(pmax, 127.f);
         const float sS = __fdiv_rn(dsmax, 127.f);
 
@@ -300,13 +295,13 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(BwdArgs a) {
             }
             // ---- dS codes and scale to the workspace (key-major, swizzled)
             const size_t t = (size_t)bh * tph + tile_index<BQ, CAUSAL>(i, j, Tn);
-            int8_t* drow = a.dsw + t * (BQ * 64) + kr * BQ;
+            int8_t* drow = dsw + t * (BQ * 64) + kr * BQ;
 #pragma unroll
             for (int kq = 0; kq < KQ; ++kq) {
                 const int slot = (KQ * g + kq) ^ (kr & (CH - 1));
                 *reinterpret_cast<v4i*>(drow + slot * 16) = dsop[kq];
             }
-            if (kg == 0 && lane == 0) a.sds[t] = sS;
+            if (kg == 0 && lane == 0) sds[t] = sS;
             if (QSMOOTH) {
                 // dK bias (dS^T 1) mu_Q^T from the unquantised dS
                 float cs = 0.f;
@@ -316,7 +311,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(BwdArgs a) {
                     for (int r = 0; r < 4; ++r) cs += ds[mb][r];
                 cs += __shfl_xor(cs, 16);
                 cs += __shfl_xor(cs, 32);
-                const float* mq = a.mu_q + ((size_t)bh * Tm + i) * D;
+                const float* mq = mu_q + ((size_t)bh * Tm + i) * D;
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
                     const v4f m4 = *reinterpret_cast<const v4f*>(mq + 16 * db + 4 * g);
@@ -325,7 +320,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(BwdArgs a) {
                 }
             }
             // ---- dV^T += dO^^T P^,  dK^T += Q^^T dS^
-            const float fv = sP * a.sdo[(size_t)bh * Tm + i];
+            const float fv = sP * sdoi;
             const float fk = sS * sqi;
             const int kk = n16 >> 1, hf = n16 & 1;
 #pragma unroll
@@ -333,11 +328,11 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(BwdArgs a) {
                 v4i accv = magic4, acck = magic4;
 #pragma unroll
                 for (int kq = 0; kq < KQ; ++kq) {
-                    const v4i av = reinterpret_cast<const v4i*>(sdot)[kq * 4 * D + g * D + 16 * db + n16];
+                    const v4i av = reinterpret_cast<const v4i*>(cur.dot)[kq * 4 * D + g * D + 16 * db + n16];
                     // Q^ transposed: rows = d (lane), k = queries 64 kq + 16 (e/4) + 4 g + e%4
                     const int qa = 64 * kq + 16 * (kk >> 2) + 4 * g + (kk & 3);
-                    const v2i r1 = lds_read_tr8(sq + off_r32(qa, 16 * db, D) + 8 * hf);
-                    const v2i r2 = lds_read_tr8(sq + off_r32(qa + 32, 16 * db, D) + 8 * hf);
+                    const v2i r1 = lds_read_tr8(cur.q + off_r32(qa, 16 * db, D) + 8 * hf);
+                    const v2i r2 = lds_read_tr8(cur.q + off_r32(qa + 32, 16 * db, D) + 8 * hf);
                     const v4i ak = v4i{r1[0], r1[1], r2[0], r2[1]};
                     accv = mfma16_i8(av, pop[kq], accv);
                     acck = mfma16_i8(ak, dsop[kq], acck);
@@ -350,31 +345,52 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(BwdArgs a) {
             }
         }
         if (more && tid < BQ) {
-            sm.l2[b ^ 1][tid] = (float)((double)nL * kLog2e_d);
-            sm.delta[b ^ 1][tid] = nd;
+            asm volatile("" : "+v"(nL), "+v"(nd));   // keep the conversion here, after the work
+            nxt.l2[tid] = (float)((double)nL * kLog2e_d);
+            nxt.delta[tid] = nd;
         }
-        wait_vmem();       // the next tile has landed in LDS
-        __syncthreads();   // ... for every wave; this stage may be overwritten
+        __syncthreads();   // the next tile has landed in LDS for every wave; `cur` may be overwritten
+    };
+
+    // ---- prologue: first query tile into st0
+    stage_query_tile<BQ, D>(st0, qh + (size_t)istart * BQ * D, doth + (size_t)istart * BQ * D,
+                            dorh + (size_t)istart * BQ * D, w, lane);
+    if (tid < BQ) {
+        st0.l2[tid] = (float)((double)Lh[istart * BQ + tid] * kLog2e_d);
+        st0.delta[tid] = dlh[istart * BQ + tid];
+    }
+    __syncthreads();
+    for (int i = istart; i < Tm; i += 2) {
+        step(i, st0, st1);
+        if (i + 1 < Tm) step(i + 1, st1, st0);
     }
 
     // ---- write dV and dK (lane = key, 4 consecutive d per block)
     if (kv_on) {
-        float* dV = a.dV + head + (size_t)key * D;
-        float* dK = a.dK + head + (size_t)key * D;
+        float* dVk = dV + head + (size_t)key * D;
+        float* dKk = dK + head + (size_t)key * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
             v4f kv;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) kv[r] = (float)((double)dkt[db][r] * a.scale);
-            *reinterpret_cast<v4f*>(dV + 16 * db + 4 * g) = dvt[db];
-            *reinterpret_cast<v4f*>(dK + 16 * db + 4 * g) = kv;
+            for (int r = 0; r < 4; ++r) kv[r] = (float)((double)dkt[db][r] * scale);
+            *reinterpret_cast<v4f*>(dVk + 16 * db + 4 * g) = dvt[db];
+            *reinterpret_cast<v4f*>(dKk + 16 * db + 4 * g) = kv;
         }
     }
 }
 
 // dQ_i = scale * sum_j s_dS,ij s_K,j M(dS^_ij, K^_j), one workgroup per query
 // tile; wave w owns the BQ/4 dS positions [w BQ/4, (w+1) BQ/4) (queries
-// 16 mb + 4 w + r) and all D columns.
+// 16 mb + 4 w + r) and all D columns.  Each key tile (its dS codes and the
+// K codes, column tiles) streams through two LDS stages (separate objects,
+// loop unrolled by two) filled one tile ahead by asynchronous copies.
+template <int BQ, int D>
+struct DqStage {
+    int8_t ds[BQ * 64];   // dS codes of one tile, key-major (workspace layout)
+    int8_t k[64 * D];     // K codes of the key block, C64N
+};
+
 template <int D, int BQ, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void dq_kernel(const int8_t* __restrict__ dsw, const float* __restrict__ sds,
                                                    const int8_t* __restrict__ kt, const float* __restrict__ sk,
@@ -385,10 +401,10 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const int8_t* __restrict__ d
     constexpr int CH = BQ / 16;
     constexpr int DS_BYTES = BQ * 64;
     constexpr int K_BYTES = 64 * D;
-    constexpr int ST = DS_BYTES + K_BYTES;
-    constexpr int ROUNDS = ST / 4096;
-    static_assert(ST % 4096 == 0 && DS_BYTES % 1024 == 0, "stage shape");
-    __shared__ __align__(16) int8_t stage[2][ST];
+    constexpr int ROUNDS = (DS_BYTES + K_BYTES) / 4096;
+    static_assert((DS_BYTES + K_BYTES) % 4096 == 0 && DS_BYTES % 1024 == 0, "stage shape");
+    __shared__ __align__(16) DqStage<BQ, D> st0;
+    __shared__ __align__(16) DqStage<BQ, D> st1;
 
     const int Tn = N / 64, Tm = N / BQ;
     int unit, bh;
@@ -397,18 +413,19 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const int8_t* __restrict__ d
     const size_t head = (size_t)bh * N * D;
     const size_t tph = tiles_per_head<BQ, CAUSAL>(Tm, Tn);
     const int tid = threadIdx.x;
-    const int w = tid >> 6, lane = tid & 63, n16 = lane & 15, g = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, n16 = lane & 15, g = lane >> 4;
     const int jend = CAUSAL ? (i + 1) * BQ / 64 : Tn;
 
-    auto load = [&](int j, int b) {
+    auto load = [&](int j, DqStage<BQ, D>& st) __attribute__((always_inline)) {
         const size_t t = (size_t)bh * tph + tile_index<BQ, CAUSAL>(i, j, Tn);
         const int8_t* s1 = dsw + t * DS_BYTES;
         const int8_t* s2 = kt + head + (size_t)j * K_BYTES;
 #pragma unroll
         for (int u = 0; u < ROUNDS; ++u) {
             const int c0 = u * 4096 + w * 1024;
-            const int8_t* src = c0 < DS_BYTES ? s1 + c0 : s2 + (c0 - DS_BYTES);
-            copy16_to_lds(src + lane * 16, stage[b] + c0);
+            if (c0 < DS_BYTES) copy16_to_lds(s1 + c0 + lane * 16, st.ds + c0);
+            else copy16_to_lds(s2 + (c0 - DS_BYTES) + lane * 16, st.k + (c0 - DS_BYTES));
         }
     };
 
@@ -419,16 +436,11 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const int8_t* __restrict__ d
         for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = v4f{0, 0, 0, 0};
     const v4i magic4 = v4i{kMagicBits, kMagicBits, kMagicBits, kMagicBits};
 
-    load(0, 0);
-    wait_vmem();
-    __syncthreads();
-    for (int j = 0; j < jend; ++j) {
-        const int b = j & 1;
-        if (j + 1 < jend) load(j + 1, b ^ 1);
+    auto step = [&](int j, DqStage<BQ, D>& cur, DqStage<BQ, D>& nxt) __attribute__((always_inline)) {
         const size_t t = (size_t)bh * tph + tile_index<BQ, CAUSAL>(i, j, Tn);
         const float cj = (float)((double)sds[t] * (double)sk[(size_t)bh * Tn + j] * scale);
-        const int8_t* lds = stage[b];
-        const v4i* lk = reinterpret_cast<const v4i*>(stage[b] + DS_BYTES);
+        if (j + 1 < jend) load(j + 1, nxt);
+        const v4i* lk = reinterpret_cast<const v4i*>(cur.k);
         // A = dS^ rows (positions), k = keys 16 g + e, read transposed from the
         // key-major rows: two transpose reads of eight keys each
         v4i av[MBq];
@@ -440,7 +452,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const int8_t* __restrict__ d
             for (int h = 0; h < 2; ++h) {
                 const int krow = 16 * g + 8 * h + (n16 >> 1);
                 const int slot = c ^ (krow & (CH - 1));
-                r[h] = lds_read_tr8(lds + krow * BQ + slot * 16 + 8 * (n16 & 1));
+                r[h] = lds_read_tr8(cur.ds + krow * BQ + slot * 16 + 8 * (n16 & 1));
             }
             av[mb] = v4i{r[0][0], r[0][1], r[1][0], r[1][1]};
         }
@@ -454,8 +466,14 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const int8_t* __restrict__ d
                 for (int r = 0; r < 4; ++r) acc[mb][nb][r] = fmaf(unmagic(x[r]), cj, acc[mb][nb][r]);
             }
         }
-        wait_vmem();
-        __syncthreads();
+        __syncthreads();   // next tile landed for every wave; `cur` may be overwritten
+    };
+
+    load(0, st0);
+    __syncthreads();
+    for (int j = 0; j < jend; j += 2) {
+        step(j, st0, st1);
+        if (j + 1 < jend) step(j + 1, st1, st0);
     }
     // position p = QPW w + 16 mb + 4 g + r  ->  query 64 mb + 16 g + 4 w + r
     float* out = dQ + head + (size_t)(i * BQ) * D;
@@ -469,24 +487,34 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const int8_t* __restrict__ d
         }
 }
 
+// Device pointers of one sage_bwd call.
+struct BwdPtrs {
+    const sage_qtensors* qk;
+    const sage_dotensors* dos;
+    const float* L;
+    int8_t* dsw;
+    float* sds;
+    float *dQ, *dK, *dV;
+};
+
 template <bool BF16, int D, int BQ, bool CAUSAL>
-hipError_t bwd_dispatch(const Dims& d, const BwdArgs& a, const int8_t* kt, float* dQ, hipStream_t s) {
-    const int gx = (d.Tn() + 1) / 2;
-    const dim3 grid(gx * d.BH());
-    if (d.q_smooth) bwd_kernel<BF16, D, BQ, CAUSAL, true><<<grid, 512, 0, s>>>(a);
-    else bwd_kernel<BF16, D, BQ, CAUSAL, false><<<grid, 512, 0, s>>>(a);
-    dq_kernel<D, BQ, CAUSAL><<<dim3(d.Tm() * d.BH()), 256, 0, s>>>(a.dsw, a.sds, kt, a.sk, dQ, d.N, d.BH(),
+hipError_t bwd_dispatch(const Dims& d, const BwdPtrs& p, hipStream_t s) {
+    const sage_qtensors& qk = *p.qk;
+    const sage_dotensors& dos = *p.dos;
+    const dim3 grid(((d.Tn() + 1) / 2) * d.BH());
+    auto kern = d.q_smooth ? bwd_kernel<BF16, D, BQ, CAUSAL, true> : bwd_kernel<BF16, D, BQ, CAUSAL, false>;
+    kern<<<grid, 512, 0, s>>>(qk.q, qk.sq, qk.k, qk.sk, qk.vr, qk.mu_q, qk.qk_bias, dos.delta, dos.dot, dos.sdo,
+                              dos.dor, p.L, p.dsw, p.sds, p.dK, p.dV, d.N, d.BH(), d.scale);
+    dq_kernel<D, BQ, CAUSAL><<<dim3(d.Tm() * d.BH()), 256, 0, s>>>(p.dsw, p.sds, qk.kt, qk.sk, p.dQ, d.N, d.BH(),
                                                                    d.scale);
     return hipGetLastError();
 }
 
 template <bool BF16, int D>
-hipError_t bwd_dispatch_bq(const Dims& d, const BwdArgs& a, const int8_t* kt, float* dQ, hipStream_t s) {
+hipError_t bwd_dispatch_bq(const Dims& d, const BwdPtrs& p, hipStream_t s) {
     if (d.bq == 128)
-        return d.causal ? bwd_dispatch<BF16, D, 128, true>(d, a, kt, dQ, s)
-                        : bwd_dispatch<BF16, D, 128, false>(d, a, kt, dQ, s);
-    return d.causal ? bwd_dispatch<BF16, D, 64, true>(d, a, kt, dQ, s)
-                    : bwd_dispatch<BF16, D, 64, false>(d, a, kt, dQ, s);
+        return d.causal ? bwd_dispatch<BF16, D, 128, true>(d, p, s) : bwd_dispatch<BF16, D, 128, false>(d, p, s);
+    return d.causal ? bwd_dispatch<BF16, D, 64, true>(d, p, s) : bwd_dispatch<BF16, D, 64, false>(d, p, s);
 }
 
 size_t total_tiles(const Dims& d) {
@@ -505,11 +533,9 @@ hipError_t launch_bwd(const Dims& d, const sage_qtensors& qk, const sage_dotenso
                       void* workspace, float* dQ, float* dK, float* dV, hipStream_t s) {
     int8_t* dsw = static_cast<int8_t*>(workspace);
     float* sds = reinterpret_cast<float*>(dsw + codes_bytes(d));
-    const BwdArgs a{qk.q,  qk.sq,    qk.k,    qk.sk,   qk.vr, qk.mu_q, qk.qk_bias, dos.delta, dos.dot,
-                    dos.sdo, dos.dor, L, dsw, sds, dK, dV, d.N, d.BH(), d.scale};
-    if (d.bf16)
-        return d.D == 128 ? bwd_dispatch_bq<true, 128>(d, a, qk.kt, dQ, s) : bwd_dispatch_bq<true, 64>(d, a, qk.kt, dQ, s);
-    return d.D == 128 ? bwd_dispatch_bq<false, 128>(d, a, qk.kt, dQ, s) : bwd_dispatch_bq<false, 64>(d, a, qk.kt, dQ, s);
+    const BwdPtrs p{&qk, &dos, L, dsw, sds, dQ, dK, dV};
+    if (d.bf16) return d.D == 128 ? bwd_dispatch_bq<true, 128>(d, p, s) : bwd_dispatch_bq<true, 64>(d, p, s);
+    return d.D == 128 ? bwd_dispatch_bq<false, 128>(d, p, s) : bwd_dispatch_bq<false, 64>(d, p, s);
 }
 
 }  // namespace sage
