@@ -118,9 +118,8 @@ __device__ __forceinline__ void stage_query_tile(BwdStage<BQ, D>& st, const int8
     }
 }
 
-// The two stages are separate LDS objects and the tile loop is unrolled by
-// two, so the compiler sees that the asynchronous copy into one stage never
-// aliases the reads of the other and does not wait for it.
+// Two LDS stages alternate: tile i is read from stage (i - istart) & 1 while
+// the next tile is copied into the other one.
 template <bool BF16, int D, int BQ, bool CAUSAL, bool QSMOOTH>
 __global__ __launch_bounds__(512, 1) void bwd_kernel(
     const int8_t* __restrict__ q, const float* __restrict__ sq, const int8_t* __restrict__ k,
@@ -135,8 +134,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
     constexpr int KSH = D / 32;   // 16-bit contraction steps over d
     constexpr int DB = D / 16;    // 16-wide blocks of d
     constexpr int CH = BQ / 16;   // 16-byte chunks per dS key row
-    __shared__ __align__(16) BwdStage<BQ, D> st0;
-    __shared__ __align__(16) BwdStage<BQ, D> st1;
+    __shared__ __align__(16) BwdStage<BQ, D> st[2];
     __shared__ float red[2][2][4];   // [key block][P | dS][key group]
 
     const int Tn = N / 64, Tm = N / BQ;
@@ -152,7 +150,14 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
     const int kr = 16 * kg + n16;     // key row inside the block
     const int key = j * 64 + kr;
 
+    // A key block past a ragged end computes on zero operands and stores
+    // nothing; keeping it in the same straight-line code as the others
+    // avoids merging two paths over the accumulators on every tile.
     v4i kop[KS8], vop[KSH];
+#pragma unroll
+    for (int ks = 0; ks < KS8; ++ks) kop[ks] = v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int ks = 0; ks < KSH; ++ks) vop[ks] = v4i{0, 0, 0, 0};
     float skj = 0.f;
     if (kv_on) {
 #pragma unroll
@@ -195,12 +200,30 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
             stage_query_tile<BQ, D>(nxt, qh + (size_t)(qbase + BQ) * D, doth + (size_t)(qbase + BQ) * D,
                                     dorh + (size_t)(qbase + BQ) * D, w, lane);
 
+        // the tile exists and has a visible key (it is stored for the dQ pass)
         const bool tile_on = kv_on && (!CAUSAL || j * 64 <= qbase + BQ - 1);
         const float sqi = sq[(size_t)bh * Tm + i];
         const float sdoi = sdo[(size_t)bh * Tm + i];
-        float p[MB][4], ds[MB][4];
-        float pmax = 0.f, dsmax = 0.f;
-        if (tile_on) {
+        // Tile maxima over the key block's four waves, then the scales.  Raw
+        // barrier: the copy of the next tile stays in flight.
+        auto tile_scales = [&](float pmax, float dsmax, float& sP, float& sS) __attribute__((always_inline)) {
+            pmax = wave_max_nonneg(pmax);
+            dsmax = wave_max_nonneg(dsmax);
+            if (lane == 0) {
+                red[kb][0][kg] = pmax;
+                red[kb][1][kg] = dsmax;
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            pmax = fmaxf(fmaxf(red[kb][0][0], red[kb][0][1]), fmaxf(red[kb][0][2], red[kb][0][3]));
+            dsmax = fmaxf(fmaxf(red[kb][1][0], red[kb][1][1]), fmaxf(red[kb][1][2], red[kb][1][3]));
+            sP = __fdiv_rn(pmax, 127.f);
+            sS = __fdiv_rn(dsmax, 127.f);
+        };
+        {
+            float p[MB][4], ds[MB][4];
+            float pmax = 0.f, dsmax = 0.f;
             const float c2 = (float)((double)sqi * (double)skj * scale * kLog2e_d);  // one rounding
             float bias2 = 0.f;
             if (QSMOOTH) bias2 = (float)((double)qk_bias[((size_t)bh * Tm + i) * N + key] * kLog2e_d);
@@ -210,21 +233,19 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
                 const int row = 16 * mb + n16;  // query row (in tile) this lane supplies
-                s[mb] = magic4;
 #pragma unroll
                 for (int ks = 0; ks < KS8; ++ks) {
                     const v4i av = *reinterpret_cast<const v4i*>(cur.q + off_r32(row, 64 * ks + 16 * g, D));
-                    s[mb] = mfma16_i8(av, kop[ks], s[mb]);
+                    s[mb] = mfma16_i8(av, kop[ks], ks == 0 ? magic4 : s[mb]);
                 }
             }
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
                 const int row = 16 * mb + n16;
-                dp[mb] = v4f{0, 0, 0, 0};
 #pragma unroll
                 for (int ks = 0; ks < KSH; ++ks) {
                     const v4i av = *reinterpret_cast<const v4i*>(cur.dor + off_r16h(row, 32 * ks + 8 * g, D));
-                    dp[mb] = mfma16_h<BF16>(av, vop[ks], dp[mb]);
+                    dp[mb] = mfma16_h<BF16>(av, vop[ks], ks == 0 ? v4f{0, 0, 0, 0} : dp[mb]);
                 }
             }
 #pragma unroll
@@ -244,9 +265,9 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
                 }
             }
             if (CAUSAL && (j * 64 + 63 > qbase)) {
-                // diagonal tile: zero the keys after each query (by selection,
-                // so an overflowed exp there never reaches a product) and take
-                // the maxima again
+                // diagonal (or invisible) tile: zero the keys after each query
+                // (by selection, so an overflowed exp there never reaches a
+                // product) and take the maxima again
                 pmax = 0.f;
                 dsmax = 0.f;
 #pragma unroll
@@ -260,24 +281,8 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
                         dsmax = fmaxf(dsmax, fabsf(ds[mb][r]));
                     }
             }
-        }
-        // ---- tile maxima over the key block's four waves (raw barrier: the
-        // copy of the next tile stays in flight)
-        pmax = wave_max_nonneg(pmax);
-        dsmax = wave_max_nonneg(dsmax);
-        if (lane == 0) {
-            red[kb][0][kg] = pmax;
-            red[kb][1][kg] = dsmax;
-        }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        pmax = fmaxf(fmaxf(red[kb][0][0], red[kb][0][1]), fmaxf(red[kb][0][2], red[kb][0][3]));
-        dsmax = fmaxf(fmaxf(red[kb][1][0], red[kb][1][1]), fmaxf(red[kb][1][2], red[kb][1][3]));
-        const float sP = __fdiv_rn(pmax, 127.f);
-        const float sS = __fdiv_rn(dsmax, 127.f);
-
-        if (tile_on) {
+            float sP, sS;
+            tile_scales(pmax, dsmax, sP, sS);
             const float invP = sP > 0.f ? 1.f / sP : 0.f;
             const float invS = sS > 0.f ? 1.f / sS : 0.f;
             // ---- codes, query-contiguous per lane (4 queries per dword)
@@ -295,13 +300,15 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
             }
             // ---- dS codes and scale to the workspace (key-major, swizzled)
             const size_t t = (size_t)bh * tph + tile_index<BQ, CAUSAL>(i, j, Tn);
-            int8_t* drow = dsw + t * (BQ * 64) + kr * BQ;
+            if (tile_on) {
+                int8_t* drow = dsw + t * (BQ * 64) + kr * BQ;
 #pragma unroll
-            for (int kq = 0; kq < KQ; ++kq) {
-                const int slot = (KQ * g + kq) ^ (kr & (CH - 1));
-                *reinterpret_cast<v4i*>(drow + slot * 16) = dsop[kq];
+                for (int kq = 0; kq < KQ; ++kq) {
+                    const int slot = (KQ * g + kq) ^ (kr & (CH - 1));
+                    *reinterpret_cast<v4i*>(drow + slot * 16) = dsop[kq];
+                }
+                if (kg == 0 && lane == 0) sds[t] = sS;
             }
-            if (kg == 0 && lane == 0) sds[t] = sS;
             if (QSMOOTH) {
                 // dK bias (dS^T 1) mu_Q^T from the unquantised dS
                 float cs = 0.f;
@@ -325,7 +332,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
             const int kk = n16 >> 1, hf = n16 & 1;
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                v4i accv = magic4, acck = magic4;
+                v4i accv, acck;
 #pragma unroll
                 for (int kq = 0; kq < KQ; ++kq) {
                     const v4i av = reinterpret_cast<const v4i*>(cur.dot)[kq * 4 * D + g * D + 16 * db + n16];
@@ -334,8 +341,8 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
                     const v2i r1 = lds_read_tr8(cur.q + off_r32(qa, 16 * db, D) + 8 * hf);
                     const v2i r2 = lds_read_tr8(cur.q + off_r32(qa + 32, 16 * db, D) + 8 * hf);
                     const v4i ak = v4i{r1[0], r1[1], r2[0], r2[1]};
-                    accv = mfma16_i8(av, pop[kq], accv);
-                    acck = mfma16_i8(ak, dsop[kq], acck);
+                    accv = mfma16_i8(av, pop[kq], kq == 0 ? magic4 : accv);
+                    acck = mfma16_i8(ak, dsop[kq], kq == 0 ? magic4 : acck);
                 }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -349,20 +356,24 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
             nxt.l2[tid] = (float)((double)nL * kLog2e_d);
             nxt.delta[tid] = nd;
         }
+        wait_vmem();       // the asynchronous copies are not seen by the compiler's waits
         __syncthreads();   // the next tile has landed in LDS for every wave; `cur` may be overwritten
     };
 
     // ---- prologue: first query tile into st0
-    stage_query_tile<BQ, D>(st0, qh + (size_t)istart * BQ * D, doth + (size_t)istart * BQ * D,
+    stage_query_tile<BQ, D>(st[0], qh + (size_t)istart * BQ * D, doth + (size_t)istart * BQ * D,
                             dorh + (size_t)istart * BQ * D, w, lane);
     if (tid < BQ) {
-        st0.l2[tid] = (float)((double)Lh[istart * BQ + tid] * kLog2e_d);
-        st0.delta[tid] = dlh[istart * BQ + tid];
+        st[0].l2[tid] = (float)((double)Lh[istart * BQ + tid] * kLog2e_d);
+        st[0].delta[tid] = dlh[istart * BQ + tid];
     }
+    wait_vmem();       // the asynchronous copies are not seen by the compiler's waits
     __syncthreads();
-    for (int i = istart; i < Tm; i += 2) {
-        step(i, st0, st1);
-        if (i + 1 < Tm) step(i + 1, st1, st0);
+    // pairs of tiles in straight-line code (no merge over the accumulators
+    // inside the loop), then an odd last tile
+    for (int i = istart; i < Tm; ++i) {
+        const int b = (i - istart) & 1;
+        step(i, st[b], st[b ^ 1]);
     }
 
     // ---- write dV and dK (lane = key, 4 consecutive d per block)
@@ -383,8 +394,8 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
 // dQ_i = scale * sum_j s_dS,ij s_K,j M(dS^_ij, K^_j), one workgroup per query
 // tile; wave w owns the BQ/4 dS positions [w BQ/4, (w+1) BQ/4) (queries
 // 16 mb + 4 w + r) and all D columns.  Each key tile (its dS codes and the
-// K codes, column tiles) streams through two LDS stages (separate objects,
-// loop unrolled by two) filled one tile ahead by asynchronous copies.
+// K codes, column tiles) streams through two alternating LDS stages filled
+// one tile ahead by asynchronous copies.
 template <int BQ, int D>
 struct DqStage {
     int8_t ds[BQ * 64];   // dS codes of one tile, key-major (workspace layout)
@@ -403,8 +414,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const int8_t* __restrict__ d
     constexpr int K_BYTES = 64 * D;
     constexpr int ROUNDS = (DS_BYTES + K_BYTES) / 4096;
     static_assert((DS_BYTES + K_BYTES) % 4096 == 0 && DS_BYTES % 1024 == 0, "stage shape");
-    __shared__ __align__(16) DqStage<BQ, D> st0;
-    __shared__ __align__(16) DqStage<BQ, D> st1;
+    __shared__ __align__(16) DqStage<BQ, D> st[2];
 
     const int Tn = N / 64, Tm = N / BQ;
     int unit, bh;
@@ -466,15 +476,14 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const int8_t* __restrict__ d
                 for (int r = 0; r < 4; ++r) acc[mb][nb][r] = fmaf(unmagic(x[r]), cj, acc[mb][nb][r]);
             }
         }
+        wait_vmem();       // the asynchronous copies are not seen by the compiler's waits
         __syncthreads();   // next tile landed for every wave; `cur` may be overwritten
     };
 
-    load(0, st0);
+    load(0, st[0]);
+    wait_vmem();       // the asynchronous copies are not seen by the compiler's waits
     __syncthreads();
-    for (int j = 0; j < jend; j += 2) {
-        step(j, st0, st1);
-        if (j + 1 < jend) step(j + 1, st1, st0);
-    }
+    for (int j = 0; j < jend; ++j) step(j, st[j & 1], st[(j & 1) ^ 1]);
     // position p = QPW w + 16 mb + 4 g + r  ->  query 64 mb + 16 g + 4 w + r
     float* out = dQ + head + (size_t)(i * BQ) * D;
 #pragma unroll

@@ -132,10 +132,23 @@ __device__ __forceinline__ v2i lds_read_tr8(const int8_t* p) {
 }
 
 // Asynchronous 16-byte copy global -> LDS: lane l's 16 bytes from src land at
-// dst_wave + 16 * l (dst_wave must be the same for the whole wave).  Tracked
-// by vmcnt; wait with wait_vmem() before a barrier that publishes the data.
-__device__ __forceinline__ void copy16_to_lds(const void* src, void* dst_wave) {
-    __builtin_amdgcn_global_load_lds(src, SAGE_LDS(dst_wave), 16, 0, 0);
+// lds_wave + 16 * l (lds_wave must be the same for the whole wave).  Tracked
+// by vmcnt only; wait with wait_vmem() before the barrier that publishes the
+// data.  Issued from inline assembly on purpose: the compiler would otherwise
+// wait for the copy before every later LDS read it cannot prove disjoint from
+// the destination, which serialises the copy of the next tile with the work
+// on the current one.  M0 (the LDS base of the copy) is saved and restored
+// around it, so the compiler's view of M0 is unchanged.
+__device__ __forceinline__ void copy16_to_lds(const void* src, void* lds_wave) {
+    const unsigned off =
+        (unsigned)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(lds_wave));
+    unsigned saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, off\n\ts_nop 0\n\ts_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(__builtin_amdgcn_readfirstlane(off)), "v"(src)
+        : "memory");
 }
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
