@@ -65,16 +65,19 @@ __device__ __forceinline__ int pack_magic(float a, float b, float c, float d) {
     return (int)(lo | hi);
 }
 
-// Workgroup -> (unit, head).  Blocks are dealt to the eight XCDs round-robin;
-// when the heads divide evenly, each XCD takes whole heads one after another
-// (so a head's streamed tiles stay in that XCD's L2), units in order within
-// a head; `units` is the number of units per head.
+// Workgroup -> (unit, head); `units` is the number of units per head.
+// Blocks are dealt to the eight XCDs round-robin; when the heads divide
+// evenly each XCD owns whole heads.  UNITS_OUTER = false: the XCD works
+// through its heads one after another, units in order (a head's streamed
+// tiles stay in that XCD's L2).  UNITS_OUTER = true: unit-major across the
+// XCD's heads (the first units, the heaviest, start first).
+template <bool UNITS_OUTER>
 __device__ __forceinline__ void xcd_coords(int units, int BH, int& unit, int& bh) {
     const int id = blockIdx.x;
     if ((BH & 7) == 0) {
-        const int xcd = id & 7, k = id >> 3;
-        bh = xcd + 8 * (k / units);
-        unit = k % units;
+        const int xcd = id & 7, k = id >> 3, hpx = BH >> 3;
+        if (UNITS_OUTER) { unit = k / hpx; bh = xcd + 8 * (k % hpx); }
+        else { bh = xcd + 8 * (k / units); unit = k % units; }
     } else {
         bh = id / units;
         unit = id % units;
@@ -139,7 +142,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
 
     const int Tn = N / 64, Tm = N / BQ;
     int jj, bh;
-    xcd_coords((Tn + 1) / 2, BH, jj, bh);
+    xcd_coords<false>((Tn + 1) / 2, BH, jj, bh);
     const size_t head = (size_t)bh * N * D;
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -418,7 +421,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const int8_t* __restrict__ d
 
     const int Tn = N / 64, Tm = N / BQ;
     int unit, bh;
-    xcd_coords(Tm, BH, unit, bh);
+    xcd_coords<true>(Tm, BH, unit, bh);
     const int i = CAUSAL ? (Tm - 1 - unit) : unit;  // heavy tiles first
     const size_t head = (size_t)bh * N * D;
     const size_t tph = tiles_per_head<BQ, CAUSAL>(Tm, Tn);

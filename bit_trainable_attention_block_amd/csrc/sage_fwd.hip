@@ -54,25 +54,53 @@ __device__ __forceinline__ int pack_magic(float a, float b, float c, float d) {
     return (int)(lo | hi);
 }
 
+template <int D>
+struct FwdStage {
+    int8_t k[kKTile * D];   // K codes of the key tile, R32
+    int8_t v[kKTile * D];   // V codes of the key tile, C32P
+};
+
+// Lowest integer sum a product can hold (|sum| <= 127^2 D < 2^21), as the
+// magic-started accumulator sees it: a masked key never wins a row maximum,
+// and a row with no visible key in the tile keeps a finite maximum.
+constexpr int kMaskedSum = kMagicBits - (1 << 22) + 1;
+
 template <bool BF16, int D, bool CAUSAL, bool QSMOOTH>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     constexpr int TILE_BYTES = kKTile * D;           // K or V codes of one tile
-    constexpr int CHUNKS = 2 * TILE_BYTES / 16;      // 16-byte chunks per stage (K + V)
-    constexpr int CPT = CHUNKS / 256;                // chunks per thread
     constexpr int KS = D / 32;                       // contraction steps over d
     constexpr int DB = D / 32;                       // 32-wide blocks of d
-    __shared__ __align__(16) int8_t stage[2][2 * TILE_BYTES];
+    static_assert(TILE_BYTES % 4096 == 0, "stage shape");
+    __shared__ __align__(16) FwdStage<D> st[2];
 
     const int N = a.N;
     const int Tn = N / kKTile;
     const int Tm = N / a.bq;
     const int ntiles = (N + kQTile - 1) / kQTile;
-    const int qt = CAUSAL ? (ntiles - 1 - (int)blockIdx.x) : (int)blockIdx.x;  // heavy tiles first
-    const int bh = blockIdx.y;
+    // Workgroup -> (query tile, head).  Blocks are dealt to the eight XCDs
+    // round-robin; when the heads divide evenly each XCD owns whole heads
+    // (their K/V stay in its L2), and across an XCD's heads the query tiles
+    // go heavy first (causal: the last tiles see the most keys).
+    int qt, bh;
+    {
+        const int id = blockIdx.x;
+        const int BH = (int)gridDim.x / ntiles;
+        int unit;
+        if ((BH & 7) == 0) {
+            const int xcd = id & 7, k = id >> 3, hpx = BH >> 3;
+            bh = xcd + 8 * (k % hpx);
+            unit = k / hpx;
+        } else {
+            bh = id % BH;
+            unit = id / BH;
+        }
+        qt = CAUSAL ? (ntiles - 1 - unit) : unit;
+    }
     const size_t head = (size_t)bh * N * D;
 
     const int tid = threadIdx.x;
-    const int w = tid >> 6, lane = tid & 63, n = lane & 31, hh = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, n = lane & 31, hh = lane >> 5;
     const int q0 = qt * kQTile + w * 32;
     const bool active = q0 < N;
     const int query = q0 + n;
@@ -98,109 +126,94 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+    v16i magic16;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) magic16[r] = kMagicBits;
 
-    // stage loader: chunk c < CHUNKS/2 from K, the rest from V
-    auto load_chunks = [&](int j, v4i (&buf)[CPT]) {
+    // asynchronous copy of key tile j (K and V codes: two contiguous runs)
+    auto load = [&](int j, FwdStage<D>& dst) __attribute__((always_inline)) {
+        const int8_t* ks_ = a.k + head + (size_t)j * TILE_BYTES;
+        const int8_t* vs_ = a.vt + head + (size_t)j * TILE_BYTES;
 #pragma unroll
-        for (int u = 0; u < CPT; ++u) {
-            const int c = tid + u * 256;
-            const int half = c / (CHUNKS / 2), cc = c % (CHUNKS / 2);
-            const int8_t* src = (half == 0 ? a.k : a.vt) + head + (size_t)j * TILE_BYTES + cc * 16;
-            buf[u] = *reinterpret_cast<const v4i*>(src);
-        }
-    };
-    auto store_chunks = [&](int sidx, const v4i (&buf)[CPT]) {
-#pragma unroll
-        for (int u = 0; u < CPT; ++u) {
-            const int c = tid + u * 256;
-            *reinterpret_cast<v4i*>(&stage[sidx][c * 16]) = buf[u];
+        for (int c0 = 0; c0 < TILE_BYTES; c0 += 4096) {
+            copy16_to_lds(ks_ + c0 + w * 1024 + lane * 16, dst.k + c0 + w * 1024);
+            copy16_to_lds(vs_ + c0 + w * 1024 + lane * 16, dst.v + c0 + w * 1024);
         }
     };
 
-    v4i pre[CPT];
-    if (jend > 0) {
-        load_chunks(0, pre);
-        store_chunks(0, pre);
-    }
+    if (jend > 0) load(0, st[0]);
+    wait_vmem();   // the asynchronous copies are not seen by the compiler's waits
     __syncthreads();
 
     for (int j = 0; j < jend; ++j) {
-        const int sidx = j & 1;
-        const bool more = j + 1 < jend;
-        if (more) load_chunks(j + 1, pre);
+        const FwdStage<D>& cur = st[j & 1];
+        if (j + 1 < jend) load(j + 1, st[(j + 1) & 1]);
 
         const int k0 = j * kKTile;
         const bool wave_on = active && (!CAUSAL || k0 <= q0 + 31);
         if (wave_on) {
-            const v4i* lk = reinterpret_cast<const v4i*>(&stage[sidx][0]);
-            const v4i* lv = reinterpret_cast<const v4i*>(&stage[sidx][TILE_BYTES]);
+            const v4i* lk = reinterpret_cast<const v4i*>(cur.k);
+            const v4i* lv = reinterpret_cast<const v4i*>(cur.v);
             v16i s[2];
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb) {
-                s[mb] = v16i{0};
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     v4i av = lk[mb * 2 * D + (2 * ks + hh) * 32 + n];
-                    s[mb] = mfma32_i8(av, qop[ks], s[mb]);
+                    s[mb] = mfma32_i8(av, qop[ks], ks == 0 ? magic16 : s[mb]);
                 }
             }
             // one rounding from the exact product of the scales (keeps the
             // logits within an ulp of the definition)
             const float c2 = (float)((double)sqv * (double)a.sk[(size_t)bh * Tn + j] * a.scale2);
-            // Diagonal tiles (some key after some query) take the masked
-            // instantiation; every other tile runs without a compare.
-            auto tile = [&](auto mask_tag) {
+            float rm, sum;
+            v4i pc[2];
+            auto codes = [&](auto mask_tag) __attribute__((always_inline)) {
                 constexpr bool MASK = decltype(mask_tag)::value;
                 // Row maximum of this tile (log2 units).  Without Q-smoothing the
-                // logits are one positive scale times the int32 sums, so the max
-                // is taken on the integers; masked keys never win it.
-                float rm;
+                // logits are one positive scale times the integer sums, so the
+                // maximum is taken on the accumulator bits (which order like the
+                // sums); masked keys never win it.
                 float bias2[2][16];
                 if (QSMOOTH) {
                     rm = -INFINITY;
-    #pragma unroll
+#pragma unroll
                     for (int mb = 0; mb < 2; ++mb)
-    #pragma unroll
+#pragma unroll
                         for (int r = 0; r < 16; ++r) {
                             const int key = k0 + 32 * mb + 8 * (r >> 2) + 4 * hh + (r & 3);
                             bias2[mb][r] = (float)((double)bias_row[key] * kLog2e_d);
-                            const float v = fmaf((float)s[mb][r], c2, bias2[mb][r]);
+                            const float v = fmaf(unmagic(s[mb][r]), c2, bias2[mb][r]);
                             if (!(MASK && key > query)) rm = fmaxf(rm, v);
                         }
                 } else {
-                    int im = INT_MIN;
+                    int im = kMaskedSum;
                     if (MASK) {
-    #pragma unroll
+#pragma unroll
                         for (int mb = 0; mb < 2; ++mb)
-    #pragma unroll
+#pragma unroll
                             for (int r = 0; r < 16; ++r) {
                                 const int key = k0 + 32 * mb + 8 * (r >> 2) + 4 * hh + (r & 3);
-                                im = max(im, key > query ? INT_MIN : s[mb][r]);
+                                im = max(im, key > query ? kMaskedSum : s[mb][r]);
                             }
                     } else {
-    #pragma unroll
+#pragma unroll
                         for (int mb = 0; mb < 2; ++mb)
-    #pragma unroll
+#pragma unroll
                             for (int r = 0; r < 16; r += 2) im = max(im, max(s[mb][r], s[mb][r + 1]));
                     }
-                    rm = (float)im * c2;
+                    rm = unmagic(im) * c2;
                 }
                 rm = fmaxf(rm, __shfl_xor(rm, 32));
-                // Reference maximum: moves only when the row max exceeds it by
-                // more than 2^8, so the rescale below is rare.  The codes
-                // 127 * 2^(x - rm) do not depend on it, only l and O's common
-                // factor do, and those use it consistently.
-                const float m_new = (rm > m + kLazy) ? rm : m;
                 const float shift = rm - kLog2_127;
-                float sum = 0.f;
-                v4i pc[2];
-    #pragma unroll
+                sum = 0.f;
+#pragma unroll
                 for (int mb = 0; mb < 2; ++mb) {
                     float c[16];
-    #pragma unroll
+#pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        float x = QSMOOTH ? fmaf((float)s[mb][r], c2, bias2[mb][r] - shift)
-                                          : fmaf((float)s[mb][r], c2, -shift);
+                        float x = QSMOOTH ? fmaf(unmagic(s[mb][r]), c2, bias2[mb][r] - shift)
+                                          : fmaf(unmagic(s[mb][r]), c2, -shift);
                         if (MASK) {
                             const int key = k0 + 32 * mb + 8 * (r >> 2) + 4 * hh + (r & 3);
                             if (key > query) x = -INFINITY;
@@ -209,44 +222,48 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
                         sum += e;
                         c[r] = e + kMagic;                           // rint(e) in the low byte
                     }
-    #pragma unroll
+#pragma unroll
                     for (int qd = 0; qd < 4; ++qd)
                         pc[mb][qd] = pack_magic(c[4 * qd], c[4 * qd + 1], c[4 * qd + 2], c[4 * qd + 3]);
                 }
                 sum += __shfl_xor(sum, 32);
-                const float sP = __fdiv_rn(__builtin_amdgcn_exp2f(rm - m_new), 127.f);
-                if (__builtin_expect(__any(m_new != m), 0)) {
-                    // rare: a row's reference maximum moved; rescale l and O
-                    const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 0 on the first tile
-                    l *= alpha;
-    #pragma unroll
-                    for (int db = 0; db < DB; ++db)
-    #pragma unroll
-                        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-                }
-                l = fmaf(sum, sP, l);
-                m = m_new;
-                const float beta = sP * a.sv[(size_t)bh * Tn + j];
-    #pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    v16i acc = v16i{0};
-    #pragma unroll
-                    for (int mb = 0; mb < 2; ++mb) {
-                        v4i av = lv[(mb * 2 + hh) * D + 32 * db + n];
-                        acc = mfma32_i8(av, pc[mb], acc);
-                    }
-    #pragma unroll
-                    for (int r = 0; r < 16; ++r) o[db][r] = fmaf((float)acc[r], beta, o[db][r]);
-                }
             };
-            if (CAUSAL && (k0 + kKTile - 1 > q0)) tile(std::true_type{});
-            else tile(std::false_type{});
+            // Diagonal tiles (some key after some query) take the masked
+            // instantiation; every other tile runs without a compare.
+            if (CAUSAL && (k0 + kKTile - 1 > q0)) codes(std::true_type{});
+            else codes(std::false_type{});
+            // Reference maximum: moves only when the row max exceeds it by
+            // more than 2^8, so the rescale below is rare.  The codes
+            // 127 * 2^(x - rm) do not depend on it, only l and O's common
+            // factor do, and those use it consistently.
+            const float m_new = (rm > m + kLazy) ? rm : m;
+            const float sP = __fdiv_rn(__builtin_amdgcn_exp2f(rm - m_new), 127.f);
+            if (__builtin_expect(__any(m_new != m), 0)) {
+                // rare: a row's reference maximum moved; rescale l and O
+                const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 0 on the first tile
+                l *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+            }
+            l = fmaf(sum, sP, l);
+            m = m_new;
+            const float beta = sP * a.sv[(size_t)bh * Tn + j];
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                v16i acc;
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb) {
+                    v4i av = lv[(mb * 2 + hh) * D + 32 * db + n];
+                    acc = mfma32_i8(av, pc[mb], mb == 0 ? magic16 : acc);
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[db][r] = fmaf(unmagic(acc[r]), beta, o[db][r]);
+            }
         }
-        if (more) {
-            __syncthreads();  // everyone is done reading the other stage
-            store_chunks(sidx ^ 1, pre);
-            __syncthreads();
-        }
+        wait_vmem();       // the next tile has landed
+        __syncthreads();   // ... for every wave; this stage may be overwritten
     }
 
     if (active) {
@@ -269,7 +286,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 
 template <bool BF16, int D>
 hipError_t fwd_dispatch(const Dims& d, const FwdArgs& a, hipStream_t s) {
-    dim3 grid((d.N + kQTile - 1) / kQTile, d.BH());
+    const dim3 grid(((d.N + kQTile - 1) / kQTile) * d.BH());
     if (d.causal) {
         if (d.q_smooth) fwd_kernel<BF16, D, true, true><<<grid, 256, 0, s>>>(a);
         else fwd_kernel<BF16, D, true, false><<<grid, 256, 0, s>>>(a);
