@@ -44,17 +44,77 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from the committed counter summary, or
-    None when absent or taken on different kernel sources."""
+def measured_traffic(call: str):
+    """HBM bytes per launch of C-ABI call `call` from the committed counter
+    summary (profiles/traffic.json), or None when absent or taken on
+    different kernel sources."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
         if t.get("source_hash") != kernel_source_hash():
             return None
-        return t["kernels"][kernel]["bytes_per_launch"]
+        return t["calls"][call]["bytes_per_launch"]
     except (OSError, KeyError, ValueError):
         return None
+
+
+# kernels of each C-ABI call (by name prefix in the counter output)
+CALL_KERNELS = {
+    "sage_quantize": ("zero_f64_kernel", "quant_v_ksum_kernel", "quant_q_kernel", "quant_k_kernel"),
+    "sage_fwd": ("fwd_kernel",),
+    "sage_bwd_pre": ("bwd_pre_kernel",),
+    "sage_bwd": ("bwd_kernel", "dq_kernel"),
+}
+
+
+def _counter_means(directory):
+    """{short kernel name: {counter: mean value per dispatch}} from the
+    rocprofv3 counter_collection.csv files under `directory`."""
+    import csv
+    import glob
+    sums, counts = {}, {}
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(path)):
+            name = r["Kernel_Name"].replace("sage::(anonymous namespace)::", "").replace("void ", "")
+            name = name.split("(")[0].split("<")[0].strip()
+            key = (name, r["Counter_Name"])
+            sums[key] = sums.get(key, 0.0) + float(r["Counter_Value"])
+            counts.setdefault(key, set()).add(r["Dispatch_Id"])
+    out = {}
+    for (name, ctr), v in sums.items():
+        out.setdefault(name, {})[ctr] = v / len(counts[(name, ctr)])
+    return out
+
+
+def traffic_from(directory, copy_bytes):
+    """Write profiles/traffic.json (and print it) from four rocprofv3 --pmc
+    runs under `directory`: fetch/ and write/ (FETCH_SIZE, WRITE_SIZE over one
+    bench step) and copy_fetch/, copy_write/ (the same counters over a plain
+    device copy of `copy_bytes` bytes, which calibrates both counters)."""
+    fetch = _counter_means(os.path.join(directory, "fetch"))
+    write = _counter_means(os.path.join(directory, "write"))
+    cf = _counter_means(os.path.join(directory, "copy_fetch"))
+    cw = _counter_means(os.path.join(directory, "copy_write"))
+    copy_kernel = max(cf, key=lambda k: cf[k].get("FETCH_SIZE", 0.0))
+    k_fetch = copy_bytes / (cf[copy_kernel]["FETCH_SIZE"] * 1024.0)
+    k_write = copy_bytes / (cw[copy_kernel]["WRITE_SIZE"] * 1024.0)
+    kernels, calls = {}, {}
+    for name in sorted(set(fetch) | set(write)):
+        fb = fetch.get(name, {}).get("FETCH_SIZE", 0.0) * 1024.0 * k_fetch
+        wb = write.get(name, {}).get("WRITE_SIZE", 0.0) * 1024.0 * k_write
+        kernels[name] = {"fetch_bytes": fb, "write_bytes": wb, "bytes_per_launch": fb + wb}
+    for call, names in CALL_KERNELS.items():
+        fb = sum(kernels[n]["fetch_bytes"] for n in names if n in kernels)
+        wb = sum(kernels[n]["write_bytes"] for n in names if n in kernels)
+        calls[call] = {"fetch_bytes": fb, "write_bytes": wb, "bytes_per_launch": fb + wb}
+    out = {"source_hash": kernel_source_hash(), "workload": "d128_n8k_causal_qknorm",
+           "copy_probe": {"kernel": copy_kernel, "bytes": copy_bytes, "fetch_factor": k_fetch,
+                          "write_factor": k_write},
+           "calls": calls, "kernels": kernels}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
 
 
 # whole heads timed for the CPU baseline: about 10-15 s of single-core work
@@ -90,10 +150,16 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-from", default="",
+                    help="summarise rocprofv3 FETCH_SIZE/WRITE_SIZE runs in this directory into "
+                         "profiles/traffic.json (no GPU needed) and exit")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run one plain device-to-device copy of this many MiB (the known-size "
                          "reference that scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
+    if args.traffic_from:
+        traffic_from(args.traffic_from, 1024 << 20)
+        return
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
               "(heads shard across GPUs with no exchange; see the design notes)", file=sys.stderr)
