@@ -230,29 +230,27 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
             const float c2 = (float)((double)sqi * (double)skj * scale * kLog2e_d);  // one rounding
             float bias2 = 0.f;
             if (QSMOOTH) bias2 = (float)((double)qk_bias[((size_t)bh * Tm + i) * N + key] * kLog2e_d);
-            // ---- S and dP for this wave's 16 keys and all BQ queries
+            // ---- S and dP for this wave's 16 keys and all BQ queries, one
+            // 16-query block ahead of the vector work on the previous block
             v4i s[MB];
             v4f dp[MB];
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
+            auto mfma_block = [&](int mb) __attribute__((always_inline)) {
                 const int row = 16 * mb + n16;  // query row (in tile) this lane supplies
 #pragma unroll
                 for (int ks = 0; ks < KS8; ++ks) {
                     const v4i av = *reinterpret_cast<const v4i*>(cur.q + off_r32(row, 64 * ks + 16 * g, D));
                     s[mb] = mfma16_i8(av, kop[ks], ks == 0 ? magic4 : s[mb]);
                 }
-            }
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-                const int row = 16 * mb + n16;
 #pragma unroll
                 for (int ks = 0; ks < KSH; ++ks) {
                     const v4i av = *reinterpret_cast<const v4i*>(cur.dor + off_r16h(row, 32 * ks + 8 * g, D));
                     dp[mb] = mfma16_h<BF16>(av, vop[ks], ks == 0 ? v4f{0, 0, 0, 0} : dp[mb]);
                 }
-            }
+            };
+            mfma_block(0);
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
+                if (mb + 1 < MB) mfma_block(mb + 1);
                 const v4f l2 = *reinterpret_cast<const v4f*>(&cur.l2[16 * mb + 4 * g]);
                 const v4f dl = *reinterpret_cast<const v4f*>(&cur.delta[16 * mb + 4 * g]);
 #pragma unroll
@@ -266,6 +264,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
                     pmax = fmaxf(pmax, pv);
                     dsmax = fmaxf(dsmax, fabsf(dsv));
                 }
+                __builtin_amdgcn_sched_barrier(0);
             }
             if (CAUSAL && (j * 64 + 63 > qbase)) {
                 // diagonal (or invisible) tile: zero the keys after each query
@@ -333,9 +332,8 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
             const float fv = sP * sdoi;
             const float fk = sS * sqi;
             const int kk = n16 >> 1, hf = n16 & 1;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                v4i accv, acck;
+            v4i accv[DB], acck[DB];
+            auto mfma_db = [&](int db) __attribute__((always_inline)) {
 #pragma unroll
                 for (int kq = 0; kq < KQ; ++kq) {
                     const v4i av = reinterpret_cast<const v4i*>(cur.dot)[kq * 4 * D + g * D + 16 * db + n16];
@@ -344,14 +342,21 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
                     const v2i r1 = lds_read_tr8(cur.q + off_r32(qa, 16 * db, D) + 8 * hf);
                     const v2i r2 = lds_read_tr8(cur.q + off_r32(qa + 32, 16 * db, D) + 8 * hf);
                     const v4i ak = v4i{r1[0], r1[1], r2[0], r2[1]};
-                    accv = mfma16_i8(av, pop[kq], kq == 0 ? magic4 : accv);
-                    acck = mfma16_i8(ak, dsop[kq], kq == 0 ? magic4 : acck);
+                    accv[db] = mfma16_i8(av, pop[kq], kq == 0 ? magic4 : accv[db]);
+                    acck[db] = mfma16_i8(ak, dsop[kq], kq == 0 ? magic4 : acck[db]);
                 }
+            };
+            // one d-block of products ahead of the accumulation of the previous
+            mfma_db(0);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                if (db + 1 < DB) mfma_db(db + 1);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    dvt[db][r] = fmaf(unmagic(accv[r]), fv, dvt[db][r]);
-                    dkt[db][r] = fmaf(unmagic(acck[r]), fk, dkt[db][r]);
+                    dvt[db][r] = fmaf(unmagic(accv[db][r]), fv, dvt[db][r]);
+                    dkt[db][r] = fmaf(unmagic(acck[db][r]), fk, dkt[db][r]);
                 }
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
         if (more && tid < BQ) {
