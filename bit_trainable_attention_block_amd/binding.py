@@ -249,11 +249,6 @@ def layout_offsets(kind: str, N: int, D: int):
     r = np.broadcast_to(r, (N, D)); c = np.broadcast_to(c, (N, D))
     if kind == "R32":
         return (r // 32) * (32 * D) + (((c // 16) * 32 + r % 32) * 16) + c % 16
-    if kind == "C32P":
-        rr = r % 32
-        h = (rr // 4) % 2
-        e = (rr // 8) * 4 + rr % 4
-        return (r // 32) * (32 * D) + (h * D + c) * 16 + e
     if kind == "C64P":
         rr = r % 64
         g = (rr // 4) % 4

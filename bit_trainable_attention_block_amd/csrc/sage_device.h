@@ -1,17 +1,13 @@
 // Device-side helpers shared by the SageBwd kernels (gfx950 only).
 //
 // Matrix-instruction operand orders used throughout (wave64, lane l):
-//   v_mfma_i32_32x32x32_i8 / v_mfma_f32_32x32x16_*: A row m = l%32, B column
-//     n = l%32; both carry the contraction index in lane half h = l/32 and
-//     register byte/element e; result register j holds row 8*(j/4)+4*h+j%4,
-//     column l%32.
 //   v_mfma_i32_16x16x64_i8 / v_mfma_f32_16x16x32_*: A row m = l%16, B column
 //     n = l%16; lane group g = l/16 and byte/element e carry the contraction
 //     index; result register j holds row 4*g+j, column l%16.
-// A and B only have to agree on which (h|g, e) carries which contraction
+// A and B only have to agree on which (g, e) carries which contraction
 // index, so a result tile can feed the next product straight from registers
 // once the other operand is stored in the matching permuted order (the
-// C32P / C64P layouts of sage.h).
+// C64P layout of sage.h).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -20,9 +16,7 @@
 namespace sage {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
-typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef uint16_t u16;
@@ -59,13 +53,6 @@ __device__ __forceinline__ u16 from_f32(float x) {
 // sage.h.  D is the head dimension.
 __device__ __forceinline__ int off_r32(int row, int col, int D) {
     return (row >> 5) * (32 * D) + (((col >> 4) * 32 + (row & 31)) << 4) + (col & 15);
-}
-// C32P: 32-row group, (h, e) -> in-group row 8*(e/4) + 4*h + e%4.
-__device__ __forceinline__ int off_c32p(int row, int col, int D) {
-    int r = row & 31;
-    int h = (r >> 2) & 1;
-    int e = ((r >> 3) << 2) | (r & 3);
-    return (row >> 5) * (32 * D) + ((h * D + col) << 4) + e;
 }
 // C64P: 64-row group, (g, e) -> in-group row 16*(e/4) + 4*g + e%4.
 __device__ __forceinline__ int off_c64p(int row, int col, int D) {
@@ -161,9 +148,6 @@ constexpr int kMagicBits = 0x4B400000;
 constexpr float kMagicF = 12582912.0f;
 __device__ __forceinline__ float unmagic(int x) { return __int_as_float(x) - kMagicF; }
 
-__device__ __forceinline__ v16i mfma32_i8(v4i a, v4i b, v16i c) {
-    return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
-}
 __device__ __forceinline__ v4i mfma16_i8(v4i a, v4i b, v4i c) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }

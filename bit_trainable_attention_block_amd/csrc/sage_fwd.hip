@@ -1,24 +1,28 @@
 // SageBwd INT8 forward (SageBwd method summary, forward steps (3)-(5);
 // SageAttention3 write-up Eq. 1 and Eq. 8).
 //
-// One workgroup = 4 waves = 128 queries of one head; wave w owns 32 queries.
-// Key/value tiles of 64 keys (one K/V quantisation block) stream through a
-// double-buffered LDS stage: the K codes (R32 row tiles) and the V codes (C32P
-// column tiles) are contiguous 64*D-byte runs in HBM, so a stage is a plain
-// coalesced copy and every operand read is a conflict-free 16-byte LDS read.
+// One workgroup = 8 waves = 128 queries of one head; wave w owns 16 queries,
+// so a wave holds little state (about 100 registers) and four waves share
+// each SIMD: while some wait on products or LDS, others keep the vector
+// units busy.  Key/value tiles of 64 keys (one K/V quantisation block)
+// stream through two LDS stages filled one tile ahead by asynchronous copies:
+// the K codes (R32 row tiles) and the V codes (C64P column tiles) are
+// contiguous 64*D-byte runs in HBM.
 //
-// Per tile and wave, on the matrix cores (v_mfma_i32_32x32x32_i8):
-//   S^T (64 keys x 32 queries) = K^_j Q^_i^T            int32
-// so each lane holds 32 logits of ONE query (lane % 32) and row statistics
-// are in-lane plus one exchange between the two lane halves.  Then, in
-// float32 on the vector units and in log2 units (x = S * log2 e):
+// Per tile and wave, on the matrix cores (v_mfma_i32_16x16x64_i8):
+//   S^T (64 keys x 16 queries) = K^_j Q^_i^T            int32
+// each lane holds the 16 logits of one query (lane % 16) in four key blocks
+// of four, the other 48 keys of that query being in the lanes 16, 32 and 48
+// away (row statistics: in-lane, then two lane swaps).  Then, in float32 and
+// log2 units (x = S * log2 e):
 //   rm = rowmax, m = reference maximum (moved lazily, see below),
 //   P^ codes = rint(127 * 2^(x - rm))         (= P~ / s_P, independent of m)
 //   s_P = 2^(rm - m) / 127,  l += s_P * sum(127 * 2^(x - rm))
 // and the codes feed the second product straight from registers:
-//   O^T (D x 32 queries) += V^_j^T P^^T  (int32) -> O = O * alpha + f32 * s_P s_V.
-// The result register order of S^T is the operand order of P^ once the V
-// codes are stored permuted (C32P), so no shuffle or LDS round trip is needed.
+//   O^T (D x 16 queries) += V^_j^T P^^T  (int32) -> O = O * alpha + f32 * s_P s_V.
+// The result order of S^T (key 16 kb + 4 g + r in lane group g, register r
+// of key block kb) is the operand order of a 64-key contraction once the V
+// codes are stored permuted (C64P), so no shuffle or LDS round trip is needed.
 #include <climits>
 #include <type_traits>
 
@@ -42,9 +46,10 @@ struct FwdArgs {
     double scale2;  // softmax scale * log2(e)
 };
 
-constexpr int kQTile = 128;  // queries per workgroup
-constexpr int kKTile = 64;   // keys per stage (= the K/V quantisation block)
-constexpr float kLazy = 8.f; // log2 slack before the reference maximum moves
+constexpr int kWaves = 8;
+constexpr int kQTile = 16 * kWaves;  // queries per workgroup
+constexpr int kKTile = 64;           // keys per stage (= the K/V quantisation block)
+constexpr float kLazy = 8.f;         // log2 slack before the reference maximum moves
 constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23: x + kMagic holds rint(x) in its low byte
 
 // Byte 0 of four magic-rounded floats -> one dword.
@@ -54,10 +59,31 @@ __device__ __forceinline__ int pack_magic(float a, float b, float c, float d) {
     return (int)(lo | hi);
 }
 
+// Maximum / sum over the four lane groups holding one query (lanes l, l^16,
+// l^32, l^48): each lane swap returns a lane's own value and its partner's.
+__device__ __forceinline__ float qmax4(float x) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ int qmax4i(int x) {
+    auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    x = max((int)a[0], (int)a[1]);
+    auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return max((int)b[0], (int)b[1]);
+}
+__device__ __forceinline__ float qsum4(float x) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 template <int D>
 struct FwdStage {
     int8_t k[kKTile * D];   // K codes of the key tile, R32
-    int8_t v[kKTile * D];   // V codes of the key tile, C32P
+    int8_t v[kKTile * D];   // V codes of the key tile, C64P
 };
 
 // Lowest integer sum a product can hold (|sum| <= 127^2 D < 2^21), as the
@@ -66,17 +92,19 @@ struct FwdStage {
 constexpr int kMaskedSum = kMagicBits - (1 << 22) + 1;
 
 template <bool BF16, int D, bool CAUSAL, bool QSMOOTH>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
-    constexpr int TILE_BYTES = kKTile * D;           // K or V codes of one tile
-    constexpr int KS = D / 32;                       // contraction steps over d
-    constexpr int DB = D / 32;                       // 32-wide blocks of d
-    static_assert(TILE_BYTES % 4096 == 0, "stage shape");
+__global__ __launch_bounds__(64 * kWaves, 2) void fwd_kernel(FwdArgs a) {
+    constexpr int TILE_BYTES = kKTile * D;   // K or V codes of one tile
+    constexpr int KS = D / 64;               // contraction steps over d (S^T)
+    constexpr int DB = D / 16;               // 16-row blocks of d (O^T)
+    constexpr int NT = 64 * kWaves;
+    static_assert(TILE_BYTES % 1024 == 0, "stage shape");
     __shared__ __align__(16) FwdStage<D> st[2];
 
     const int N = a.N;
     const int Tn = N / kKTile;
     const int Tm = N / a.bq;
     const int ntiles = (N + kQTile - 1) / kQTile;
+
     // Workgroup -> (query tile, head).  Blocks are dealt to the eight XCDs
     // round-robin; when the heads divide evenly each XCD owns whole heads
     // (their K/V stay in its L2), and across an XCD's heads the query tiles
@@ -100,44 +128,46 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63, n = lane & 31, hh = lane >> 5;
-    const int q0 = qt * kQTile + w * 32;
+    const int lane = tid & 63, n = lane & 15, g = lane >> 4;
+    const int q0 = qt * kQTile + w * 16;
     const bool active = q0 < N;
     const int query = q0 + n;
 
     int jend = Tn;
     if (CAUSAL) jend = min(Tn, (qt * kQTile + kQTile) / kKTile);
 
-    // Q codes as the B operand of S^T: lane = query, 16 bytes of d per step.
+    // Q codes as the B operand of S^T: column = query (lane % 16), 16 bytes
+    // of d per lane group and contraction step.
     v4i qop[KS];
     float sqv = 0.f;
     if (active) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            qop[ks] = *reinterpret_cast<const v4i*>(a.q + head + off_r32(query, 32 * ks + 16 * hh, D));
+            qop[ks] = *reinterpret_cast<const v4i*>(a.q + head + off_r32(query, 64 * ks + 16 * g, D));
         sqv = a.sq[(size_t)bh * Tm + q0 / a.bq];
+    } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qop[ks] = v4i{0, 0, 0, 0};
     }
     const float* bias_row = nullptr;
     if (QSMOOTH && active) bias_row = a.qk_bias + ((size_t)bh * Tm + q0 / a.bq) * N;
 
     float m = -INFINITY, l = 0.f;
-    float o[DB][16];
+    v4f o[DB];
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
-    v16i magic16;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) magic16[r] = kMagicBits;
+    for (int db = 0; db < DB; ++db) o[db] = v4f{0, 0, 0, 0};
+    const v4i magic4 = v4i{kMagicBits, kMagicBits, kMagicBits, kMagicBits};
 
     // asynchronous copy of key tile j (K and V codes: two contiguous runs)
     auto load = [&](int j, FwdStage<D>& dst) __attribute__((always_inline)) {
         const int8_t* ks_ = a.k + head + (size_t)j * TILE_BYTES;
         const int8_t* vs_ = a.vt + head + (size_t)j * TILE_BYTES;
 #pragma unroll
-        for (int c0 = 0; c0 < TILE_BYTES; c0 += 4096) {
-            copy16_to_lds(ks_ + c0 + w * 1024 + lane * 16, dst.k + c0 + w * 1024);
-            copy16_to_lds(vs_ + c0 + w * 1024 + lane * 16, dst.v + c0 + w * 1024);
+        for (int c0 = 0; c0 < TILE_BYTES; c0 += NT * 16) {
+            if (c0 + w * 1024 < TILE_BYTES) {   // a d=64 tile is half a round
+                copy16_to_lds(ks_ + c0 + w * 1024 + lane * 16, dst.k + c0 + w * 1024);
+                copy16_to_lds(vs_ + c0 + w * 1024 + lane * 16, dst.v + c0 + w * 1024);
+            }
         }
     };
 
@@ -150,83 +180,74 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         if (j + 1 < jend) load(j + 1, st[(j + 1) & 1]);
 
         const int k0 = j * kKTile;
-        const bool wave_on = active && (!CAUSAL || k0 <= q0 + 31);
+        const bool wave_on = active && (!CAUSAL || k0 <= q0 + 15);
         if (wave_on) {
-            const v4i* lk = reinterpret_cast<const v4i*>(cur.k);
             const v4i* lv = reinterpret_cast<const v4i*>(cur.v);
-            v16i s[2];
+            // S^T for the four 16-key blocks of the tile
+            v4i s[4];
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
+            for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    v4i av = lk[mb * 2 * D + (2 * ks + hh) * 32 + n];
-                    s[mb] = mfma32_i8(av, qop[ks], ks == 0 ? magic16 : s[mb]);
+                    const v4i av = *reinterpret_cast<const v4i*>(cur.k + off_r32(16 * kb + n, 64 * ks + 16 * g, D));
+                    s[kb] = mfma16_i8(av, qop[ks], ks == 0 ? magic4 : s[kb]);
                 }
             }
             // one rounding from the exact product of the scales (keeps the
             // logits within an ulp of the definition)
             const float c2 = (float)((double)sqv * (double)a.sk[(size_t)bh * Tn + j] * a.scale2);
             float rm, sum;
-            v4i pc[2];
+            v4i pc;
             auto codes = [&](auto mask_tag) __attribute__((always_inline)) {
                 constexpr bool MASK = decltype(mask_tag)::value;
                 // Row maximum of this tile (log2 units).  Without Q-smoothing the
                 // logits are one positive scale times the integer sums, so the
                 // maximum is taken on the accumulator bits (which order like the
                 // sums); masked keys never win it.
-                float bias2[2][16];
+                float bias2[4][4];
                 if (QSMOOTH) {
                     rm = -INFINITY;
 #pragma unroll
-                    for (int mb = 0; mb < 2; ++mb)
+                    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int key = k0 + 32 * mb + 8 * (r >> 2) + 4 * hh + (r & 3);
-                            bias2[mb][r] = (float)((double)bias_row[key] * kLog2e_d);
-                            const float v = fmaf(unmagic(s[mb][r]), c2, bias2[mb][r]);
+                        for (int r = 0; r < 4; ++r) {
+                            const int key = k0 + 16 * kb + 4 * g + r;
+                            bias2[kb][r] = (float)((double)bias_row[key] * kLog2e_d);
+                            const float v = fmaf(unmagic(s[kb][r]), c2, bias2[kb][r]);
                             if (!(MASK && key > query)) rm = fmaxf(rm, v);
                         }
+                    rm = qmax4(rm);
                 } else {
                     int im = kMaskedSum;
-                    if (MASK) {
 #pragma unroll
-                        for (int mb = 0; mb < 2; ++mb)
+                    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-                            for (int r = 0; r < 16; ++r) {
-                                const int key = k0 + 32 * mb + 8 * (r >> 2) + 4 * hh + (r & 3);
-                                im = max(im, key > query ? kMaskedSum : s[mb][r]);
-                            }
-                    } else {
-#pragma unroll
-                        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                            for (int r = 0; r < 16; r += 2) im = max(im, max(s[mb][r], s[mb][r + 1]));
-                    }
-                    rm = unmagic(im) * c2;
+                        for (int r = 0; r < 4; ++r) {
+                            const int key = k0 + 16 * kb + 4 * g + r;
+                            im = max(im, (MASK && key > query) ? kMaskedSum : s[kb][r]);
+                        }
+                    rm = unmagic(qmax4i(im)) * c2;
                 }
-                rm = fmaxf(rm, __shfl_xor(rm, 32));
                 const float shift = rm - kLog2_127;
                 sum = 0.f;
 #pragma unroll
-                for (int mb = 0; mb < 2; ++mb) {
-                    float c[16];
+                for (int kb = 0; kb < 4; ++kb) {
+                    float c[4];
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        float x = QSMOOTH ? fmaf(unmagic(s[mb][r]), c2, bias2[mb][r] - shift)
-                                          : fmaf(unmagic(s[mb][r]), c2, -shift);
+                    for (int r = 0; r < 4; ++r) {
+                        float x = QSMOOTH ? fmaf(unmagic(s[kb][r]), c2, bias2[kb][r] - shift)
+                                          : fmaf(unmagic(s[kb][r]), c2, -shift);
                         if (MASK) {
-                            const int key = k0 + 32 * mb + 8 * (r >> 2) + 4 * hh + (r & 3);
+                            const int key = k0 + 16 * kb + 4 * g + r;
                             if (key > query) x = -INFINITY;
                         }
                         const float e = __builtin_amdgcn_exp2f(x);  // 127 * 2^(x - rm), in [0, 127]
                         sum += e;
                         c[r] = e + kMagic;                           // rint(e) in the low byte
                     }
-#pragma unroll
-                    for (int qd = 0; qd < 4; ++qd)
-                        pc[mb][qd] = pack_magic(c[4 * qd], c[4 * qd + 1], c[4 * qd + 2], c[4 * qd + 3]);
+                    pc[kb] = pack_magic(c[0], c[1], c[2], c[3]);
                 }
-                sum += __shfl_xor(sum, 32);
+                sum = qsum4(sum);
             };
             // Diagonal tiles (some key after some query) take the masked
             // instantiation; every other tile runs without a compare.
@@ -243,56 +264,52 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
                 const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 0 on the first tile
                 l *= alpha;
 #pragma unroll
-                for (int db = 0; db < DB; ++db)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+                for (int db = 0; db < DB; ++db) o[db] *= alpha;
             }
             l = fmaf(sum, sP, l);
             m = m_new;
             const float beta = sP * a.sv[(size_t)bh * Tn + j];
+            // O^T += V^^T P^^T: one product per 16 rows of d, the 64 keys of the
+            // tile as the contraction (V codes C64P, P codes from registers)
+            v4i acc[DB];
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                v16i acc;
+            for (int db = 0; db < DB; ++db) acc[db] = mfma16_i8(lv[g * D + 16 * db + n], pc, magic4);
 #pragma unroll
-                for (int mb = 0; mb < 2; ++mb) {
-                    v4i av = lv[(mb * 2 + hh) * D + 32 * db + n];
-                    acc = mfma32_i8(av, pc[mb], mb == 0 ? magic16 : acc);
-                }
+            for (int db = 0; db < DB; ++db)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) o[db][r] = fmaf(unmagic(acc[r]), beta, o[db][r]);
-            }
+                for (int r = 0; r < 4; ++r) o[db][r] = fmaf(unmagic(acc[db][r]), beta, o[db][r]);
         }
         wait_vmem();       // the next tile has landed
         __syncthreads();   // ... for every wave; this stage may be overwritten
     }
 
+    // O^T block db holds rows d = 16 db + 4 g + r of column (query) n
     if (active) {
         u16* O = reinterpret_cast<u16*>(a.O) + head + (size_t)query * D;
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DB; ++db) {
+            u16 h[4];
 #pragma unroll
-            for (int qd = 0; qd < 4; ++qd) {
-                u16 h[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) h[r] = from_f32<BF16>(__fdiv_rn(o[db][4 * qd + r], l));
-                uint2 pk;
-                pk.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
-                pk.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
-                *reinterpret_cast<uint2*>(O + 32 * db + 8 * qd + 4 * hh) = pk;
-            }
-        if (hh == 0) a.L[(size_t)bh * N + query] = (m + log2f(l)) * kLn2;
+            for (int r = 0; r < 4; ++r) h[r] = from_f32<BF16>(__fdiv_rn(o[db][r], l));
+            uint2 pk;
+            pk.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+            pk.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+            *reinterpret_cast<uint2*>(O + 16 * db + 4 * g) = pk;
+        }
+        if (g == 0) a.L[(size_t)bh * N + query] = (m + log2f(l)) * kLn2;
     }
 }
 
 template <bool BF16, int D>
 hipError_t fwd_dispatch(const Dims& d, const FwdArgs& a, hipStream_t s) {
     const dim3 grid(((d.N + kQTile - 1) / kQTile) * d.BH());
+    const dim3 block(64 * kWaves);
     if (d.causal) {
-        if (d.q_smooth) fwd_kernel<BF16, D, true, true><<<grid, 256, 0, s>>>(a);
-        else fwd_kernel<BF16, D, true, false><<<grid, 256, 0, s>>>(a);
+        if (d.q_smooth) fwd_kernel<BF16, D, true, true><<<grid, block, 0, s>>>(a);
+        else fwd_kernel<BF16, D, true, false><<<grid, block, 0, s>>>(a);
     } else {
-        if (d.q_smooth) fwd_kernel<BF16, D, false, true><<<grid, 256, 0, s>>>(a);
-        else fwd_kernel<BF16, D, false, false><<<grid, 256, 0, s>>>(a);
+        if (d.q_smooth) fwd_kernel<BF16, D, false, true><<<grid, block, 0, s>>>(a);
+        else fwd_kernel<BF16, D, false, false><<<grid, block, 0, s>>>(a);
     }
     return hipGetLastError();
 }

@@ -102,12 +102,11 @@ __device__ __forceinline__ void codes_to_lds(const float (&x)[Blk<R, D>::PER_T][
     }
 }
 
-enum Layout { R32, C32P, C64P, C64N };
+enum Layout { R32, C64P, C64N };
 
 // In-block row of byte e of output chunk (h|g) for the column layouts.
 template <Layout L>
 __device__ __forceinline__ int col_layout_row(int grp_part, int e) {
-    if constexpr (L == C32P) return 8 * (e >> 2) + 4 * grp_part + (e & 3);
     if constexpr (L == C64P) return 16 * (e >> 2) + 4 * grp_part + (e & 3);
     return 16 * grp_part + e;  // C64N
 }
@@ -124,7 +123,7 @@ __device__ __forceinline__ void store_codes(const uint8_t* codes, int8_t* __rest
             const int col16 = rem / 32, r = rem % 32;
             out = *reinterpret_cast<const v4i*>(codes + (32 * g + r) * D + col16 * 16);
         } else {
-            constexpr int GR = (L == C32P) ? 32 : 64;  // rows per group
+            constexpr int GR = 64;                     // rows per group
             constexpr int PARTS = GR / 16;             // h or g values
             const int grp = oc / (PARTS * D), rem = oc % (PARTS * D);
             const int part = rem / D, col = rem % D;
@@ -166,7 +165,7 @@ __global__ void zero_f64_kernel(double* p, int n) {
     if (i < n) p[i] = 0.0;
 }
 
-// V blocks (64 rows): codes -> vt (C32P), scale -> sv, raw copy -> vr (R16H).
+// V blocks (64 rows): codes -> vt (C64P), scale -> sv, raw copy -> vr (R16H).
 // K blocks (same rows): float64 column sums accumulated into ws[bh][D]
 // (exact: sums of 16-bit values fit float64 without rounding, so the order of
 // the atomic additions does not change the result).
@@ -200,7 +199,7 @@ __global__ __launch_bounds__(kThreads) void quant_v_ksum_kernel(
     codes_to_lds<R, D>(x, s, codes);
     if (threadIdx.x == 0) sv[(size_t)bh * (N / R) + j] = s;
     __syncthreads();
-    store_codes<C32P, R, D>(codes, vt + head + (size_t)row0 * D);
+    store_codes<C64P, R, D>(codes, vt + head + (size_t)row0 * D);
 
     if (k_smooth) {
         load_block<R, D>(K + head + (size_t)row0 * D, raw);

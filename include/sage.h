@@ -34,9 +34,6 @@
  * is 16, 32 or 64 consecutive rows; each layout is [B, H, N/group, ...]):
  *   R32   row tiles:  byte (row, col) at group row/32, offset
  *         ((col/16) * 32 + row%32) * 16 + col%16.
- *   C32P  column tiles, 32-row groups, permuted: byte (row, col) at group
- *         row/32, offset (h * D + col) * 16 + e, where the in-group row
- *         r = 8*(e/4) + 4*h + e%4  (h in {0,1}, e in [0,16)).
  *   C64P  column tiles, 64-row groups, permuted: offset (g * D + col) * 16 + e,
  *         with in-group row r = 16*(e/4) + 4*g + e%4  (g in [0,4)).
  *   C64N  column tiles, 64-row groups, natural order: offset
@@ -92,7 +89,7 @@ typedef struct sage_qtensors {
     int8_t* k;        /* R32,  N*D:   codes of K - mu_K (K if !k_smooth) */
     int8_t* kt;       /* C64N, N*D:   the same codes, column tiles */
     float* sk;        /* T_n floats:  K block scales */
-    int8_t* vt;       /* C32P, N*D:   codes of V, column tiles */
+    int8_t* vt;       /* C64P, N*D:   codes of V, column tiles */
     float* sv;        /* T_n floats:  V block scales */
     uint16_t* vr;     /* R16H, N*D*2: V re-laid as 16-bit row tiles */
     float* mu_k;      /* D floats:    K token mean (written if k_smooth) */

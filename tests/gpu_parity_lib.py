@@ -93,7 +93,7 @@ def check_quantize(cfg, inputs, g, b, h):
     np.testing.assert_array_equal(un("qt", "C64P"), qz.Qc.astype(np.int8))
     np.testing.assert_array_equal(un("k", "R32"), qz.Kc.astype(np.int8))
     np.testing.assert_array_equal(un("kt", "C64N"), qz.Kc.astype(np.int8))
-    np.testing.assert_array_equal(un("vt", "C32P"), qz.Vc.astype(np.int8))
+    np.testing.assert_array_equal(un("vt", "C64P"), qz.Vc.astype(np.int8))
     np.testing.assert_array_equal(qt["sq"][b, h], qz.sQ.astype(np.float32))
     np.testing.assert_array_equal(qt["sk"][b, h], qz.sK.astype(np.float32))
     np.testing.assert_array_equal(qt["sv"][b, h], qz.sV.astype(np.float32))
