@@ -187,11 +187,16 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
     const int8_t* qh = q + head;
     const int8_t* doth = dot + head;
     const u16* dorh = dor + head;
+    // Q-smoothing bias of this lane's key for the current query tile, loaded
+    // one tile ahead (a key past a ragged end reads nothing)
+    float nbias = 0.f;
+    if (QSMOOTH && kv_on) nbias = qk_bias[((size_t)bh * Tm + istart) * N + key];
 
     // One query tile, read from `cur`; the next one is copied into `nxt`.
     auto step = [&](int i, BwdStage<BQ, D>& cur, BwdStage<BQ, D>& nxt) __attribute__((always_inline)) {
         const int qbase = i * BQ;
         const bool more = i + 1 < Tm;
+        const float biasv = nbias;
         // small loads of the next tile first: waiting for them never waits
         // for the copies issued after them
         float nL = 0.f, nd = 0.f;
@@ -199,6 +204,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
             nL = Lh[qbase + BQ + tid];
             nd = dlh[qbase + BQ + tid];
         }
+        if (QSMOOTH && kv_on && more) nbias = qk_bias[((size_t)bh * Tm + i + 1) * N + key];
         if (more)
             stage_query_tile<BQ, D>(nxt, qh + (size_t)(qbase + BQ) * D, doth + (size_t)(qbase + BQ) * D,
                                     dorh + (size_t)(qbase + BQ) * D, w, lane);
@@ -229,7 +235,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
             float pmax = 0.f, dsmax = 0.f;
             const float c2 = (float)((double)sqi * (double)skj * scale * kLog2e_d);  // one rounding
             float bias2 = 0.f;
-            if (QSMOOTH) bias2 = (float)((double)qk_bias[((size_t)bh * Tm + i) * N + key] * kLog2e_d);
+            if (QSMOOTH) bias2 = (float)((double)biasv * kLog2e_d);
             // ---- S and dP for this wave's 16 keys and all BQ queries, one
             // 16-query block ahead of the vector work on the previous block
             v4i s[MB];
@@ -365,6 +371,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
             nxt.delta[tid] = nd;
         }
         wait_vmem();       // the asynchronous copies are not seen by the compiler's waits
+        if (QSMOOTH) settle(nbias);
         __syncthreads();   // the next tile has landed in LDS for every wave; `cur` may be overwritten
     };
 
@@ -376,9 +383,14 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
         st[0].delta[tid] = dlh[istart * BQ + tid];
     }
     wait_vmem();       // the asynchronous copies are not seen by the compiler's waits
+    // the operands held in registers are complete here, not at their first
+    // use inside the loop (after that tile's copies)
+#pragma unroll
+    for (int ks = 0; ks < KS8; ++ks) settle(kop[ks]);
+#pragma unroll
+    for (int ks = 0; ks < KSH; ++ks) settle(vop[ks]);
+    if (QSMOOTH) settle(nbias);
     __syncthreads();
-    // pairs of tiles in straight-line code (no merge over the accumulators
-    // inside the loop), then an odd last tile
     for (int i = istart; i < Tm; ++i) {
         const int b = (i - istart) & 1;
         step(i, st[b], st[b ^ 1]);

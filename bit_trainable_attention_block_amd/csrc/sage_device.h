@@ -138,6 +138,14 @@ __device__ __forceinline__ void copy16_to_lds(const void* src, void* lds_wave) {
         : "memory");
 }
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// The compiler does not count the copies above either, so a register loaded
+// from global memory before some copies and first used after them would get
+// its wait at the use, where that wait (vmcnt counts in issue order) also
+// waits for every copy issued in between.  settle() right after wait_vmem()
+// makes the compiler take its wait for the register there instead, where it
+// costs nothing.
+template <typename T>
+__device__ __forceinline__ void settle(T& x) { asm volatile("" : "+v"(x)); }
 
 // ---------------------------------------------------------------- MFMA
 // Integer products with a float conversion for free: an int32 accumulator

@@ -40,7 +40,7 @@ struct FwdArgs {
     const int8_t* vt;
     const float* sv;
     const float* qk_bias;
-    void* O;
+    u16* O;
     float* L;
     int N, bq;
     double scale2;  // softmax scale * log2(e)
@@ -82,8 +82,9 @@ __device__ __forceinline__ float qsum4(float x) {
 
 template <int D>
 struct FwdStage {
-    int8_t k[kKTile * D];   // K codes of the key tile, R32
-    int8_t v[kKTile * D];   // V codes of the key tile, C64P
+    int8_t k[kKTile * D];          // K codes of the key tile, R32
+    int8_t v[kKTile * D];          // V codes of the key tile, C64P
+    float bias[kQTile / 64][kKTile];  // Q-smoothing bias rows of the tile's Q blocks
 };
 
 // Lowest integer sum a product can hold (|sum| <= 127^2 D < 2^21), as the
@@ -92,7 +93,11 @@ struct FwdStage {
 constexpr int kMaskedSum = kMagicBits - (1 << 22) + 1;
 
 template <bool BF16, int D, bool CAUSAL, bool QSMOOTH>
-__global__ __launch_bounds__(64 * kWaves, 2) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(64 * kWaves, 2) void fwd_kernel(
+    const int8_t* __restrict__ q, const float* __restrict__ sq, const int8_t* __restrict__ k,
+    const float* __restrict__ sk, const int8_t* __restrict__ vt, const float* __restrict__ sv,
+    const float* __restrict__ qk_bias, u16* __restrict__ Out, float* __restrict__ L, int N, int bq,
+    double scale2) {
     constexpr int TILE_BYTES = kKTile * D;   // K or V codes of one tile
     constexpr int KS = D / 64;               // contraction steps over d (S^T)
     constexpr int DB = D / 16;               // 16-row blocks of d (O^T)
@@ -100,9 +105,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void fwd_kernel(FwdArgs a) {
     static_assert(TILE_BYTES % 1024 == 0, "stage shape");
     __shared__ __align__(16) FwdStage<D> st[2];
 
-    const int N = a.N;
     const int Tn = N / kKTile;
-    const int Tm = N / a.bq;
+    const int Tm = N / bq;
     const int ntiles = (N + kQTile - 1) / kQTile;
 
     // Workgroup -> (query tile, head).  Blocks are dealt to the eight XCDs
@@ -143,14 +147,12 @@ __global__ __launch_bounds__(64 * kWaves, 2) void fwd_kernel(FwdArgs a) {
     if (active) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            qop[ks] = *reinterpret_cast<const v4i*>(a.q + head + off_r32(query, 64 * ks + 16 * g, D));
-        sqv = a.sq[(size_t)bh * Tm + q0 / a.bq];
+            qop[ks] = *reinterpret_cast<const v4i*>(q + head + off_r32(query, 64 * ks + 16 * g, D));
+        sqv = sq[(size_t)bh * Tm + q0 / bq];
     } else {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) qop[ks] = v4i{0, 0, 0, 0};
     }
-    const float* bias_row = nullptr;
-    if (QSMOOTH && active) bias_row = a.qk_bias + ((size_t)bh * Tm + q0 / a.bq) * N;
 
     float m = -INFINITY, l = 0.f;
     v4f o[DB];
@@ -158,10 +160,11 @@ __global__ __launch_bounds__(64 * kWaves, 2) void fwd_kernel(FwdArgs a) {
     for (int db = 0; db < DB; ++db) o[db] = v4f{0, 0, 0, 0};
     const v4i magic4 = v4i{kMagicBits, kMagicBits, kMagicBits, kMagicBits};
 
-    // asynchronous copy of key tile j (K and V codes: two contiguous runs)
+    // asynchronous copy of key tile j (K and V codes: two contiguous runs;
+    // with Q-smoothing also the tile's 64 bias values of each Q block)
     auto load = [&](int j, FwdStage<D>& dst) __attribute__((always_inline)) {
-        const int8_t* ks_ = a.k + head + (size_t)j * TILE_BYTES;
-        const int8_t* vs_ = a.vt + head + (size_t)j * TILE_BYTES;
+        const int8_t* ks_ = k + head + (size_t)j * TILE_BYTES;
+        const int8_t* vs_ = vt + head + (size_t)j * TILE_BYTES;
 #pragma unroll
         for (int c0 = 0; c0 < TILE_BYTES; c0 += NT * 16) {
             if (c0 + w * 1024 < TILE_BYTES) {   // a d=64 tile is half a round
@@ -169,10 +172,23 @@ __global__ __launch_bounds__(64 * kWaves, 2) void fwd_kernel(FwdArgs a) {
                 copy16_to_lds(vs_ + c0 + w * 1024 + lane * 16, dst.v + c0 + w * 1024);
             }
         }
+        if (QSMOOTH && w == kWaves - 1) {
+            // lane group r of the first kQTile/64 groups: Q block row r, 16 B
+            // per lane (a row of 64 floats lands in bias[r])
+            const int r = lane >> 4;
+            const int qb = qt * kQTile / bq + r;
+            if (r < kQTile / bq && qb < Tm)
+                copy16_to_lds(qk_bias + ((size_t)bh * Tm + qb) * N + (size_t)j * kKTile + 4 * (lane & 15),
+                              &dst.bias[0][0]);
+        }
     };
 
     if (jend > 0) load(0, st[0]);
     wait_vmem();   // the asynchronous copies are not seen by the compiler's waits
+    // the Q codes are complete here, not at their first use inside the loop
+    // (after that tile's copies)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) settle(qop[ks]);
     __syncthreads();
 
     for (int j = 0; j < jend; ++j) {
@@ -195,7 +211,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void fwd_kernel(FwdArgs a) {
             }
             // one rounding from the exact product of the scales (keeps the
             // logits within an ulp of the definition)
-            const float c2 = (float)((double)sqv * (double)a.sk[(size_t)bh * Tn + j] * a.scale2);
+            const float c2 = (float)((double)sqv * (double)sk[(size_t)bh * Tn + j] * scale2);
             float rm, sum;
             v4i pc;
             auto codes = [&](auto mask_tag) __attribute__((always_inline)) {
@@ -206,16 +222,19 @@ __global__ __launch_bounds__(64 * kWaves, 2) void fwd_kernel(FwdArgs a) {
                 // sums); masked keys never win it.
                 float bias2[4][4];
                 if (QSMOOTH) {
+                    const float* brow = cur.bias[(16 * w) / bq];
                     rm = -INFINITY;
 #pragma unroll
-                    for (int kb = 0; kb < 4; ++kb)
+                    for (int kb = 0; kb < 4; ++kb) {
+                        const v4f b4 = *reinterpret_cast<const v4f*>(brow + 16 * kb + 4 * g);
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             const int key = k0 + 16 * kb + 4 * g + r;
-                            bias2[kb][r] = (float)((double)bias_row[key] * kLog2e_d);
+                            bias2[kb][r] = (float)((double)b4[r] * kLog2e_d);
                             const float v = fmaf(unmagic(s[kb][r]), c2, bias2[kb][r]);
                             if (!(MASK && key > query)) rm = fmaxf(rm, v);
                         }
+                    }
                     rm = qmax4(rm);
                 } else {
                     int im = kMaskedSum;
@@ -268,7 +287,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void fwd_kernel(FwdArgs a) {
             }
             l = fmaf(sum, sP, l);
             m = m_new;
-            const float beta = sP * a.sv[(size_t)bh * Tn + j];
+            const float beta = sP * sv[(size_t)bh * Tn + j];
             // O^T += V^^T P^^T: one product per 16 rows of d, the 64 keys of the
             // tile as the contraction (V codes C64P, P codes from registers)
             v4i acc[DB];
@@ -285,7 +304,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void fwd_kernel(FwdArgs a) {
 
     // O^T block db holds rows d = 16 db + 4 g + r of column (query) n
     if (active) {
-        u16* O = reinterpret_cast<u16*>(a.O) + head + (size_t)query * D;
+        u16* O = Out + head + (size_t)query * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
             u16 h[4];
@@ -296,7 +315,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void fwd_kernel(FwdArgs a) {
             pk.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
             *reinterpret_cast<uint2*>(O + 16 * db + 4 * g) = pk;
         }
-        if (g == 0) a.L[(size_t)bh * N + query] = (m + log2f(l)) * kLn2;
+        if (g == 0) L[(size_t)bh * N + query] = (m + log2f(l)) * kLn2;
     }
 }
 
@@ -304,20 +323,23 @@ template <bool BF16, int D>
 hipError_t fwd_dispatch(const Dims& d, const FwdArgs& a, hipStream_t s) {
     const dim3 grid(((d.N + kQTile - 1) / kQTile) * d.BH());
     const dim3 block(64 * kWaves);
+#define SAGE_FWD_ARGS a.q, a.sq, a.k, a.sk, a.vt, a.sv, a.qk_bias, a.O, a.L, a.N, a.bq, a.scale2
     if (d.causal) {
-        if (d.q_smooth) fwd_kernel<BF16, D, true, true><<<grid, block, 0, s>>>(a);
-        else fwd_kernel<BF16, D, true, false><<<grid, block, 0, s>>>(a);
+        if (d.q_smooth) fwd_kernel<BF16, D, true, true><<<grid, block, 0, s>>>(SAGE_FWD_ARGS);
+        else fwd_kernel<BF16, D, true, false><<<grid, block, 0, s>>>(SAGE_FWD_ARGS);
     } else {
-        if (d.q_smooth) fwd_kernel<BF16, D, false, true><<<grid, block, 0, s>>>(a);
-        else fwd_kernel<BF16, D, false, false><<<grid, block, 0, s>>>(a);
+        if (d.q_smooth) fwd_kernel<BF16, D, false, true><<<grid, block, 0, s>>>(SAGE_FWD_ARGS);
+        else fwd_kernel<BF16, D, false, false><<<grid, block, 0, s>>>(SAGE_FWD_ARGS);
     }
+#undef SAGE_FWD_ARGS
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_fwd(const Dims& d, const sage_qtensors& qk, void* O, float* L, hipStream_t s) {
-    FwdArgs a{qk.q, qk.sq, qk.k, qk.sk, qk.vt, qk.sv, qk.qk_bias, O, L, d.N, d.bq, d.scale * kLog2e_d};
+    FwdArgs a{qk.q, qk.sq, qk.k, qk.sk, qk.vt, qk.sv, qk.qk_bias, static_cast<u16*>(O), L, d.N, d.bq,
+              d.scale * kLog2e_d};
     if (d.bf16) return d.D == 128 ? fwd_dispatch<true, 128>(d, a, s) : fwd_dispatch<true, 64>(d, a, s);
     return d.D == 128 ? fwd_dispatch<false, 128>(d, a, s) : fwd_dispatch<false, 64>(d, a, s);
 }
