@@ -95,19 +95,36 @@ struct BwdStage {
 
 // Asynchronous copy of query tile qbase (Q codes, dO codes, dO) into a stage.
 // The three regions are contiguous BQ*D, BQ*D and 2*BQ*D byte runs; each
-// wave instruction moves 1 KiB.
+// wave instruction moves 1 KiB, and round u of the eight waves moves the
+// stage's u-th 8 KiB.  When a region is a whole number of rounds (BQ*D a
+// multiple of 8 KiB) the region of a round is known at compile time.
 template <int BQ, int D>
 __device__ __forceinline__ void stage_query_tile(BwdStage<BQ, D>& st, const int8_t* q, const int8_t* dot,
                                                  const u16* dor, int w, int lane) {
     constexpr int QB = BQ * D, TOT = 4 * QB, ROUNDS = TOT / (8 * 1024);
     static_assert(TOT % (8 * 1024) == 0 && QB % 1024 == 0, "stage shape");
     const int8_t* dorb = reinterpret_cast<const int8_t*>(dor);
+    int8_t* dst_dor = reinterpret_cast<int8_t*>(st.dor);
 #pragma unroll
     for (int u = 0; u < ROUNDS; ++u) {
         const int c0 = u * 8 * 1024 + w * 1024;
         const int8_t* src;
         int8_t* dst;
-        if (c0 < QB) {
+        if constexpr (QB % (8 * 1024) == 0) {
+            constexpr int RQ = QB / (8 * 1024);   // rounds per 1-byte region
+            const int off = (u % RQ) * 8 * 1024 + w * 1024;
+            if (u < RQ) {
+                src = q + off;
+                dst = st.q + off;
+            } else if (u < 2 * RQ) {
+                src = dot + off;
+                dst = st.dot + off;
+            } else {
+                const int o2 = (u - 2 * RQ) * 8 * 1024 + w * 1024;
+                src = dorb + o2;
+                dst = dst_dor + o2;
+            }
+        } else if (c0 < QB) {
             src = q + c0;
             dst = st.q + c0;
         } else if (c0 < 2 * QB) {
@@ -115,7 +132,7 @@ __device__ __forceinline__ void stage_query_tile(BwdStage<BQ, D>& st, const int8
             dst = st.dot + (c0 - QB);
         } else {
             src = dorb + (c0 - 2 * QB);
-            dst = reinterpret_cast<int8_t*>(st.dor) + (c0 - 2 * QB);
+            dst = dst_dor + (c0 - 2 * QB);
         }
         copy16_to_lds(src + lane * 16, dst);
     }
