@@ -257,23 +257,36 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
             // 16-query block ahead of the vector work on the previous block
             v4i s[MB];
             v4f dp[MB];
-            auto mfma_block = [&](int mb) __attribute__((always_inline)) {
+            // LDS operands of a 16-query block are read one block before its
+            // products are issued, so the products never wait on LDS
+            struct OpsA {
+                v4i q[KS8];
+                v4i d[KSH];
+            };
+            OpsA opa[2];
+            auto read_block = [&](int mb, OpsA& o) __attribute__((always_inline)) {
                 const int row = 16 * mb + n16;  // query row (in tile) this lane supplies
 #pragma unroll
-                for (int ks = 0; ks < KS8; ++ks) {
-                    const v4i av = *reinterpret_cast<const v4i*>(cur.q + off_r32(row, 64 * ks + 16 * g, D));
-                    s[mb] = mfma16_i8(av, kop[ks], ks == 0 ? magic4 : s[mb]);
-                }
+                for (int ks = 0; ks < KS8; ++ks)
+                    o.q[ks] = *reinterpret_cast<const v4i*>(cur.q + off_r32(row, 64 * ks + 16 * g, D));
 #pragma unroll
-                for (int ks = 0; ks < KSH; ++ks) {
-                    const v4i av = *reinterpret_cast<const v4i*>(cur.dor + off_r16h(row, 32 * ks + 8 * g, D));
-                    dp[mb] = mfma16_h<BF16>(av, vop[ks], ks == 0 ? v4f{0, 0, 0, 0} : dp[mb]);
-                }
+                for (int ks = 0; ks < KSH; ++ks)
+                    o.d[ks] = *reinterpret_cast<const v4i*>(cur.dor + off_r16h(row, 32 * ks + 8 * g, D));
             };
-            mfma_block(0);
+            auto mfma_block = [&](int mb, const OpsA& o) __attribute__((always_inline)) {
+#pragma unroll
+                for (int ks = 0; ks < KS8; ++ks) s[mb] = mfma16_i8(o.q[ks], kop[ks], ks == 0 ? magic4 : s[mb]);
+#pragma unroll
+                for (int ks = 0; ks < KSH; ++ks)
+                    dp[mb] = mfma16_h<BF16>(o.d[ks], vop[ks], ks == 0 ? v4f{0, 0, 0, 0} : dp[mb]);
+            };
+            read_block(0, opa[0]);
+            if (MB > 1) read_block(1, opa[1]);
+            mfma_block(0, opa[0]);
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
-                if (mb + 1 < MB) mfma_block(mb + 1);
+                if (mb + 2 < MB) read_block(mb + 2, opa[mb & 1]);
+                if (mb + 1 < MB) mfma_block(mb + 1, opa[(mb + 1) & 1]);
                 const v4f l2 = *reinterpret_cast<const v4f*>(&cur.l2[16 * mb + 4 * g]);
                 const v4f dl = *reinterpret_cast<const v4f*>(&cur.delta[16 * mb + 4 * g]);
 #pragma unroll
