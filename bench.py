@@ -144,6 +144,47 @@ def cpu_baseline(cfg, heads=CPU_HEADS):
                       f"(quantize, fwd, bwd_pre, bwd), {dt:.1f} s on 1 host core"}
 
 
+def mfma_probe(iters=4000):
+    """Achieved rate of v_mfma_i32_16x16x64_i8 on this device (two 8-wave
+    workgroups per CU, register operands) and the shader clock under it."""
+    import torch
+
+    from bit_trainable_attention_block_amd import binding as bd
+    blocks = 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    clk = torch.zeros(3, dtype=torch.int64, device="cuda")
+    bd.probe_mfma_i8(blocks, 200, clk)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    bd.probe_mfma_i8(blocks, iters, clk)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    ops = blocks * 8 * iters * 8 * 32768
+    c = [int(v) for v in clk.cpu().tolist()]
+    tops = ops / (ms * 1e-3) / 1e12
+    return {"kernel": "v_mfma_i32_16x16x64_i8", "tops": round(tops, 1),
+            "clock_ghz": round(c[0] / (c[1] / 100e6) / 1e9, 3) if c[1] else None,
+            "frac_of_spec": round(tops / INT8_PEAK_TOPS, 4)}
+
+
+def copy_gbps(mib=512, reps=5):
+    """Plain device copy bandwidth (bytes read + written per second)."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    return 2 * n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -260,6 +301,19 @@ def main():
         "pct_int8_peak_fwd_bwd": round(100 * tops / INT8_PEAK_TOPS, 2),
         "pct_int8_peak_fwd_kernel": round(100 * fwd_ops / (call_ms["sage_fwd"] * 1e-3) / 1e12 / INT8_PEAK_TOPS, 2),
     }
+    # second denominator: the INT8 product rate this device achieves, and the
+    # HBM-bound calls against a plain copy (algorithmic bytes per call:
+    # quantise 15 B and the backward pre-pass 7 + 4/D B per (token, channel))
+    probe = mfma_probe()
+    breakdown["mfma_probe"] = probe
+    breakdown["pct_measured_i8_fwd_bwd"] = round(100 * tops / probe["tops"], 2)
+    elems = cfg.B * cfg.H * cfg.N * cfg.D
+    cp = copy_gbps()
+    q_gbps = 15 * elems / (call_ms["sage_quantize"] * 1e-3) / 1e9
+    p_gbps = (7 + 4 / cfg.D) * elems / (call_ms["sage_bwd_pre"] * 1e-3) / 1e9
+    breakdown["hbm"] = {"copy_gbps": round(cp, 1), "sage_quantize_gbps": round(q_gbps, 1),
+                        "sage_quantize_pct_copy": round(100 * q_gbps / cp, 1),
+                        "sage_bwd_pre_gbps": round(p_gbps, 1), "sage_bwd_pre_pct_copy": round(100 * p_gbps / cp, 1)}
 
     out = {
         "metric": METRIC, "value": round(tops, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,

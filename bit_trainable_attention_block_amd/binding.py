@@ -59,6 +59,8 @@ SIGNATURES = {
     "sage_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "sage_last_hip_error": (ctypes.c_int, []),
     "sage_version": (ctypes.c_char_p, []),
+    # include/sage_probe.h (measurement aid)
+    "sage_probe_mfma_i8": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _P, _P]),
 }
 
 _lib = None
@@ -223,6 +225,13 @@ def bwd(sh: Shape, qt, dot, L, dQ=None, dK=None, dV=None, ws=None, stream=None):
     _check(lib.sage_bwd(ctypes.byref(cs), ctypes.byref(_qstruct(qt)), ctypes.byref(_dostruct(dot)), _ptr(L),
                         _ptr(ws), _ptr(dQ), _ptr(dK), _ptr(dV), _stream(stream)), "sage_bwd")
     return dQ, dK, dV
+
+
+def probe_mfma_i8(blocks: int, iters: int, clk: torch.Tensor, stream=None):
+    """Measurement aid (include/sage_probe.h): `blocks` workgroups of 8 waves,
+    each wave issuing iters x 8 INT8 16x16x64 products; clk (3 int64 on the
+    device) receives the shader cycles and 100 MHz ticks of workgroup 0."""
+    _check(load().sage_probe_mfma_i8(blocks, iters, _ptr(clk), _stream(stream)), "sage_probe_mfma_i8")
 
 
 def run(sh: Shape, Q, K, V, dO, stream=None):

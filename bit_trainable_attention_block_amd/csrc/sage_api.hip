@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdint>
 
+#include "../../include/sage_probe.h"
 #include "sage_internal.h"
 
 namespace {
@@ -143,6 +144,11 @@ const char* sage_status_str(int status) {
 }
 
 int sage_last_hip_error(void) { return g_last_hip_error; }
+
+int sage_probe_mfma_i8(int blocks, int iters, unsigned long long* clk, hipStream_t stream) {
+    if (blocks < 1 || iters < 1 || clk == nullptr || !aligned(clk, 8)) return SAGE_EINVAL;
+    return finish(sage::launch_probe_mfma_i8(blocks, iters, clk, stream));
+}
 
 const char* sage_version(void) { return "sage-mi355x 0.1 (gfx950)"; }
 

@@ -29,5 +29,6 @@ hipError_t launch_fwd(const Dims& d, const sage_qtensors& qk, void* O, float* L,
 size_t bwd_workspace_bytes(const Dims& d);
 hipError_t launch_bwd(const Dims& d, const sage_qtensors& qk, const sage_dotensors& dos,
                       const float* L, void* workspace, float* dQ, float* dK, float* dV, hipStream_t s);
+hipError_t launch_probe_mfma_i8(int blocks, int iters, unsigned long long* clk, hipStream_t s);
 
 }  // namespace sage

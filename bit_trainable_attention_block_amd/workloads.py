@@ -81,14 +81,14 @@ SIGMAS = (1.0, 3.0, 5.0, 8.0, 10.0)
 # (4) the sigma sweep; (5) long context with optional Q-smoothing.
 C1 = Config("tiny", 1, 1, 1, 128, 64, FP16, 64, 64, causal=False)
 C2 = Config("d64_n2k", 2, 4, 16, 2048, 64, BF16, 128, 64, causal=False)
-C2_CAUSAL = C2.replace(causal=True)
+C2_CAUSAL = C2.replace(name="d64_n2k_causal", causal=True)
 C3 = Config("d128_n8k_causal_qknorm", 3, 2, 16, 8192, 128, BF16, 128, 64, causal=True,
             qk_norm=True, k_offset_sigma=2.0)
 C4 = tuple(Config(f"sigma{int(s)}_d128_n4k", 4, 1, 32, 4096, 128, BF16, 128, 64, causal=False,
                   sigma=s, variant=vi) for vi, s in enumerate(SIGMAS))
 C5 = Config("long_n32k_causal_qknorm", 5, 1, 8, 32768, 128, BF16, 128, 64, causal=True,
             qk_norm=True, k_offset_sigma=1.0)
-C5_QSMOOTH = C5.replace(q_smooth=True)
+C5_QSMOOTH = C5.replace(name="long_n32k_causal_qknorm_qsmooth", q_smooth=True)
 
 ALL = {c.name: c for c in (C1, C2, C3, C5)}
 

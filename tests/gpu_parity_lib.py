@@ -10,7 +10,7 @@ import torch
 
 from bit_trainable_attention_block_amd import binding as bd
 from bit_trainable_attention_block_amd import workloads as wl
-from oracle import metrics, sage
+from oracle import fpa, metrics, sage
 
 # Floating-point bar for O, dQ, dK, dV against the oracle.
 REL_L2_MAX = 1e-3
@@ -140,6 +140,7 @@ def check_fwd(cfg, inputs, g, b, h, qz, q_blocks, log=None):
     rows = np.concatenate([np.arange(i * cfg.bq, (i + 1) * cfg.bq) for i in q_blocks])
     close(f"O[{b},{h}]", g["O"][b, h][rows], O[rows], log=log)
     np.testing.assert_allclose(g["L"][b, h][rows], L[rows], rtol=2e-5, atol=2e-5)
+    return O
 
 
 def check_bwd(cfg, inputs, g, b, h, qz, kv_blocks, q_blocks, log=None):
@@ -155,6 +156,48 @@ def check_bwd(cfg, inputs, g, b, h, qz, kv_blocks, q_blocks, log=None):
     close(f"dK[{b},{h}]", g["dK"][b, h][kr], dK[kr], log=log)
     close(f"dV[{b},{h}]", g["dV"][b, h][kr], dV[kr], log=log)
     close(f"dQ[{b},{h}]", g["dQ"][b, h][qr], dQ[qr], log=log)
+    return dQ, dK, dV
+
+
+# Heads up to this length get dK, dV against full-precision attention too (the
+# float64 N x N intermediates of a longer head are too large for the check).
+FPA_FULL_MAX_N = 8192
+
+
+def fpa_rows(Q, K, V, dO, scale, causal, rows):
+    """Full-precision O and dQ of the given query rows only (float64; the
+    textbook definitions of oracle/fpa.py restricted to those rows)."""
+    S = (Q[rows] @ K.T) * scale
+    if causal:
+        S = np.where(np.arange(K.shape[0])[None, :] <= rows[:, None], S, -np.inf)
+    m = S.max(axis=1, keepdims=True)
+    E = np.exp(S - m)
+    P = E / E.sum(axis=1, keepdims=True)
+    O = P @ V
+    dP = dO[rows] @ V.T
+    delta = np.sum(dO[rows] * O, axis=1)
+    dQ = scale * ((P * (dP - delta[:, None])) @ K)
+    return O, dQ
+
+
+def report_vs_fpa(cfg, inputs, g, b, h, q_blocks, kv_blocks, ours):
+    """Accuracy against full-precision float64 attention on the sampled rows:
+    the GPU's and the oracle's outputs, each compared with the same reference
+    (recorded, not asserted: SageBwd approximates attention).  `ours` holds
+    the oracle's O, dQ, dK, dV on those rows."""
+    shp = sage.Shape.of(cfg)
+    Q, K, V, dO = (a.astype(np.float64) for a in head_inputs(inputs, b, h))
+    qr = np.concatenate([np.arange(i * cfg.bq, (i + 1) * cfg.bq) for i in q_blocks])
+    kr = np.concatenate([np.arange(j * cfg.bkv, (j + 1) * cfg.bkv) for j in kv_blocks])
+    O_f, dQ_f = fpa_rows(Q, K, V, dO, shp.scale, cfg.causal, qr)
+    pairs = [("O", g["O"][b, h][qr], ours["O"][qr], O_f), ("dQ", g["dQ"][b, h][qr], ours["dQ"][qr], dQ_f)]
+    if cfg.N <= FPA_FULL_MAX_N:
+        r = fpa.backward(Q, K, V, dO, shp.scale, cfg.causal)
+        pairs += [("dK", g["dK"][b, h][kr], ours["dK"][kr], r["dK"][kr]),
+                  ("dV", g["dV"][b, h][kr], ours["dV"][kr], r["dV"][kr])]
+    for name, gpu, orc, ref in pairs:
+        record(f"fpa_gpu_{name}[{b},{h}]", metrics.all_metrics(gpu, ref))
+        record(f"fpa_oracle_{name}[{b},{h}]", metrics.all_metrics(orc, ref))
 
 
 # End-to-end chain bar.  sage_bwd is judged on the O and L it is given (the

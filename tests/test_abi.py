@@ -9,13 +9,18 @@ import pytest
 
 from bit_trainable_attention_block_amd import binding as bd
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "sage.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include")
+HEADER = os.path.join(INCLUDE, "sage.h")
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(sage_[a-z_0-9]+)\s*\(", text)))
+    """Every function any header under include/ declares."""
+    names = set()
+    for f in sorted(os.listdir(INCLUDE)):
+        if f.endswith(".h"):
+            text = re.sub(r"/\*.*?\*/", "", open(os.path.join(INCLUDE, f)).read(), flags=re.S)
+            names |= set(re.findall(r"\b(sage_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -163,3 +168,10 @@ def test_layout_offsets_are_permutations():
         for N, D in ((64, 64), (128, 128), (192, 64)):
             off = bd.layout_offsets(kind, N, D)
             assert np.array_equal(np.sort(off.ravel()), np.arange(N * D)), (kind, N, D)
+
+
+def test_probe_rejects_bad_arguments(lib):
+    buf = (ctypes.c_uint64 * 4)()
+    base = ctypes.addressof(buf)
+    for blocks, iters, ptr in ((0, 1, base), (1, 0, base), (1, 1, None), (1, 1, base + 4)):
+        assert lib.sage_probe_mfma_i8(blocks, iters, ptr, None) == bd.SAGE_EINVAL

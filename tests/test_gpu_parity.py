@@ -101,18 +101,20 @@ def test_full_size_sampled(cfg, heads):
     Tm, Tn = cfg.N // cfg.bq, cfg.N // cfg.bkv
     q_blocks = sorted({0, Tm // 2, Tm - 1})
     kv_blocks = sorted({0, Tn // 3, Tn - 1})
-    for (b, h) in heads:
+    for k, (b, h) in enumerate(heads):
         qz = gp.check_quantize(cfg, x, g, b, h)
-        gp.check_fwd(cfg, x, g, b, h, qz, q_blocks)
-        gp.check_bwd(cfg, x, g, b, h, qz, kv_blocks, q_blocks)
+        O = gp.check_fwd(cfg, x, g, b, h, qz, q_blocks)
+        dQ, dK, dV = gp.check_bwd(cfg, x, g, b, h, qz, kv_blocks, q_blocks)
+        if k == 0:
+            gp.report_vs_fpa(cfg, x, g, b, h, q_blocks, kv_blocks, {"O": O, "dQ": dQ, "dK": dK, "dV": dV})
     # every head: codes of the first Q and K blocks (cheap, bit-exact) and finite outputs
     for k in ("O", "L", "dQ", "dK", "dV"):
         assert np.all(np.isfinite(g[k])), k
 
 
 def test_repeat_is_deterministic():
-    """Two runs on the same inputs: codes, scales, O, L, dK, dV identical; dQ
-    (float atomics) equal up to the order of additions."""
+    """Two runs on the same inputs give identical codes, scales, O, L, dQ, dK
+    and dV (no atomics anywhere: dQ is a separate pass with a fixed order)."""
     cfg = wl.C2_CAUSAL.replace(B=1, H=4)
     x = wl.generate(cfg)
     gp.say("[gpu] determinism")
@@ -120,6 +122,5 @@ def test_repeat_is_deterministic():
     g2 = gp.run_gpu(cfg, x)
     for k in ("q", "k", "vt", "sq", "sk", "sv"):
         np.testing.assert_array_equal(g1["qt"][k], g2["qt"][k])
-    for k in ("O_bits", "L", "dK", "dV"):
+    for k in ("O_bits", "L", "dQ", "dK", "dV"):
         np.testing.assert_array_equal(g1[k], g2[k])
-    np.testing.assert_allclose(g1["dQ"], g2["dQ"], rtol=1e-5, atol=1e-7)
