@@ -50,6 +50,9 @@ Numeric model (the readings taken where the pages leave a choice open)
   tiles whose keys all lie after the block's last query are skipped.
 * delta = rowsum(dO o O) uses the stored (rounded) O.
 * dP = dO V^T uses the 16-bit input values exactly, summed in float64.
+* Ablation switch Shape.dp_int8 (not the method; the SageAttention3 write-up,
+  Table 1c, compares dO V^T in INT8 against FP16): dP = (dO^_i V^_j^T) *
+  s_dO,i * s_V,j from the same per-block codes the other products use.
 
 Quantisation-off mode (quant=False): every quantise/dequantise pair becomes
 the identity (codes = values, scales = 1), nothing is rounded, and the result
@@ -102,6 +105,10 @@ class Shape:
     q_smooth: bool = False
     dtype: int = 1
     sm_scale: Optional[float] = None
+    # Ablation, not the method: dP = dO V^T from the per-block INT8 codes of
+    # dO (bq-row blocks) and V (bkv-row blocks) instead of the 16-bit values
+    # (SageAttention3 write-up, Table 1c compares the two).
+    dp_int8: bool = False
 
     @property
     def scale(self) -> float:
@@ -119,7 +126,8 @@ class Shape:
     def of(cfg) -> "Shape":
         """Build from a workload description (anything with the same fields)."""
         return Shape(N=cfg.N, D=cfg.D, bq=cfg.bq, bkv=cfg.bkv, causal=bool(cfg.causal),
-                     k_smooth=bool(cfg.k_smooth), q_smooth=bool(cfg.q_smooth), dtype=int(cfg.dtype))
+                     k_smooth=bool(cfg.k_smooth), q_smooth=bool(cfg.q_smooth), dtype=int(cfg.dtype),
+                     dp_int8=bool(getattr(cfg, "dp_int8", False)))
 
 
 # ---------------------------------------------------------------------------
@@ -355,8 +363,12 @@ def backward_tile(qz: Quantized, V, dO, dOc, sdO, L, delta, i: int, j: int, sh: 
     # (3) dV_j += M(P^_ij^T, dO^_i) * s_P * s_dO, P quantised per tile
     P_hat, sPb = quantize_block(P, quant)
     dV = (P_hat.T @ dOc[rows]) * (sPb * sdO[i])
-    # (4) dP_ij = dO_i V_j^T from the 16-bit values, no quantisation
-    dP = dO[rows] @ V[keys].T
+    # (4) dP_ij = dO_i V_j^T from the 16-bit values, no quantisation; the
+    # ablation takes it from the INT8 codes of dO_i and V_j with their scales
+    if sh.dp_int8:
+        dP = (dOc[rows] @ qz.Vc[keys].T) * (sdO[i] * qz.sV[j])
+    else:
+        dP = dO[rows] @ V[keys].T
     # (5) dS_ij = P_ij o (dP_ij - D_i), then per-tile INT8 quantisation
     dS = P * (dP - delta[rows][:, None])
     dS_hat, sdS = quantize_block(dS, quant)
