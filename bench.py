@@ -17,6 +17,7 @@ sample (ten whole heads of the same workload).
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -326,6 +327,30 @@ def main():
         "roofline": roofline,
         "breakdown": breakdown,
     }
+    # the INT8-dP ablation (not the method): the same step with dP formed from
+    # the INT8 codes of dO and V; reported beside the headline, never as it
+    sha = dataclasses.replace(sh, dp_int8=True)
+    ab_ms = []
+    for k in range(args.warmup + max(3, args.steps // 4)):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        ev[0].record(stream)
+        bd.quantize(sha, Q, K, V, out=qt)
+        ev[1].record(stream)
+        bd.fwd(sha, qt, O, L)
+        ev[2].record(stream)
+        bd.bwd_pre(sha, O, dO, out=dot)
+        ev[3].record(stream)
+        bd.bwd(sha, qt, dot, L, dQ, dK, dV, ws=bws)
+        ev[4].record(stream)
+        torch.cuda.synchronize()
+        if k >= args.warmup:
+            ab_ms.append([ev[i].elapsed_time(ev[i + 1]) for i in range(4)])
+    ab = np.mean(np.array(ab_ms), axis=0)
+    breakdown["ablation_dp_int8"] = {
+        "call_ms": {c: round(float(v), 4) for c, v in zip(calls, ab)},
+        "bwd_kernel_tops": round(bwd_ops / (ab[3] * 1e-3) / 1e12, 1),
+        "fwd_bwd_tops": round(total_ops / (float(ab.sum()) * 1e-3) / 1e12, 1)}
+
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg)
     print(json.dumps(out), flush=True)

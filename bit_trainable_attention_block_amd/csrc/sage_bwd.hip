@@ -84,30 +84,31 @@ __device__ __forceinline__ void xcd_coords(int units, int BH, int& unit, int& bh
     }
 }
 
-template <int BQ, int D>
+template <int BQ, int D, bool DPI8>
 struct BwdStage {
     int8_t q[BQ * D];     // Q codes, R32
     int8_t dot[BQ * D];   // dO codes, C64P
-    u16 dor[BQ * D];      // dO, R16H
+    int8_t dor[(DPI8 ? 1 : 2) * BQ * D];   // dO, R16H; with dp_int8 dO's codes, R32
     float l2[BQ];         // L * log2 e
     float delta[BQ];
 };
 
 // Asynchronous copy of query tile qbase (Q codes, dO codes, dO) into a stage.
-// The three regions are contiguous BQ*D, BQ*D and 2*BQ*D byte runs; each
-// wave instruction moves 1 KiB, and round u of the eight waves moves the
-// stage's u-th 8 KiB.  When a region is a whole number of rounds (BQ*D a
-// multiple of 8 KiB) the region of a round is known at compile time.
-template <int BQ, int D>
-__device__ __forceinline__ void stage_query_tile(BwdStage<BQ, D>& st, const int8_t* q, const int8_t* dot,
-                                                 const u16* dor, int w, int lane) {
-    constexpr int QB = BQ * D, TOT = 4 * QB, ROUNDS = TOT / (8 * 1024);
-    static_assert(TOT % (8 * 1024) == 0 && QB % 1024 == 0, "stage shape");
-    const int8_t* dorb = reinterpret_cast<const int8_t*>(dor);
-    int8_t* dst_dor = reinterpret_cast<int8_t*>(st.dor);
+// The three regions are contiguous BQ*D, BQ*D and 2*BQ*D byte runs (BQ*D for
+// the third with dp_int8); each wave instruction moves 1 KiB, and round u of
+// the eight waves moves the stage's u-th 8 KiB.  When a region is a whole
+// number of rounds (BQ*D a multiple of 8 KiB) the region of a round is known
+// at compile time.
+template <int BQ, int D, bool DPI8>
+__device__ __forceinline__ void stage_query_tile(BwdStage<BQ, D, DPI8>& st, const int8_t* q, const int8_t* dot,
+                                                 const int8_t* dorb, int w, int lane) {
+    constexpr int QB = BQ * D, TOT = (DPI8 ? 3 : 4) * QB, ROUNDS = (TOT + 8 * 1024 - 1) / (8 * 1024);
+    static_assert(QB % 1024 == 0, "stage shape");
+    int8_t* dst_dor = st.dor;
 #pragma unroll
     for (int u = 0; u < ROUNDS; ++u) {
         const int c0 = u * 8 * 1024 + w * 1024;
+        if (c0 >= TOT) break;   // the last round of a stage that is not a whole number of rounds
         const int8_t* src;
         int8_t* dst;
         if constexpr (QB % (8 * 1024) == 0) {
@@ -140,10 +141,11 @@ __device__ __forceinline__ void stage_query_tile(BwdStage<BQ, D>& st, const int8
 
 // Two LDS stages alternate: tile i is read from stage (i - istart) & 1 while
 // the next tile is copied into the other one.
-template <bool BF16, int D, int BQ, bool CAUSAL, bool QSMOOTH>
+template <bool BF16, int D, int BQ, bool CAUSAL, bool QSMOOTH, bool DPI8>
 __global__ __launch_bounds__(512, 1) void bwd_kernel(
     const int8_t* __restrict__ q, const float* __restrict__ sq, const int8_t* __restrict__ k,
-    const float* __restrict__ sk, const u16* __restrict__ vr, const float* __restrict__ mu_q,
+    const float* __restrict__ sk, const u16* __restrict__ vr, const float* __restrict__ sv,
+    const float* __restrict__ mu_q,
     const float* __restrict__ qk_bias, const float* __restrict__ delta, const int8_t* __restrict__ dot,
     const float* __restrict__ sdo, const u16* __restrict__ dor, const float* __restrict__ L,
     int8_t* __restrict__ dsw, float* __restrict__ sds, float* __restrict__ dK, float* __restrict__ dV, int N,
@@ -154,7 +156,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
     constexpr int KSH = D / 32;   // 16-bit contraction steps over d
     constexpr int DB = D / 16;    // 16-wide blocks of d
     constexpr int CH = BQ / 16;   // 16-byte chunks per dS key row
-    __shared__ __align__(16) BwdStage<BQ, D> st[2];
+    __shared__ __align__(16) BwdStage<BQ, D, DPI8> st[2];
     __shared__ float red[2][2][4];   // [key block][P | dS][key group]
 
     const int Tn = N / 64, Tm = N / BQ;
@@ -173,20 +175,25 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
     // A key block past a ragged end computes on zero operands and stores
     // nothing; keeping it in the same straight-line code as the others
     // avoids merging two paths over the accumulators on every tile.
-    v4i kop[KS8], vop[KSH];
+    // V as the B operand of dP: 16-bit row tiles, or with dp_int8 its codes
+    constexpr int KSV = DPI8 ? KS8 : KSH;
+    v4i kop[KS8], vop[KSV];
 #pragma unroll
     for (int ks = 0; ks < KS8; ++ks) kop[ks] = v4i{0, 0, 0, 0};
 #pragma unroll
-    for (int ks = 0; ks < KSH; ++ks) vop[ks] = v4i{0, 0, 0, 0};
-    float skj = 0.f;
+    for (int ks = 0; ks < KSV; ++ks) vop[ks] = v4i{0, 0, 0, 0};
+    float skj = 0.f, svj = 0.f;
     if (kv_on) {
 #pragma unroll
         for (int ks = 0; ks < KS8; ++ks)
             kop[ks] = *reinterpret_cast<const v4i*>(k + head + off_r32(key, 64 * ks + 16 * g, D));
 #pragma unroll
-        for (int ks = 0; ks < KSH; ++ks)
-            vop[ks] = *reinterpret_cast<const v4i*>(vr + head + off_r16h(key, 32 * ks + 8 * g, D));
+        for (int ks = 0; ks < KSV; ++ks)
+            vop[ks] = DPI8 ? *reinterpret_cast<const v4i*>(reinterpret_cast<const int8_t*>(vr) + head +
+                                                           off_r32(key, 64 * ks + 16 * g, D))
+                           : *reinterpret_cast<const v4i*>(vr + head + off_r16h(key, 32 * ks + 8 * g, D));
         skj = sk[(size_t)bh * Tn + j];
+        if (DPI8) svj = sv[(size_t)bh * Tn + j];
     }
 
     v4f dvt[DB], dkt[DB];
@@ -203,14 +210,15 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
     const float* dlh = delta + (size_t)bh * N;
     const int8_t* qh = q + head;
     const int8_t* doth = dot + head;
-    const u16* dorh = dor + head;
+    constexpr int DOR_B = DPI8 ? 1 : 2;   // bytes per element of the dP operand copy of dO
+    const int8_t* dorh = reinterpret_cast<const int8_t*>(dor) + DOR_B * head;
     // Q-smoothing bias of this lane's key for the current query tile, loaded
     // one tile ahead (a key past a ragged end reads nothing)
     float nbias = 0.f;
     if (QSMOOTH && kv_on) nbias = qk_bias[((size_t)bh * Tm + istart) * N + key];
 
     // One query tile, read from `cur`; the next one is copied into `nxt`.
-    auto step = [&](int i, BwdStage<BQ, D>& cur, BwdStage<BQ, D>& nxt) __attribute__((always_inline)) {
+    auto step = [&](int i, BwdStage<BQ, D, DPI8>& cur, BwdStage<BQ, D, DPI8>& nxt) __attribute__((always_inline)) {
         const int qbase = i * BQ;
         const bool more = i + 1 < Tm;
         const float biasv = nbias;
@@ -223,8 +231,8 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
         }
         if (QSMOOTH && kv_on && more) nbias = qk_bias[((size_t)bh * Tm + i + 1) * N + key];
         if (more)
-            stage_query_tile<BQ, D>(nxt, qh + (size_t)(qbase + BQ) * D, doth + (size_t)(qbase + BQ) * D,
-                                    dorh + (size_t)(qbase + BQ) * D, w, lane);
+            stage_query_tile<BQ, D, DPI8>(nxt, qh + (size_t)(qbase + BQ) * D, doth + (size_t)(qbase + BQ) * D,
+                                          dorh + (size_t)DOR_B * (qbase + BQ) * D, w, lane);
 
         // the tile exists and has a visible key (it is stored for the dQ pass)
         const bool tile_on = kv_on && (!CAUSAL || j * 64 <= qbase + BQ - 1);
@@ -256,12 +264,16 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
             // ---- S and dP for this wave's 16 keys and all BQ queries, one
             // 16-query block ahead of the vector work on the previous block
             v4i s[MB];
-            v4f dp[MB];
+            // dP in float32 from 16-bit operands, or with dp_int8 as an INT8
+            // product with dP = f32(sum) * f32(s_dO * s_V) (one rounding)
+            using DpT = typename std::conditional<DPI8, v4i, v4f>::type;
+            DpT dp[MB];
+            const float cdp = DPI8 ? (float)((double)sdoi * (double)svj) : 0.f;
             // LDS operands of a 16-query block are read one block before its
             // products are issued, so the products never wait on LDS
             struct OpsA {
                 v4i q[KS8];
-                v4i d[KSH];
+                v4i d[KSV];
             };
             OpsA opa[2];
             auto read_block = [&](int mb, OpsA& o) __attribute__((always_inline)) {
@@ -270,15 +282,18 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
                 for (int ks = 0; ks < KS8; ++ks)
                     o.q[ks] = *reinterpret_cast<const v4i*>(cur.q + off_r32(row, 64 * ks + 16 * g, D));
 #pragma unroll
-                for (int ks = 0; ks < KSH; ++ks)
-                    o.d[ks] = *reinterpret_cast<const v4i*>(cur.dor + off_r16h(row, 32 * ks + 8 * g, D));
+                for (int ks = 0; ks < KSV; ++ks)
+                    o.d[ks] = DPI8 ? *reinterpret_cast<const v4i*>(cur.dor + off_r32(row, 64 * ks + 16 * g, D))
+                                   : *reinterpret_cast<const v4i*>(cur.dor + 2 * off_r16h(row, 32 * ks + 8 * g, D));
             };
             auto mfma_block = [&](int mb, const OpsA& o) __attribute__((always_inline)) {
 #pragma unroll
                 for (int ks = 0; ks < KS8; ++ks) s[mb] = mfma16_i8(o.q[ks], kop[ks], ks == 0 ? magic4 : s[mb]);
 #pragma unroll
-                for (int ks = 0; ks < KSH; ++ks)
-                    dp[mb] = mfma16_h<BF16>(o.d[ks], vop[ks], ks == 0 ? v4f{0, 0, 0, 0} : dp[mb]);
+                for (int ks = 0; ks < KSV; ++ks) {
+                    if constexpr (DPI8) dp[mb] = mfma16_i8(o.d[ks], vop[ks], ks == 0 ? magic4 : dp[mb]);
+                    else dp[mb] = mfma16_h<BF16>(o.d[ks], vop[ks], ks == 0 ? v4f{0, 0, 0, 0} : dp[mb]);
+                }
             };
             read_block(0, opa[0]);
             if (MB > 1) read_block(1, opa[1]);
@@ -294,7 +309,10 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
                     float x = fmaf(unmagic(s[mb][r]), c2, -l2[r]);
                     if (QSMOOTH) x += bias2;
                     const float pv = __builtin_amdgcn_exp2f(x);
-                    const float dsv = pv * (dp[mb][r] - dl[r]);
+                    float dpv;
+                    if constexpr (DPI8) dpv = unmagic(dp[mb][r]) * cdp;
+                    else dpv = dp[mb][r];
+                    const float dsv = pv * (dpv - dl[r]);
                     p[mb][r] = pv;
                     ds[mb][r] = dsv;
                     pmax = fmaxf(pmax, pv);
@@ -406,8 +424,8 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
     };
 
     // ---- prologue: first query tile into st0
-    stage_query_tile<BQ, D>(st[0], qh + (size_t)istart * BQ * D, doth + (size_t)istart * BQ * D,
-                            dorh + (size_t)istart * BQ * D, w, lane);
+    stage_query_tile<BQ, D, DPI8>(st[0], qh + (size_t)istart * BQ * D, doth + (size_t)istart * BQ * D,
+                                  dorh + (size_t)DOR_B * istart * BQ * D, w, lane);
     if (tid < BQ) {
         st[0].l2[tid] = (float)((double)Lh[istart * BQ + tid] * kLog2e_d);
         st[0].delta[tid] = dlh[istart * BQ + tid];
@@ -418,7 +436,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
 #pragma unroll
     for (int ks = 0; ks < KS8; ++ks) settle(kop[ks]);
 #pragma unroll
-    for (int ks = 0; ks < KSH; ++ks) settle(vop[ks]);
+    for (int ks = 0; ks < KSV; ++ks) settle(vop[ks]);
     if (QSMOOTH) settle(nbias);
     __syncthreads();
     for (int i = istart; i < Tm; ++i) {
@@ -561,9 +579,12 @@ hipError_t bwd_dispatch(const Dims& d, const BwdPtrs& p, hipStream_t s) {
     const sage_qtensors& qk = *p.qk;
     const sage_dotensors& dos = *p.dos;
     const dim3 grid(((d.Tn() + 1) / 2) * d.BH());
-    auto kern = d.q_smooth ? bwd_kernel<BF16, D, BQ, CAUSAL, true> : bwd_kernel<BF16, D, BQ, CAUSAL, false>;
-    kern<<<grid, 512, 0, s>>>(qk.q, qk.sq, qk.k, qk.sk, qk.vr, qk.mu_q, qk.qk_bias, dos.delta, dos.dot, dos.sdo,
-                              dos.dor, p.L, p.dsw, p.sds, p.dK, p.dV, d.N, d.BH(), d.scale);
+    auto kern = d.dp_int8 ? (d.q_smooth ? bwd_kernel<BF16, D, BQ, CAUSAL, true, true>
+                                        : bwd_kernel<BF16, D, BQ, CAUSAL, false, true>)
+                          : (d.q_smooth ? bwd_kernel<BF16, D, BQ, CAUSAL, true, false>
+                                        : bwd_kernel<BF16, D, BQ, CAUSAL, false, false>);
+    kern<<<grid, 512, 0, s>>>(qk.q, qk.sq, qk.k, qk.sk, qk.vr, qk.sv, qk.mu_q, qk.qk_bias, dos.delta, dos.dot,
+                              dos.sdo, dos.dor, p.L, p.dsw, p.sds, p.dK, p.dV, d.N, d.BH(), d.scale);
     dq_kernel<D, BQ, CAUSAL><<<dim3(d.Tm() * d.BH()), 256, 0, s>>>(p.dsw, p.sds, qk.kt, qk.sk, p.dQ, d.N, d.BH(),
                                                                    d.scale);
     return hipGetLastError();

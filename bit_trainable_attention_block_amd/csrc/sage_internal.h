@@ -13,6 +13,7 @@ namespace sage {
 struct Dims {
     int B, H, N, D, bq, bkv;
     bool bf16, causal, k_smooth, q_smooth;
+    bool dp_int8;  // ablation: dP from the INT8 codes of dO and V
     double scale;  // softmax scale; 1/sqrt(D) in double unless given
     int BH() const { return B * H; }
     int Tm() const { return N / bq; }

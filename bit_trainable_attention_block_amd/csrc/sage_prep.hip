@@ -165,14 +165,15 @@ __global__ void zero_f64_kernel(double* p, int n) {
     if (i < n) p[i] = 0.0;
 }
 
-// V blocks (64 rows): codes -> vt (C64P), scale -> sv, raw copy -> vr (R16H).
+// V blocks (64 rows): codes -> vt (C64P), scale -> sv, raw copy -> vr (R16H);
+// with dp_int8 the codes again, as R32 row tiles, -> vr instead of the copy.
 // K blocks (same rows): float64 column sums accumulated into ws[bh][D]
 // (exact: sums of 16-bit values fit float64 without rounding, so the order of
 // the atomic additions does not change the result).
 template <bool BF16, int D>
 __global__ __launch_bounds__(kThreads) void quant_v_ksum_kernel(
     const u16* __restrict__ K, const u16* __restrict__ V, int N, int8_t* __restrict__ vt,
-    float* __restrict__ sv, u16* __restrict__ vr, double* __restrict__ ws, int k_smooth) {
+    float* __restrict__ sv, u16* __restrict__ vr, double* __restrict__ ws, int k_smooth, int dp_int8) {
     constexpr int R = 64;
     using B = Blk<R, D>;
     __shared__ float red[4];
@@ -193,13 +194,14 @@ __global__ __launch_bounds__(kThreads) void quant_v_ksum_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[k][e]));
     }
-    store_r16h<R, D>(raw, vr + head, row0);
+    if (!dp_int8) store_r16h<R, D>(raw, vr + head, row0);
     const float a = block_max(m, red);
     const float s = __fdiv_rn(a, 127.f);
     codes_to_lds<R, D>(x, s, codes);
     if (threadIdx.x == 0) sv[(size_t)bh * (N / R) + j] = s;
     __syncthreads();
     store_codes<C64P, R, D>(codes, vt + head + (size_t)row0 * D);
+    if (dp_int8) store_codes<R32, R, D>(codes, reinterpret_cast<int8_t*>(vr) + head + (size_t)row0 * D);
 
     if (k_smooth) {
         load_block<R, D>(K + head + (size_t)row0 * D, raw);
@@ -345,14 +347,15 @@ __global__ __launch_bounds__(kThreads) void quant_k_kernel(
 }
 
 // Backward pre-pass on one BQ-row block: delta = rowsum(dO o O) (float64,
-// rounded once), dO codes -> dot (C64P), scale -> sdo, raw dO -> dor (R16H).
+// rounded once), dO codes -> dot (C64P), scale -> sdo, raw dO -> dor (R16H);
+// with dp_int8 the codes again, as R32 row tiles, -> dor instead of the copy.
 template <bool BF16, int D, int BQ>
 __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const u16* __restrict__ O,
                                                            const u16* __restrict__ dO, int N,
                                                            float* __restrict__ delta,
                                                            int8_t* __restrict__ dot,
                                                            float* __restrict__ sdo,
-                                                           u16* __restrict__ dor) {
+                                                           u16* __restrict__ dor, int dp_int8) {
     using B = Blk<BQ, D>;
     __shared__ float red[4];
     __shared__ __align__(16) uint8_t codes[BQ * D];
@@ -366,7 +369,7 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const u16* __restrict
     float x[B::PER_T][8];
     load_block<BQ, D>(dO + head + (size_t)row0 * D, raw);
     load_block<BQ, D>(O + head + (size_t)row0 * D, rawo);
-    store_r16h<BQ, D>(raw, dor + head, row0);
+    if (!dp_int8) store_r16h<BQ, D>(raw, dor + head, row0);
     float m = 0.f;
 #pragma unroll
     for (int k = 0; k < B::PER_T; ++k) {
@@ -389,6 +392,7 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const u16* __restrict
     if (threadIdx.x == 0) sdo[(size_t)bh * Tm + i] = s;
     __syncthreads();
     store_codes<C64P, BQ, D>(codes, dot + head + (size_t)row0 * D);
+    if (dp_int8) store_codes<R32, BQ, D>(codes, reinterpret_cast<int8_t*>(dor) + head + (size_t)row0 * D);
 }
 
 template <bool BF16, int D>
@@ -401,7 +405,7 @@ hipError_t quantize_impl(const Dims& d, const void* Q, const void* K, const void
         zero_f64_kernel<<<(n + 255) / 256, 256, 0, s>>>(ws, n);
     }
     quant_v_ksum_kernel<BF16, D><<<dim3(d.Tn(), BH), blk, 0, s>>>(
-        (const u16*)K, (const u16*)V, d.N, out.vt, out.sv, out.vr, ws, d.k_smooth ? 1 : 0);
+        (const u16*)K, (const u16*)V, d.N, out.vt, out.sv, out.vr, ws, d.k_smooth ? 1 : 0, d.dp_int8 ? 1 : 0);
     if (d.bq == 128)
         quant_q_kernel<BF16, D, 128><<<dim3(d.Tm(), BH), blk, 0, s>>>((const u16*)Q, d.N, out.q, out.qt,
                                                                       out.sq, d.q_smooth ? out.mu_q : nullptr);
@@ -420,10 +424,12 @@ hipError_t bwd_pre_impl(const Dims& d, const void* O, const void* dO, const sage
     dim3 grid(d.Tm(), d.BH());
     if (d.bq == 128)
         bwd_pre_kernel<BF16, D, 128><<<grid, kThreads, 0, s>>>((const u16*)O, (const u16*)dO, d.N,
-                                                               out.delta, out.dot, out.sdo, out.dor);
+                                                               out.delta, out.dot, out.sdo, out.dor,
+                                                               d.dp_int8 ? 1 : 0);
     else
         bwd_pre_kernel<BF16, D, 64><<<grid, kThreads, 0, s>>>((const u16*)O, (const u16*)dO, d.N,
-                                                              out.delta, out.dot, out.sdo, out.dor);
+                                                              out.delta, out.dot, out.sdo, out.dor,
+                                                              d.dp_int8 ? 1 : 0);
     return hipGetLastError();
 }
 

@@ -54,6 +54,7 @@ class Config:
     variant: int = 0      # sigma index (sigma sweep) or 0
     qk_norm: bool = False
     k_offset_sigma: float = 0.0
+    dp_int8: bool = False # ablation: dP from INT8 codes (the method keeps it 16-bit)
 
     @property
     def sm_scale(self) -> float:
@@ -89,6 +90,8 @@ C4 = tuple(Config(f"sigma{int(s)}_d128_n4k", 4, 1, 32, 4096, 128, BF16, 128, 64,
 C5 = Config("long_n32k_causal_qknorm", 5, 1, 8, 32768, 128, BF16, 128, 64, causal=True,
             qk_norm=True, k_offset_sigma=1.0)
 C5_QSMOOTH = C5.replace(name="long_n32k_causal_qknorm_qsmooth", q_smooth=True)
+# the d=128 N=8K workload with the INT8-dP ablation (not the method)
+C3_DPINT8 = C3.replace(name="d128_n8k_causal_qknorm_dpint8", dp_int8=True)
 
 ALL = {c.name: c for c in (C1, C2, C3, C5)}
 

@@ -75,6 +75,15 @@ typedef struct sage_shape {
     int32_t k_smooth;   /* 1 = subtract the per-head token mean of K */
     int32_t q_smooth;   /* 1 = subtract the mean of each Q block */
     float sm_scale;     /* softmax scale; 0 selects 1/sqrt(D) */
+    int32_t dp_int8;    /* 0 = the method: dP = dO V^T from the 16-bit values.
+                           1 = ablation (SageAttention3 write-up, Table 1c
+                           compares it with FP16): dP from the per-block INT8
+                           codes of dO and V, dP = f32(dO^ V^^T) * f32(s_dO * s_V).
+                           Then sage_quantize stores V's codes (R32, N*D bytes
+                           per head, heads consecutive) at the start of `vr`,
+                           sage_bwd_pre stores dO's codes (R32, likewise) at
+                           the start of `dor`, and sage_bwd reads them; the
+                           three calls must agree on it. */
 } sage_shape;
 /* Supported: D in {64, 128}; bq in {64, 128}; bkv = 64; N a multiple of bq
  * and of bkv (the pages define T_m = N / B_q blocks; a ragged block is

@@ -97,8 +97,13 @@ def check_quantize(cfg, inputs, g, b, h):
     np.testing.assert_array_equal(qt["sq"][b, h], qz.sQ.astype(np.float32))
     np.testing.assert_array_equal(qt["sk"][b, h], qz.sK.astype(np.float32))
     np.testing.assert_array_equal(qt["sv"][b, h], qz.sV.astype(np.float32))
-    vr = bd.unpack_codes(qt["vr"][b, h].view(np.uint16), "R16H", N, D)
-    np.testing.assert_array_equal(vr, inputs["v"]["bits"][b, h])
+    if cfg.dp_int8:
+        # V's codes, R32, heads consecutive at the start of the buffer
+        v8 = qt["vr"].reshape(-1).view(np.int8)[: cfg.B * cfg.H * N * D].reshape(cfg.B, cfg.H, N * D)
+        np.testing.assert_array_equal(bd.unpack_codes(v8[b, h], "R32", N, D), qz.Vc.astype(np.int8))
+    else:
+        vr = bd.unpack_codes(qt["vr"][b, h].view(np.uint16), "R16H", N, D)
+        np.testing.assert_array_equal(vr, inputs["v"]["bits"][b, h])
     if cfg.k_smooth:
         np.testing.assert_array_equal(qt["mu_k"][b, h], qz.mu_k.astype(np.float32))
     if cfg.q_smooth:
@@ -119,8 +124,12 @@ def check_bwd_pre(cfg, inputs, g, b, h):
     np.testing.assert_array_equal(bd.unpack_codes(dot["dot"][b, h], "C64P", cfg.N, cfg.D), dOc.astype(np.int8))
     np.testing.assert_array_equal(dot["sdo"][b, h], sdO.astype(np.float32))
     np.testing.assert_allclose(dot["delta"][b, h], delta, rtol=1e-6, atol=1e-6)
-    np.testing.assert_array_equal(bd.unpack_codes(dot["dor"][b, h].view(np.uint16), "R16H", cfg.N, cfg.D),
-                                  inputs["do"]["bits"][b, h])
+    if cfg.dp_int8:
+        d8 = dot["dor"].reshape(-1).view(np.int8)[: cfg.B * cfg.H * cfg.N * cfg.D].reshape(cfg.B, cfg.H, -1)
+        np.testing.assert_array_equal(bd.unpack_codes(d8[b, h], "R32", cfg.N, cfg.D), dOc.astype(np.int8))
+    else:
+        np.testing.assert_array_equal(bd.unpack_codes(dot["dor"][b, h].view(np.uint16), "R16H", cfg.N, cfg.D),
+                                      inputs["do"]["bits"][b, h])
     return delta, dOc, sdO
 
 

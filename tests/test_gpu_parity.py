@@ -41,6 +41,11 @@ SMALL = [
     small("n256_d64_fp16_causal", 256, 64, 128, True, dtype=wl.FP16),
     small("n256_d128_qsmooth", 256, 128, 128, False, q_smooth=True, sigma=3.0),
     small("n512_d128_causal_b2", 512, 128, 128, True, B=2, H=1),
+    # the INT8-dP ablation: ragged, bq=64 with d=64, Q-smoothing, fp16
+    small("n192_d64_bq64_causal_dpint8", 192, 64, 64, True).replace(dp_int8=True),
+    small("n384_d128_dpint8", 384, 128, 128, False).replace(dp_int8=True),
+    small("n320_d128_bq64_causal_qsmooth_dpint8", 320, 128, 64, True, q_smooth=True).replace(dp_int8=True),
+    small("n256_d64_fp16_dpint8", 256, 64, 128, False, dtype=wl.FP16).replace(dp_int8=True),
 ]
 
 
@@ -88,6 +93,7 @@ FULL = [
     (wl.C4[4], [(0, 31)]),
     (wl.C5, [(0, 0), (0, 7)]),
     (wl.C5_QSMOOTH, [(0, 5)]),
+    (wl.C3_DPINT8, [(1, 3)]),
 ]
 
 
