@@ -50,6 +50,10 @@ Numeric model (the readings taken where the pages leave a choice open)
   tiles whose keys all lie after the block's last query are skipped.
 * delta = rowsum(dO o O) uses the stored (rounded) O.
 * dP = dO V^T uses the 16-bit input values exactly, summed in float64.
+* Ablation switch Shape.p_static (not the method; the SageAttention3 write-up
+  names the static per-block scale 1/127 beside Eq. 8 as less accurate):
+  the forward's P codes use s_P = 1/127 and P^ = P~ / s_P, P~ taken against
+  the running maximum.
 * Ablation switch Shape.dp_int8 (not the method; the SageAttention3 write-up,
   Table 1c, compares dO V^T in INT8 against FP16): dP = (dO^_i V^_j^T) *
   s_dO,i * s_V,j from the same per-block codes the other products use.
@@ -109,6 +113,10 @@ class Shape:
     # dO (bq-row blocks) and V (bkv-row blocks) instead of the 16-bit values
     # (SageAttention3 write-up, Table 1c compares the two).
     dp_int8: bool = False
+    # Ablation, not the method: the forward's P codes with the static scale
+    # s_P = 1/127 against the running maximum, P^ = P~ / s_P (the alternative
+    # the SageAttention3 write-up names beside Eq. 8 and finds less accurate)
+    p_static: bool = False
 
     @property
     def scale(self) -> float:
@@ -127,7 +135,7 @@ class Shape:
         """Build from a workload description (anything with the same fields)."""
         return Shape(N=cfg.N, D=cfg.D, bq=cfg.bq, bkv=cfg.bkv, causal=bool(cfg.causal),
                      k_smooth=bool(cfg.k_smooth), q_smooth=bool(cfg.q_smooth), dtype=int(cfg.dtype),
-                     dp_int8=bool(getattr(cfg, "dp_int8", False)))
+                     dp_int8=bool(getattr(cfg, "dp_int8", False)), p_static=bool(getattr(cfg, "p_static", False)))
 
 
 # ---------------------------------------------------------------------------
@@ -260,6 +268,20 @@ def per_token_p_quant(P_tilde, rm, m_new, quant=True):
     return sP.astype(F64), codes
 
 
+def static_p_quant(P_tilde, rm, quant=True):
+    """The static alternative to Eq. 8: s_P = 1/127 for every row with a
+    visible key, P^ = P~ / s_P rounded to integers in [0, 127] (P~ is taken
+    against the running maximum, so it lies in [0, 1])."""
+    if not quant:
+        return np.ones(P_tilde.shape[0]), P_tilde.copy()
+    sP = np.where(np.isneginf(rm), F32(0), F32(1) / F32(127)).astype(F32)
+    codes = np.zeros_like(P_tilde)
+    live = sP > 0
+    p32 = P_tilde[live].astype(F32)
+    codes[live] = np.clip(np.rint(p32 / sP[live][:, None]), 0, 127)
+    return sP.astype(F64), codes
+
+
 # ---------------------------------------------------------------------------
 # Forward (forward steps (3)-(5); SA3 Eq. 1 and Eq. 8)
 # ---------------------------------------------------------------------------
@@ -285,7 +307,10 @@ def forward(qz: Quantized, sh: Shape, quant=True, q_blocks: Optional[Iterable[in
             rm = S.max(axis=1)
             m_new = np.maximum(m, rm)
             P_tilde = _exp_shift(S, m_new)
-            sP, P_hat = per_token_p_quant(P_tilde, rm, m_new, quant)
+            if sh.p_static:
+                sP, P_hat = static_p_quant(P_tilde, rm, quant)
+            else:
+                sP, P_hat = per_token_p_quant(P_tilde, rm, m_new, quant)
             with np.errstate(invalid="ignore"):
                 alpha = np.where(np.isneginf(m), 0.0, np.exp(m - m_new))
             l = alpha * l + P_tilde.sum(axis=1)
