@@ -31,7 +31,7 @@ class c_shape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32), ("D", ctypes.c_int32),
                 ("bq", ctypes.c_int32), ("bkv", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("causal", ctypes.c_int32), ("k_smooth", ctypes.c_int32), ("q_smooth", ctypes.c_int32),
-                ("sm_scale", ctypes.c_float), ("dp_int8", ctypes.c_int32)]
+                ("sm_scale", ctypes.c_float), ("dp_int8", ctypes.c_int32), ("p_static", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -104,16 +104,18 @@ class Shape:
     q_smooth: bool = False
     sm_scale: float = 0.0
     dp_int8: bool = False   # ablation: dP from INT8 codes (see include/sage.h)
+    p_static: bool = False  # ablation: static forward P scale 1/127 (see include/sage.h)
 
     @staticmethod
     def of(cfg) -> "Shape":
         return Shape(B=cfg.B, H=cfg.H, N=cfg.N, D=cfg.D, bq=cfg.bq, bkv=cfg.bkv, dtype=cfg.dtype,
                      causal=bool(cfg.causal), k_smooth=bool(cfg.k_smooth), q_smooth=bool(cfg.q_smooth),
-                     dp_int8=bool(getattr(cfg, "dp_int8", False)))
+                     dp_int8=bool(getattr(cfg, "dp_int8", False)), p_static=bool(getattr(cfg, "p_static", False)))
 
     def c(self) -> c_shape:
         return c_shape(self.B, self.H, self.N, self.D, self.bq, self.bkv, self.dtype, int(self.causal),
-                       int(self.k_smooth), int(self.q_smooth), float(self.sm_scale), int(self.dp_int8))
+                       int(self.k_smooth), int(self.q_smooth), float(self.sm_scale), int(self.dp_int8),
+                       int(self.p_static))
 
     @property
     def torch_dtype(self):

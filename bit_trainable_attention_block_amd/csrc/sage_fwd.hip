@@ -92,7 +92,7 @@ struct FwdStage {
 // and a row with no visible key in the tile keeps a finite maximum.
 constexpr int kMaskedSum = kMagicBits - (1 << 22) + 1;
 
-template <bool BF16, int D, bool CAUSAL, bool QSMOOTH>
+template <bool BF16, int D, bool CAUSAL, bool QSMOOTH, bool PSTATIC>
 __global__ __launch_bounds__(64 * kWaves, 2) void fwd_kernel(
     const int8_t* __restrict__ q, const float* __restrict__ sq, const int8_t* __restrict__ k,
     const float* __restrict__ sk, const int8_t* __restrict__ vt, const float* __restrict__ sv,
@@ -247,7 +247,9 @@ __global__ __launch_bounds__(64 * kWaves, 2) void fwd_kernel(
                         }
                     rm = unmagic(qmax4i(im)) * c2;
                 }
-                const float shift = rm - kLog2_127;
+                // codes against the tile maximum (per token), or with the
+                // static scale against the exact running maximum
+                const float shift = (PSTATIC ? fmaxf(m, rm) : rm) - kLog2_127;
                 sum = 0.f;
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) {
@@ -276,8 +278,9 @@ __global__ __launch_bounds__(64 * kWaves, 2) void fwd_kernel(
             // more than 2^8, so the rescale below is rare.  The codes
             // 127 * 2^(x - rm) do not depend on it, only l and O's common
             // factor do, and those use it consistently.
-            const float m_new = (rm > m + kLazy) ? rm : m;
-            const float sP = __fdiv_rn(__builtin_amdgcn_exp2f(rm - m_new), 127.f);
+            // (static scale: the exact running maximum, s_P = 1/127)
+            const float m_new = PSTATIC ? fmaxf(m, rm) : ((rm > m + kLazy) ? rm : m);
+            const float sP = PSTATIC ? __fdiv_rn(1.f, 127.f) : __fdiv_rn(__builtin_amdgcn_exp2f(rm - m_new), 127.f);
             if (__builtin_expect(__any(m_new != m), 0)) {
                 // rare: a row's reference maximum moved; rescale l and O
                 const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 0 on the first tile
@@ -324,13 +327,17 @@ hipError_t fwd_dispatch(const Dims& d, const FwdArgs& a, hipStream_t s) {
     const dim3 grid(((d.N + kQTile - 1) / kQTile) * d.BH());
     const dim3 block(64 * kWaves);
 #define SAGE_FWD_ARGS a.q, a.sq, a.k, a.sk, a.vt, a.sv, a.qk_bias, a.O, a.L, a.N, a.bq, a.scale2
+#define SAGE_FWD(C, QS)                                                                     \
+    (d.p_static ? fwd_kernel<BF16, D, C, QS, true><<<grid, block, 0, s>>>(SAGE_FWD_ARGS)   \
+                : fwd_kernel<BF16, D, C, QS, false><<<grid, block, 0, s>>>(SAGE_FWD_ARGS))
     if (d.causal) {
-        if (d.q_smooth) fwd_kernel<BF16, D, true, true><<<grid, block, 0, s>>>(SAGE_FWD_ARGS);
-        else fwd_kernel<BF16, D, true, false><<<grid, block, 0, s>>>(SAGE_FWD_ARGS);
+        if (d.q_smooth) SAGE_FWD(true, true);
+        else SAGE_FWD(true, false);
     } else {
-        if (d.q_smooth) fwd_kernel<BF16, D, false, true><<<grid, block, 0, s>>>(SAGE_FWD_ARGS);
-        else fwd_kernel<BF16, D, false, false><<<grid, block, 0, s>>>(SAGE_FWD_ARGS);
+        if (d.q_smooth) SAGE_FWD(false, true);
+        else SAGE_FWD(false, false);
     }
+#undef SAGE_FWD
 #undef SAGE_FWD_ARGS
     return hipGetLastError();
 }

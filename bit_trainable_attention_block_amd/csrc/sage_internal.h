@@ -14,6 +14,7 @@ struct Dims {
     int B, H, N, D, bq, bkv;
     bool bf16, causal, k_smooth, q_smooth;
     bool dp_int8;  // ablation: dP from the INT8 codes of dO and V
+    bool p_static; // ablation: static forward P scale 1/127
     double scale;  // softmax scale; 1/sqrt(D) in double unless given
     int BH() const { return B * H; }
     int Tm() const { return N / bq; }

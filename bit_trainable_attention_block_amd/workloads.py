@@ -55,6 +55,7 @@ class Config:
     qk_norm: bool = False
     k_offset_sigma: float = 0.0
     dp_int8: bool = False # ablation: dP from INT8 codes (the method keeps it 16-bit)
+    p_static: bool = False  # ablation: static forward P scale 1/127 (the method: per token)
 
     @property
     def sm_scale(self) -> float:
@@ -92,6 +93,8 @@ C5 = Config("long_n32k_causal_qknorm", 5, 1, 8, 32768, 128, BF16, 128, 64, causa
 C5_QSMOOTH = C5.replace(name="long_n32k_causal_qknorm_qsmooth", q_smooth=True)
 # the d=128 N=8K workload with the INT8-dP ablation (not the method)
 C3_DPINT8 = C3.replace(name="d128_n8k_causal_qknorm_dpint8", dp_int8=True)
+# ... and with the static forward P scale (not the method)
+C3_PSTATIC = C3.replace(name="d128_n8k_causal_qknorm_pstatic", p_static=True)
 
 ALL = {c.name: c for c in (C1, C2, C3, C5)}
 

@@ -84,6 +84,11 @@ typedef struct sage_shape {
                            sage_bwd_pre stores dO's codes (R32, likewise) at
                            the start of `dor`, and sage_bwd reads them; the
                            three calls must agree on it. */
+    int32_t p_static;   /* 0 = the method: the forward's P codes per token,
+                           s_P = exp(rowmax(S_ij) - m_ij) / 127 (Eq. 8).
+                           1 = ablation (the SageAttention3 write-up names it
+                           beside Eq. 8 as less accurate): the static scale
+                           s_P = 1/127 against the running maximum. */
 } sage_shape;
 /* Supported: D in {64, 128}; bq in {64, 128}; bkv = 64; N a multiple of bq
  * and of bkv (the pages define T_m = N / B_q blocks; a ragged block is

@@ -39,14 +39,14 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_struct_layouts_match_header():
-    assert ctypes.sizeof(bd.c_shape) == 12 * 4
+    assert ctypes.sizeof(bd.c_shape) == 13 * 4
     assert ctypes.sizeof(bd.c_qtensors) == 12 * 8
     assert ctypes.sizeof(bd.c_dotensors) == 4 * 8
 
 
 def _shape(**kw):
     base = dict(B=1, H=2, N=256, D=128, bq=128, bkv=64, dtype=1, causal=0, k_smooth=1, q_smooth=0, sm_scale=0.0,
-                dp_int8=0)
+                dp_int8=0, p_static=0)
     base.update(kw)
     return bd.c_shape(**base)
 
@@ -78,6 +78,7 @@ BAD_SHAPES = [
     (dict(B=-1), bd.SAGE_EINVAL),
     (dict(causal=2), bd.SAGE_EINVAL),
     (dict(dp_int8=2), bd.SAGE_EINVAL),
+    (dict(p_static=-1), bd.SAGE_EINVAL),
     (dict(sm_scale=-1.0), bd.SAGE_EINVAL),
     (dict(sm_scale=float("nan")), bd.SAGE_EINVAL),
     (dict(B=70000, H=1), bd.SAGE_EUNSUPPORTED),

@@ -46,6 +46,9 @@ SMALL = [
     small("n384_d128_dpint8", 384, 128, 128, False).replace(dp_int8=True),
     small("n320_d128_bq64_causal_qsmooth_dpint8", 320, 128, 64, True, q_smooth=True).replace(dp_int8=True),
     small("n256_d64_fp16_dpint8", 256, 64, 128, False, dtype=wl.FP16).replace(dp_int8=True),
+    # the static-P ablation
+    small("n320_d128_bq64_causal_pstatic", 320, 128, 64, True).replace(p_static=True),
+    small("n256_d64_qsmooth_pstatic", 256, 64, 128, False, q_smooth=True, sigma=2.0).replace(p_static=True),
 ]
 
 
@@ -94,6 +97,7 @@ FULL = [
     (wl.C5, [(0, 0), (0, 7)]),
     (wl.C5_QSMOOTH, [(0, 5)]),
     (wl.C3_DPINT8, [(1, 3)]),
+    (wl.C3_PSTATIC, [(0, 9)]),
 ]
 
 
