@@ -31,7 +31,7 @@ import numpy as np
 FP16 = 0
 BF16 = 1
 
-TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "do": 3, "koff": 4}
+TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "do": 3, "koff": 4, "qoff": 5}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -54,6 +54,7 @@ class Config:
     variant: int = 0      # sigma index (sigma sweep) or 0
     qk_norm: bool = False
     k_offset_sigma: float = 0.0
+    q_offset_sigma: float = 0.0  # per-(b,h,channel) offset of Q, shared by all tokens
     dp_int8: bool = False # ablation: dP from INT8 codes (the method keeps it 16-bit)
     p_static: bool = False  # ablation: static forward P scale 1/127 (the method: per token)
 
@@ -149,6 +150,9 @@ def generate(cfg: Config, heads: Optional[Tuple[int, int]] = None) -> Dict[str, 
         if name == "k" and cfg.k_offset_sigma:
             off = _rng(cfg, "koff").standard_normal((cfg.B, cfg.H, 1, cfg.D), dtype=np.float32)
             x = (x + off * np.float32(cfg.k_offset_sigma)).astype(np.float32)
+        if name == "q" and cfg.q_offset_sigma:
+            off = _rng(cfg, "qoff").standard_normal((cfg.B, cfg.H, 1, cfg.D), dtype=np.float32)
+            x = (x + off * np.float32(cfg.q_offset_sigma)).astype(np.float32)
         if heads is not None:
             b, h = heads
             x = x[b:b + 1, h:h + 1]

@@ -122,6 +122,26 @@ def test_full_size_sampled(cfg, heads):
         assert np.all(np.isfinite(g[k])), k
 
 
+@pytest.mark.parametrize("ks,qs", [(False, False), (True, False), (True, True)], ids=["none", "k", "qk"])
+def test_smoothing_variants_on_offset_heads(ks, qs):
+    """The three smoothing settings on one head whose Q and K carry channel
+    offsets shared by all tokens: parity with the oracle on every block, and
+    both sides' accuracy against full-precision attention recorded (the
+    report prints them side by side)."""
+    name = {(False, False): "smoothing_none", (True, False): "smoothing_k", (True, True): "smoothing_qk"}[(ks, qs)]
+    cfg = wl.Config(name, 11, 1, 1, 1024, 128, wl.BF16, 128, 64, causal=False, k_smooth=ks, q_smooth=qs,
+                    k_offset_sigma=4.0, q_offset_sigma=3.0)
+    gp.say(f"[gpu] smoothing variant {name}")
+    gp.CURRENT_CASE[0] = name
+    x = wl.generate(cfg)
+    g = gp.run_gpu(cfg, x)
+    allq, allk = list(range(cfg.N // cfg.bq)), list(range(cfg.N // cfg.bkv))
+    qz = gp.check_quantize(cfg, x, g, 0, 0)
+    O = gp.check_fwd(cfg, x, g, 0, 0, qz, allq)
+    dQ, dK, dV = gp.check_bwd(cfg, x, g, 0, 0, qz, allk, allq)
+    gp.report_vs_fpa(cfg, x, g, 0, 0, allq, allk, {"O": O, "dQ": dQ, "dK": dK, "dV": dV})
+
+
 def test_repeat_is_deterministic():
     """Two runs on the same inputs give identical codes, scales, O, L, dQ, dK
     and dV (no atomics anywhere: dQ is a separate pass with a fixed order)."""
