@@ -1,0 +1,61 @@
+"""A training-step wrapper over the four C-ABI calls: SageBwd attention as a
+torch.autograd.Function (SageBwd paper summary, "method step details":
+forward steps (1)-(5), backward steps (1)-(7)).
+
+    O = sage_attention(Q, K, V, causal=True)     # Q, K, V: [B, H, N, D] bf16/fp16 on the GPU
+    O.backward(dO)                               # Q.grad, K.grad, V.grad in the input dtype
+
+Forward: sage_quantize then sage_fwd; the INT8 codes, scales and means, O and
+the logsumexp L are kept for the backward (about 3 bytes per element plus
+the 16-bit copy of V: the backward recomputes S and P from the codes, it
+does not keep them).  Backward: sage_bwd_pre on the incoming dO, then
+sage_bwd.  The library computes every step; this module only allocates the
+buffers, passes pointers and the current stream, and casts the float32
+gradients to the input dtype.  Without libsage.so the calls raise.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import binding as bd
+
+
+class SageAttentionFunction(torch.autograd.Function):
+    """autograd.Function over sage_quantize / sage_fwd / sage_bwd_pre / sage_bwd."""
+
+    @staticmethod
+    def forward(ctx, Q, K, V, causal: bool, k_smooth: bool, q_smooth: bool, sm_scale: float, bq: int):
+        if not (Q.is_cuda and K.is_cuda and V.is_cuda):
+            raise ValueError("sage_attention: Q, K, V must be GPU tensors")
+        if Q.dtype not in (torch.bfloat16, torch.float16) or K.dtype != Q.dtype or V.dtype != Q.dtype:
+            raise ValueError("sage_attention: Q, K, V must share one dtype, bf16 or fp16")
+        if Q.dim() != 4 or K.shape != Q.shape or V.shape != Q.shape:
+            raise ValueError("sage_attention: Q, K, V must be [B, H, N, D] of one shape")
+        B, H, N, D = Q.shape
+        sh = bd.Shape(B=B, H=H, N=N, D=D, bq=bq, bkv=64,
+                      dtype=bd.SAGE_BF16 if Q.dtype == torch.bfloat16 else bd.SAGE_FP16,
+                      causal=bool(causal), k_smooth=bool(k_smooth), q_smooth=bool(q_smooth),
+                      sm_scale=float(sm_scale))
+        Q, K, V = Q.contiguous(), K.contiguous(), V.contiguous()
+        qt = bd.quantize(sh, Q, K, V)
+        O, L = bd.fwd(sh, qt)
+        ctx.sh = sh
+        ctx.qt = qt          # codes, scales and means (and the 16-bit copy of V)
+        ctx.save_for_backward(O, L)
+        return O
+
+    @staticmethod
+    def backward(ctx, dO):
+        O, L = ctx.saved_tensors
+        sh = ctx.sh
+        dO = dO.to(O.dtype).contiguous()
+        dot = bd.bwd_pre(sh, O, dO)
+        dQ, dK, dV = bd.bwd(sh, ctx.qt, dot, L)
+        ctx.qt = None
+        return dQ.to(O.dtype), dK.to(O.dtype), dV.to(O.dtype), None, None, None, None, None
+
+
+def sage_attention(Q, K, V, causal: bool = False, k_smooth: bool = True, q_smooth: bool = False,
+                   sm_scale: float = 0.0, bq: int = 128):
+    """SageBwd INT8 attention with gradients (sm_scale 0 selects 1/sqrt(D))."""
+    return SageAttentionFunction.apply(Q, K, V, causal, k_smooth, q_smooth, sm_scale, bq)

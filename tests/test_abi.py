@@ -178,3 +178,14 @@ def test_probe_rejects_bad_arguments(lib):
     base = ctypes.addressof(buf)
     for blocks, iters, ptr in ((0, 1, base), (1, 0, base), (1, 1, None), (1, 1, base + 4)):
         assert lib.sage_probe_mfma_i8(blocks, iters, ptr, None) == bd.SAGE_EINVAL
+
+
+def test_autograd_wrapper_rejects_cpu_tensors():
+    """The training wrapper is argument marshalling only: on CPU tensors it
+    raises before touching the library (there is no CPU fallback)."""
+    import torch
+
+    from bit_trainable_attention_block_amd.autograd import sage_attention
+    x = torch.zeros((1, 1, 64, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        sage_attention(x, x, x)

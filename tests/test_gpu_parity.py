@@ -142,6 +142,42 @@ def test_smoothing_variants_on_offset_heads(ks, qs):
     gp.report_vs_fpa(cfg, x, g, 0, 0, allq, allk, {"O": O, "dQ": dQ, "dK": dK, "dV": dV})
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_autograd_wrapper_matches_the_oracle(causal):
+    """sage_attention (a torch.autograd.Function over the four calls): O and
+    the gradients it returns through autograd against the oracle's chain, and
+    identical to calling the four entry points directly."""
+    import torch
+
+    from bit_trainable_attention_block_amd.autograd import sage_attention
+    from oracle import sage as osage
+    cfg = small("autograd", 256, 128, 128, causal, H=2)
+    gp.say(f"[gpu] autograd wrapper causal={causal}")
+    gp.CURRENT_CASE[0] = f"autograd_causal{int(causal)}"
+    x = wl.generate(cfg)
+    dev = gp.to_device(x)
+    Q, K, V, dO = (dev[n].view(torch.bfloat16).clone() for n in ("q", "k", "v", "do"))
+    for t in (Q, K, V):
+        t.requires_grad_(True)
+    O = sage_attention(Q, K, V, causal=causal)
+    O.backward(dO)
+    torch.cuda.synchronize()
+    direct = gp.run_gpu(cfg, x)
+    np.testing.assert_array_equal(O.detach().view(torch.int16).cpu().numpy().view(np.uint16), direct["O_bits"])
+    for name, t in (("dQ", Q), ("dK", K), ("dV", V)):
+        ref16 = torch.from_numpy(direct[name]).to(torch.bfloat16)
+        np.testing.assert_array_equal(t.grad.cpu().view(torch.int16).numpy(), ref16.view(torch.int16).numpy())
+    shp = osage.Shape.of(cfg)
+    for h in range(cfg.H):
+        r = osage.run_head(*gp.head_inputs(x, 0, h), shp)
+        gp.close(f"O[0,{h}]", O.detach()[0, h].float().cpu().numpy(), r["O"], rel_max=gp.CHAIN_REL_L2_MAX)
+        for name, t in (("dQ", Q), ("dK", K), ("dV", V)):
+            # bf16 gradients: the 16-bit rounding (2^-9 relative) bounds the
+            # difference on top of the float32 chain bar
+            gp.close(f"{name}[0,{h}]", t.grad[0, h].float().cpu().numpy(), r[name], rel_max=gp.CHAIN_REL_L2_MAX,
+                     cos_min=0.9999)
+
+
 def test_repeat_is_deterministic():
     """Two runs on the same inputs give identical codes, scales, O, L, dQ, dK
     and dV (no atomics anywhere: dQ is a separate pass with a fixed order)."""
