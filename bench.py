@@ -142,7 +142,9 @@ def cpu_baseline(cfg, heads=CPU_HEADS):
     ops = per_head_ops * len(heads)
     return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": 1, "kind": "oracle",
             "sample": f"{len(heads)} of {cfg.B * cfg.H} heads of the same workload, whole chain "
-                      f"(quantize, fwd, bwd_pre, bwd), {dt:.1f} s on 1 host core"}
+                      f"(quantize, fwd, bwd_pre, bwd), {dt:.1f} s on 1 host core",
+            "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "blas_threads": 1}
 
 
 def mfma_probe(iters=4000):
@@ -275,6 +277,7 @@ def main():
         for i, c in enumerate(calls):
             per_call[c].append(ev[i].elapsed_time(ev[i + 1]))
     call_ms = {c: float(np.mean(v)) for c, v in per_call.items()}
+    step_ms = np.array([ev[0].elapsed_time(ev[4]) for ev in events])
     ms_per_step = wall * 1e3 / args.steps
     fwd_ops, bwd_ops = cfg.attention_ops()
     total_ops = fwd_ops + bwd_ops
@@ -295,6 +298,8 @@ def main():
     bwd_path_ms = call_ms["sage_bwd_pre"] + call_ms["sage_bwd"]
     breakdown = {
         "call_ms": {c: round(v, 4) for c, v in call_ms.items()},
+        "call_ms_min": {c: round(float(np.min(v)), 4) for c, v in per_call.items()},
+        "step_ms_median": round(float(np.median(step_ms)), 4), "step_ms_min": round(float(np.min(step_ms)), 4),
         "fwd_kernel_tops": round(fwd_ops / (call_ms["sage_fwd"] * 1e-3) / 1e12, 1),
         "bwd_kernel_tops": round(bwd_tops, 1),
         "fwd_path_tops": round(fwd_ops / (fwd_path_ms * 1e-3) / 1e12, 1),
