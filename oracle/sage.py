@@ -50,6 +50,11 @@ Numeric model (the readings taken where the pages leave a choice open)
   tiles whose keys all lie after the block's last query are skipped.
 * delta = rowsum(dO o O) uses the stored (rounded) O.
 * dP = dO V^T uses the 16-bit input values exactly, summed in float64.
+* QK-norm fused into the preprocessing (Shape.qk_norm, for training use; the
+  SageBwd paper summary trains with QK-norm, prerequisites "QK-norm"): rows
+  of Q and K are scaled by r = f32(1/sqrt(mean(x^2) + 1e-6)) (mean exact in
+  float64) and rounded to float32 before smoothing and quantisation; the
+  gradients w.r.t. the inputs are r * (dX_n - X_n * mean(dX_n o X_n)).
 * Ablation switch Shape.p_static (not the method; the SageAttention3 write-up
   names the static per-block scale 1/127 beside Eq. 8 as less accurate):
   the forward's P codes use s_P = 1/127 and P^ = P~ / s_P, P~ taken against
@@ -117,6 +122,10 @@ class Shape:
     # s_P = 1/127 against the running maximum, P^ = P~ / s_P (the alternative
     # the SageAttention3 write-up names beside Eq. 8 and finds less accurate)
     p_static: bool = False
+    # QK-norm fused into the preprocessing (training use): per-token RMS
+    # normalisation of Q and K with unit gain before smoothing and
+    # quantisation; the gradients then pass back through it
+    qk_norm: bool = False
 
     @property
     def scale(self) -> float:
@@ -135,7 +144,8 @@ class Shape:
         """Build from a workload description (anything with the same fields)."""
         return Shape(N=cfg.N, D=cfg.D, bq=cfg.bq, bkv=cfg.bkv, causal=bool(cfg.causal),
                      k_smooth=bool(cfg.k_smooth), q_smooth=bool(cfg.q_smooth), dtype=int(cfg.dtype),
-                     dp_int8=bool(getattr(cfg, "dp_int8", False)), p_static=bool(getattr(cfg, "p_static", False)))
+                     dp_int8=bool(getattr(cfg, "dp_int8", False)), p_static=bool(getattr(cfg, "p_static", False)),
+                     qk_norm=bool(getattr(cfg, "qk_norm_fused", False)))
 
 
 # ---------------------------------------------------------------------------
@@ -172,14 +182,50 @@ class Quantized:
     mu_k: np.ndarray    # [D]  (zeros when K-smoothing is off)
     mu_q: np.ndarray    # [Tm, D] (zeros when Q-smoothing is off)
     K_sm: np.ndarray    # [N, D] smoothed, unquantised K (for the Q-smoothing bias)
+    rq: Optional[np.ndarray] = None   # [N] inverse RMS of each Q row (QK-norm), else None
+    rk: Optional[np.ndarray] = None   # [N] the same for K
+
+
+QK_NORM_EPS = 1e-6
+
+
+def rms_norm(X, quant=True):
+    """QK-norm (SageBwd paper summary, prerequisites "QK-norm"; unit gain):
+    per row r = 1 / sqrt(mean(x^2) + eps) and X_n = X * r.  The mean is exact
+    in float64; with quantisation on, r is rounded once to float32 and X_n
+    rounded to float32 (the values the codes are taken from)."""
+    X = np.asarray(X, dtype=F64)
+    ms = np.sum(X * X, axis=1) / X.shape[1]
+    r = 1.0 / np.sqrt(ms + QK_NORM_EPS)
+    if quant:
+        r = r32(r)
+        return r32(X * r[:, None]), r
+    return X * r[:, None], r
+
+
+def rms_norm_backward(X, r, dXn, quant=True):
+    """Gradient through X_n = X * r(X) for rows X, given dL/dX_n:
+    dL/dX = r * (dX_n - X_n * mean(dX_n o X_n)) (the derivative of
+    (mean(x^2) + eps)^(-1/2) is -r^3 x / D)."""
+    X, dXn = np.asarray(X, dtype=F64), np.asarray(dXn, dtype=F64)
+    Xn = X * r[:, None]
+    if quant:
+        Xn = r32(Xn)
+    c = np.sum(dXn * Xn, axis=1) / X.shape[1]
+    return r[:, None] * (dXn - Xn * c[:, None])
 
 
 def quantize(Q, K, V, sh: Shape, quant=True) -> Quantized:
     """Forward steps (1)-(2): smoothing, then per-block quantisation of
-    Q (bq-row blocks), K and V (bkv-row blocks)."""
+    Q (bq-row blocks), K and V (bkv-row blocks); with QK-norm the rows of Q
+    and K are normalised first."""
     Q, K, V = (np.asarray(a, dtype=F64) for a in (Q, K, V))
     N, D = Q.shape
     rnd = r32 if quant else (lambda x: np.asarray(x, dtype=F64))
+    rq = rk = None
+    if sh.qk_norm:
+        Q, rq = rms_norm(Q, quant)
+        K, rk = rms_norm(K, quant)
 
     # K-smoothing: subtract the mean over all N tokens of the head.
     if sh.k_smooth:
@@ -208,7 +254,7 @@ def quantize(Q, K, V, sh: Shape, quant=True) -> Quantized:
         rows = slice(j * sh.bkv, (j + 1) * sh.bkv)
         Kc[rows], sK[j] = quantize_block(K_sm[rows], quant)
         Vc[rows], sV[j] = quantize_block(V[rows], quant)
-    return Quantized(Qc, sQ, Kc, sK, Vc, sV, mu_k, mu_q, K_sm)
+    return Quantized(Qc, sQ, Kc, sK, Vc, sV, mu_k, mu_q, K_sm, rq, rk)
 
 
 # ---------------------------------------------------------------------------
@@ -447,8 +493,12 @@ def run_head(Q, K, V, dO, sh: Shape, quant=True) -> Dict[str, np.ndarray]:
     O, L = forward(qz, sh, quant)
     delta, dOc, sdO = backward_pre(O, dO, sh, quant)
     dQ, dK, dV = backward(qz, V, dO, dOc, sdO, L, delta, sh, quant)
-    return {"qz": qz, "O": O, "L": L, "delta": delta, "dOc": dOc, "sdO": sdO,
-            "dQ": dQ, "dK": dK, "dV": dV}
+    out = {"qz": qz, "O": O, "L": L, "delta": delta, "dOc": dOc, "sdO": sdO, "dQ": dQ, "dK": dK, "dV": dV}
+    if sh.qk_norm:
+        # dQ, dK above are w.r.t. the normalised rows; these are w.r.t. the inputs
+        out["dQ_in"] = rms_norm_backward(Q, qz.rq, dQ, quant)
+        out["dK_in"] = rms_norm_backward(K, qz.rk, dK, quant)
+    return out
 
 
 def run(inputs: Dict[str, np.ndarray], sh: Shape, quant=True) -> Dict[str, np.ndarray]:
