@@ -24,7 +24,8 @@ class SageAttentionFunction(torch.autograd.Function):
     """autograd.Function over sage_quantize / sage_fwd / sage_bwd_pre / sage_bwd."""
 
     @staticmethod
-    def forward(ctx, Q, K, V, causal: bool, k_smooth: bool, q_smooth: bool, sm_scale: float, bq: int):
+    def forward(ctx, Q, K, V, causal: bool, k_smooth: bool, q_smooth: bool, sm_scale: float, bq: int,
+                qk_norm: bool):
         if not (Q.is_cuda and K.is_cuda and V.is_cuda):
             raise ValueError("sage_attention: Q, K, V must be GPU tensors")
         if Q.dtype not in (torch.bfloat16, torch.float16) or K.dtype != Q.dtype or V.dtype != Q.dtype:
@@ -35,27 +36,35 @@ class SageAttentionFunction(torch.autograd.Function):
         sh = bd.Shape(B=B, H=H, N=N, D=D, bq=bq, bkv=64,
                       dtype=bd.SAGE_BF16 if Q.dtype == torch.bfloat16 else bd.SAGE_FP16,
                       causal=bool(causal), k_smooth=bool(k_smooth), q_smooth=bool(q_smooth),
-                      sm_scale=float(sm_scale))
+                      sm_scale=float(sm_scale), qk_norm=bool(qk_norm))
         Q, K, V = Q.contiguous(), K.contiguous(), V.contiguous()
         qt = bd.quantize(sh, Q, K, V)
         O, L = bd.fwd(sh, qt)
         ctx.sh = sh
         ctx.qt = qt          # codes, scales and means (and the 16-bit copy of V)
-        ctx.save_for_backward(O, L)
+        if qk_norm:
+            ctx.save_for_backward(O, L, Q, K)   # the norm's gradient needs the input rows
+        else:
+            ctx.save_for_backward(O, L)
         return O
 
     @staticmethod
     def backward(ctx, dO):
-        O, L = ctx.saved_tensors
+        O, L = ctx.saved_tensors[:2]
         sh = ctx.sh
         dO = dO.to(O.dtype).contiguous()
         dot = bd.bwd_pre(sh, O, dO)
         dQ, dK, dV = bd.bwd(sh, ctx.qt, dot, L)
+        if sh.qk_norm:
+            Q, K = ctx.saved_tensors[2:]
+            bd.qk_norm_bwd(sh, Q, K, ctx.qt, dQ, dK)
         ctx.qt = None
-        return dQ.to(O.dtype), dK.to(O.dtype), dV.to(O.dtype), None, None, None, None, None
+        return dQ.to(O.dtype), dK.to(O.dtype), dV.to(O.dtype), None, None, None, None, None, None
 
 
 def sage_attention(Q, K, V, causal: bool = False, k_smooth: bool = True, q_smooth: bool = False,
-                   sm_scale: float = 0.0, bq: int = 128):
-    """SageBwd INT8 attention with gradients (sm_scale 0 selects 1/sqrt(D))."""
-    return SageAttentionFunction.apply(Q, K, V, causal, k_smooth, q_smooth, sm_scale, bq)
+                   sm_scale: float = 0.0, bq: int = 128, qk_norm: bool = False):
+    """SageBwd INT8 attention with gradients (sm_scale 0 selects 1/sqrt(D)).
+    qk_norm=True applies QK-norm (unit gain) to Q and K inside sage_quantize
+    and returns gradients w.r.t. the un-normalised inputs."""
+    return SageAttentionFunction.apply(Q, K, V, causal, k_smooth, q_smooth, sm_scale, bq, qk_norm)

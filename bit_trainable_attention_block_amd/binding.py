@@ -31,11 +31,12 @@ class c_shape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32), ("D", ctypes.c_int32),
                 ("bq", ctypes.c_int32), ("bkv", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("causal", ctypes.c_int32), ("k_smooth", ctypes.c_int32), ("q_smooth", ctypes.c_int32),
-                ("sm_scale", ctypes.c_float), ("dp_int8", ctypes.c_int32), ("p_static", ctypes.c_int32)]
+                ("sm_scale", ctypes.c_float), ("dp_int8", ctypes.c_int32), ("p_static", ctypes.c_int32),
+                ("qk_norm", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
-QT_FIELDS = ("q", "qt", "sq", "k", "kt", "sk", "vt", "sv", "vr", "mu_k", "mu_q", "qk_bias")
+QT_FIELDS = ("q", "qt", "sq", "k", "kt", "sk", "vt", "sv", "vr", "mu_k", "mu_q", "qk_bias", "rq", "rk")
 DO_FIELDS = ("delta", "dot", "sdo", "dor")
 
 
@@ -59,6 +60,7 @@ SIGNATURES = {
     "sage_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "sage_last_hip_error": (ctypes.c_int, []),
     "sage_version": (ctypes.c_char_p, []),
+    "sage_qk_norm_bwd": (ctypes.c_int, [ctypes.POINTER(c_shape), _P, _P, ctypes.POINTER(c_qtensors), _P, _P, _P]),
     # include/sage_probe.h (measurement aid)
     "sage_probe_mfma_i8": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _P, _P]),
 }
@@ -105,17 +107,19 @@ class Shape:
     sm_scale: float = 0.0
     dp_int8: bool = False   # ablation: dP from INT8 codes (see include/sage.h)
     p_static: bool = False  # ablation: static forward P scale 1/127 (see include/sage.h)
+    qk_norm: bool = False   # QK-norm fused into sage_quantize (see include/sage.h)
 
     @staticmethod
     def of(cfg) -> "Shape":
         return Shape(B=cfg.B, H=cfg.H, N=cfg.N, D=cfg.D, bq=cfg.bq, bkv=cfg.bkv, dtype=cfg.dtype,
                      causal=bool(cfg.causal), k_smooth=bool(cfg.k_smooth), q_smooth=bool(cfg.q_smooth),
-                     dp_int8=bool(getattr(cfg, "dp_int8", False)), p_static=bool(getattr(cfg, "p_static", False)))
+                     dp_int8=bool(getattr(cfg, "dp_int8", False)), p_static=bool(getattr(cfg, "p_static", False)),
+                     qk_norm=bool(getattr(cfg, "qk_norm_fused", False)))
 
     def c(self) -> c_shape:
         return c_shape(self.B, self.H, self.N, self.D, self.bq, self.bkv, self.dtype, int(self.causal),
                        int(self.k_smooth), int(self.q_smooth), float(self.sm_scale), int(self.dp_int8),
-                       int(self.p_static))
+                       int(self.p_static), int(self.qk_norm))
 
     @property
     def torch_dtype(self):
@@ -160,6 +164,8 @@ def alloc_qtensors(sh: Shape, device="cuda") -> Dict[str, torch.Tensor]:
         "mu_k": torch.zeros((B, H, D), **f32),
         "mu_q": torch.empty((B, H, sh.Tm, D), **f32) if sh.q_smooth else None,
         "qk_bias": torch.empty((B, H, sh.Tm, N), **f32) if sh.q_smooth else None,
+        "rq": torch.empty((B, H, N), **f32) if sh.qk_norm else None,
+        "rk": torch.empty((B, H, N), **f32) if sh.qk_norm else None,
         "ws": torch.empty((max(1, B * H * D),), dtype=torch.float64, device=device),
     }
     return t
@@ -231,6 +237,14 @@ def bwd(sh: Shape, qt, dot, L, dQ=None, dK=None, dV=None, ws=None, stream=None):
     return dQ, dK, dV
 
 
+def qk_norm_bwd(sh: Shape, Q, K, qt, dQ, dK, stream=None):
+    """In place: dQ, dK w.r.t. the QK-normed rows -> w.r.t. the inputs Q, K."""
+    cs = sh.c()
+    _check(load().sage_qk_norm_bwd(ctypes.byref(cs), _ptr(Q), _ptr(K), ctypes.byref(_qstruct(qt)), _ptr(dQ),
+                                   _ptr(dK), _stream(stream)), "sage_qk_norm_bwd")
+    return dQ, dK
+
+
 def probe_mfma_i8(blocks: int, iters: int, clk: torch.Tensor, stream=None):
     """Measurement aid (include/sage_probe.h): `blocks` workgroups of 8 waves,
     each wave issuing iters x 8 INT8 16x16x64 products; clk (3 int64 on the
@@ -244,7 +258,11 @@ def run(sh: Shape, Q, K, V, dO, stream=None):
     O, L = fwd(sh, qt, stream=stream)
     dot = bwd_pre(sh, O, dO, stream=stream)
     dQ, dK, dV = bwd(sh, qt, dot, L, stream=stream)
-    return {"qt": qt, "O": O, "L": L, "dot": dot, "dQ": dQ, "dK": dK, "dV": dV}
+    out = {"qt": qt, "O": O, "L": L, "dot": dot, "dQ": dQ, "dK": dK, "dV": dV}
+    if sh.qk_norm:
+        # dQ, dK above are w.r.t. the normalised rows; these w.r.t. Q and K
+        out["dQ_in"], out["dK_in"] = qk_norm_bwd(sh, Q, K, qt, dQ.clone(), dK.clone(), stream=stream)
+    return out
 
 
 # ----------------------------------------------------------------- layouts

@@ -18,7 +18,8 @@ int check_shape(const sage_shape* s, sage::Dims& d) {
     if (s == nullptr) return SAGE_EINVAL;
     if (s->B < 0 || s->H < 0 || s->N < 0) return SAGE_EINVAL;
     if (s->causal < 0 || s->causal > 1 || s->k_smooth < 0 || s->k_smooth > 1 || s->q_smooth < 0 ||
-        s->q_smooth > 1 || s->dp_int8 < 0 || s->dp_int8 > 1 || s->p_static < 0 || s->p_static > 1)
+        s->q_smooth > 1 || s->dp_int8 < 0 || s->dp_int8 > 1 || s->p_static < 0 || s->p_static > 1 ||
+        s->qk_norm < 0 || s->qk_norm > 1)
         return SAGE_EINVAL;
     if (!(s->sm_scale >= 0.f) || !std::isfinite(s->sm_scale)) return SAGE_EINVAL;
     if (s->D != 64 && s->D != 128) return SAGE_EUNSUPPORTED;
@@ -36,6 +37,7 @@ int check_shape(const sage_shape* s, sage::Dims& d) {
     d.q_smooth = s->q_smooth != 0;
     d.dp_int8 = s->dp_int8 != 0;
     d.p_static = s->p_static != 0;
+    d.qk_norm = s->qk_norm != 0;
     d.scale = s->sm_scale > 0.f ? (double)s->sm_scale : 1.0 / std::sqrt((double)s->D);
     return SAGE_OK;
 }
@@ -56,6 +58,7 @@ int check_qtensors(const sage::Dims& d, const sage_qtensors* t) {
     if (!ptrs_ok(t->q, t->qt, t->sq, t->k, t->kt, t->sk, t->vt, t->sv, t->vr)) return SAGE_EINVAL;
     if (d.k_smooth && !ptrs_ok(t->mu_k)) return SAGE_EINVAL;
     if (d.q_smooth && !ptrs_ok(t->mu_q, t->qk_bias)) return SAGE_EINVAL;
+    if (d.qk_norm && !ptrs_ok(t->rq, t->rk)) return SAGE_EINVAL;
     return SAGE_OK;
 }
 
@@ -133,6 +136,17 @@ int sage_bwd(const sage_shape* shape, const sage_qtensors* qk, const sage_dotens
     if ((st = check_dotensors(dos)) != SAGE_OK) return st;
     if (!ptrs_ok(L, workspace, dQ, dK, dV)) return SAGE_EINVAL;
     return finish(sage::launch_bwd(d, *qk, *dos, L, workspace, dQ, dK, dV, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int sage_qk_norm_bwd(const sage_shape* shape, const void* Q, const void* K, const sage_qtensors* qk, float* dQ,
+                     float* dK, sage_stream_t stream) {
+    sage::Dims d;
+    int st = check_shape(shape, d);
+    if (st != SAGE_OK) return st;
+    if (!d.qk_norm || qk == nullptr) return SAGE_EINVAL;
+    if (empty(d)) return SAGE_OK;
+    if (!ptrs_ok(Q, K, qk->rq, qk->rk, dQ, dK)) return SAGE_EINVAL;
+    return finish(sage::launch_qk_norm_bwd(d, Q, K, qk->rq, qk->rk, dQ, dK, reinterpret_cast<hipStream_t>(stream)));
 }
 
 const char* sage_status_str(int status) {

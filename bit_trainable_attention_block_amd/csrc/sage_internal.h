@@ -15,6 +15,7 @@ struct Dims {
     bool bf16, causal, k_smooth, q_smooth;
     bool dp_int8;  // ablation: dP from the INT8 codes of dO and V
     bool p_static; // ablation: static forward P scale 1/127
+    bool qk_norm;  // QK-norm fused into the preprocessing
     double scale;  // softmax scale; 1/sqrt(D) in double unless given
     int BH() const { return B * H; }
     int Tm() const { return N / bq; }
@@ -31,6 +32,8 @@ hipError_t launch_fwd(const Dims& d, const sage_qtensors& qk, void* O, float* L,
 size_t bwd_workspace_bytes(const Dims& d);
 hipError_t launch_bwd(const Dims& d, const sage_qtensors& qk, const sage_dotensors& dos,
                       const float* L, void* workspace, float* dQ, float* dK, float* dV, hipStream_t s);
+hipError_t launch_qk_norm_bwd(const Dims& d, const void* Q, const void* K, const float* rq, const float* rk,
+                              float* dQ, float* dK, hipStream_t s);
 hipError_t launch_probe_mfma_i8(int blocks, int iters, unsigned long long* clk, hipStream_t s);
 
 }  // namespace sage

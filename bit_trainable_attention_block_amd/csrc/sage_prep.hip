@@ -81,6 +81,35 @@ __device__ __forceinline__ void block_colsum(const double (&part)[8], double* re
     __syncthreads();
 }
 
+// QK-norm of the block's rows in place (unit gain): per row
+//   r = f32(1 / sqrt(mean(x^2) + eps))    (sum of squares exact in float64,
+//                                          then IEEE double sqrt and divide)
+//   x = f32(x * r)                         (one rounding; no contraction)
+// The CPR threads of a row are consecutive lanes, so the row sum is a lane
+// reduction.  r of each row goes to rout[row0 + row] when rout is set.
+constexpr double kQkNormEps = 1e-6;
+
+template <int R, int D>
+using BlockVals = float[Blk<R, D>::PER_T][8];
+
+template <int R, int D>
+__device__ __forceinline__ void rms_normalize(BlockVals<R, D>& x, float* __restrict__ rout, int row0) {
+    using B = Blk<R, D>;
+    const int t = threadIdx.x;
+    const int cc = t % B::CPR;
+#pragma unroll
+    for (int k = 0; k < B::PER_T; ++k) {
+        double ss = 0.0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += (double)x[k][e] * (double)x[k][e];
+        ss = wave_sum_d(ss, B::CPR);
+        const float r = (float)__ddiv_rn(1.0, __dsqrt_rn(ss / (double)D + kQkNormEps));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[k][e] = __fmul_rn(x[k][e], r);
+        if (rout != nullptr && cc == 0) rout[row0 + t / B::CPR + k * B::RSTEP] = r;
+    }
+}
+
 // Quantise x (values of the block held per thread) with scale s and store
 // the codes row-major into LDS codes[R][D].
 template <int R, int D>
@@ -173,7 +202,8 @@ __global__ void zero_f64_kernel(double* p, int n) {
 template <bool BF16, int D>
 __global__ __launch_bounds__(kThreads) void quant_v_ksum_kernel(
     const u16* __restrict__ K, const u16* __restrict__ V, int N, int8_t* __restrict__ vt,
-    float* __restrict__ sv, u16* __restrict__ vr, double* __restrict__ ws, int k_smooth, int dp_int8) {
+    float* __restrict__ sv, u16* __restrict__ vr, double* __restrict__ ws, int k_smooth, int dp_int8,
+    int qk_norm) {
     constexpr int R = 64;
     using B = Blk<R, D>;
     __shared__ float red[4];
@@ -205,14 +235,15 @@ __global__ __launch_bounds__(kThreads) void quant_v_ksum_kernel(
 
     if (k_smooth) {
         load_block<R, D>(K + head + (size_t)row0 * D, raw);
+        float y[B::PER_T][8];
+#pragma unroll
+        for (int k = 0; k < B::PER_T; ++k) unpack8<BF16>(raw[k], y[k]);
+        if (qk_norm) rms_normalize<R, D>(y, nullptr, row0);   // the mean of the normalised rows
         double part[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-        for (int k = 0; k < B::PER_T; ++k) {
-            float y[8];
-            unpack8<BF16>(raw[k], y);
+        for (int k = 0; k < B::PER_T; ++k)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) part[e] += (double)y[e];
-        }
+            for (int e = 0; e < 8; ++e) part[e] += (double)y[k][e];
         block_colsum<R, D>(part, dred, dsum);
         if (threadIdx.x < D) atomicAdd(ws + (size_t)bh * D + threadIdx.x, dsum[threadIdx.x]);
     }
@@ -224,7 +255,8 @@ __global__ __launch_bounds__(kThreads) void quant_q_kernel(const u16* __restrict
                                                            int8_t* __restrict__ q,
                                                            int8_t* __restrict__ qt,
                                                            float* __restrict__ sq,
-                                                           float* __restrict__ mu_q) {
+                                                           float* __restrict__ mu_q,
+                                                           float* __restrict__ rq) {
     using B = Blk<BQ, D>;
     __shared__ float red[4];
     __shared__ __align__(16) uint8_t codes[BQ * D];
@@ -241,6 +273,7 @@ __global__ __launch_bounds__(kThreads) void quant_q_kernel(const u16* __restrict
     load_block<BQ, D>(Q + head + (size_t)row0 * D, raw);
 #pragma unroll
     for (int k = 0; k < B::PER_T; ++k) unpack8<BF16>(raw[k], x[k]);
+    if (rq != nullptr) rms_normalize<BQ, D>(x, rq + (size_t)bh * N, row0);
 
     if (mu_q != nullptr) {
         double part[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -283,7 +316,7 @@ template <bool BF16, int D>
 __global__ __launch_bounds__(kThreads) void quant_k_kernel(
     const u16* __restrict__ K, int N, int8_t* __restrict__ k, int8_t* __restrict__ kt,
     float* __restrict__ sk, float* __restrict__ mu_k, const double* __restrict__ ws, int k_smooth,
-    const float* __restrict__ mu_q, float* __restrict__ qk_bias, int Tm, double scale) {
+    const float* __restrict__ mu_q, float* __restrict__ qk_bias, int Tm, double scale, float* __restrict__ rk) {
     constexpr int R = 64;
     using B = Blk<R, D>;
     __shared__ float red[4];
@@ -308,10 +341,12 @@ __global__ __launch_bounds__(kThreads) void quant_k_kernel(
     float x[B::PER_T][8];
     load_block<R, D>(K + head + (size_t)row0 * D, raw);
     const int cc = threadIdx.x % B::CPR;
+#pragma unroll
+    for (int kk = 0; kk < B::PER_T; ++kk) unpack8<BF16>(raw[kk], x[kk]);
+    if (rk != nullptr) rms_normalize<R, D>(x, rk + (size_t)bh * N, row0);
     float m = 0.f;
 #pragma unroll
     for (int kk = 0; kk < B::PER_T; ++kk) {
-        unpack8<BF16>(raw[kk], x[kk]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             if (k_smooth) x[kk][e] = __fsub_rn(x[kk][e], mu[cc * 8 + e]);
@@ -395,6 +430,45 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const u16* __restrict
     if (dp_int8) store_codes<R32, BQ, D>(codes, reinterpret_cast<int8_t*>(dor) + head + (size_t)row0 * D);
 }
 
+// Gradient through QK-norm, in place on one 64-row block of one head:
+//   x_n = f32(x * r) (as the forward formed it), c = mean(dX_n o x_n)
+//   (float64), dX = r * (dX_n - x_n * c).
+template <bool BF16, int D>
+__global__ __launch_bounds__(kThreads) void qk_norm_bwd_kernel(const u16* __restrict__ X, const float* __restrict__ r,
+                                                               float* __restrict__ dX, int N) {
+    constexpr int R = 64;
+    using B = Blk<R, D>;
+    const int j = blockIdx.x, bh = blockIdx.y;
+    const size_t head = (size_t)bh * N * D;
+    const int row0 = j * R;
+    const int t = threadIdx.x, cc = t % B::CPR;
+    v4i raw[B::PER_T];
+    load_block<R, D>(X + head + (size_t)row0 * D, raw);
+#pragma unroll
+    for (int k = 0; k < B::PER_T; ++k) {
+        const int row = row0 + t / B::CPR + k * B::RSTEP;
+        float x[8];
+        unpack8<BF16>(raw[k], x);
+        const float rr = r[(size_t)bh * N + row];
+        float* g = dX + head + (size_t)row * D + cc * 8;
+        const v4f g0 = *reinterpret_cast<const v4f*>(g), g1 = *reinterpret_cast<const v4f*>(g + 4);
+        const float gv[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+        float xn[8];
+        double c = 0.0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            xn[e] = __fmul_rn(x[e], rr);
+            c += (double)gv[e] * (double)xn[e];
+        }
+        c = wave_sum_d(c, B::CPR) / (double)D;
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = (float)((double)rr * ((double)gv[e] - (double)xn[e] * c));
+        *reinterpret_cast<v4f*>(g) = v4f{o[0], o[1], o[2], o[3]};
+        *reinterpret_cast<v4f*>(g + 4) = v4f{o[4], o[5], o[6], o[7]};
+    }
+}
+
 template <bool BF16, int D>
 hipError_t quantize_impl(const Dims& d, const void* Q, const void* K, const void* V,
                          const sage_qtensors& out, double* ws, hipStream_t s) {
@@ -405,16 +479,20 @@ hipError_t quantize_impl(const Dims& d, const void* Q, const void* K, const void
         zero_f64_kernel<<<(n + 255) / 256, 256, 0, s>>>(ws, n);
     }
     quant_v_ksum_kernel<BF16, D><<<dim3(d.Tn(), BH), blk, 0, s>>>(
-        (const u16*)K, (const u16*)V, d.N, out.vt, out.sv, out.vr, ws, d.k_smooth ? 1 : 0, d.dp_int8 ? 1 : 0);
+        (const u16*)K, (const u16*)V, d.N, out.vt, out.sv, out.vr, ws, d.k_smooth ? 1 : 0, d.dp_int8 ? 1 : 0,
+        d.qk_norm ? 1 : 0);
     if (d.bq == 128)
         quant_q_kernel<BF16, D, 128><<<dim3(d.Tm(), BH), blk, 0, s>>>((const u16*)Q, d.N, out.q, out.qt,
-                                                                      out.sq, d.q_smooth ? out.mu_q : nullptr);
+                                                                      out.sq, d.q_smooth ? out.mu_q : nullptr,
+                                                                      d.qk_norm ? out.rq : nullptr);
     else
         quant_q_kernel<BF16, D, 64><<<dim3(d.Tm(), BH), blk, 0, s>>>((const u16*)Q, d.N, out.q, out.qt,
-                                                                     out.sq, d.q_smooth ? out.mu_q : nullptr);
+                                                                     out.sq, d.q_smooth ? out.mu_q : nullptr,
+                                                                     d.qk_norm ? out.rq : nullptr);
     quant_k_kernel<BF16, D><<<dim3(d.Tn(), BH), blk, 0, s>>>(
         (const u16*)K, d.N, out.k, out.kt, out.sk, out.mu_k, ws, d.k_smooth ? 1 : 0,
-        d.q_smooth ? out.mu_q : nullptr, d.q_smooth ? out.qk_bias : nullptr, d.Tm(), d.scale);
+        d.q_smooth ? out.mu_q : nullptr, d.q_smooth ? out.qk_bias : nullptr, d.Tm(), d.scale,
+        d.qk_norm ? out.rk : nullptr);
     return hipGetLastError();
 }
 
@@ -433,7 +511,25 @@ hipError_t bwd_pre_impl(const Dims& d, const void* O, const void* dO, const sage
     return hipGetLastError();
 }
 
+template <bool BF16, int D>
+hipError_t qk_norm_bwd_impl(const Dims& d, const void* Q, const void* K, const float* rq, const float* rk,
+                            float* dQ, float* dK, hipStream_t s) {
+    const dim3 grid(d.N / 64, d.BH());
+    qk_norm_bwd_kernel<BF16, D><<<grid, kThreads, 0, s>>>((const u16*)Q, rq, dQ, d.N);
+    qk_norm_bwd_kernel<BF16, D><<<grid, kThreads, 0, s>>>((const u16*)K, rk, dK, d.N);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_qk_norm_bwd(const Dims& d, const void* Q, const void* K, const float* rq, const float* rk,
+                              float* dQ, float* dK, hipStream_t s) {
+    if (d.bf16)
+        return d.D == 128 ? qk_norm_bwd_impl<true, 128>(d, Q, K, rq, rk, dQ, dK, s)
+                          : qk_norm_bwd_impl<true, 64>(d, Q, K, rq, rk, dQ, dK, s);
+    return d.D == 128 ? qk_norm_bwd_impl<false, 128>(d, Q, K, rq, rk, dQ, dK, s)
+                      : qk_norm_bwd_impl<false, 64>(d, Q, K, rq, rk, dQ, dK, s);
+}
 
 hipError_t launch_quantize(const Dims& d, const void* Q, const void* K, const void* V,
                            const sage_qtensors& out, double* ws, hipStream_t s) {

@@ -57,6 +57,7 @@ class Config:
     q_offset_sigma: float = 0.0  # per-(b,h,channel) offset of Q, shared by all tokens
     dp_int8: bool = False # ablation: dP from INT8 codes (the method keeps it 16-bit)
     p_static: bool = False  # ablation: static forward P scale 1/127 (the method: per token)
+    qk_norm_fused: bool = False  # QK-norm applied by sage_quantize (not by the generator)
 
     @property
     def sm_scale(self) -> float:
@@ -96,6 +97,8 @@ C5_QSMOOTH = C5.replace(name="long_n32k_causal_qknorm_qsmooth", q_smooth=True)
 C3_DPINT8 = C3.replace(name="d128_n8k_causal_qknorm_dpint8", dp_int8=True)
 # ... and with the static forward P scale (not the method)
 C3_PSTATIC = C3.replace(name="d128_n8k_causal_qknorm_pstatic", p_static=True)
+# ... and with raw inputs, QK-norm applied by sage_quantize instead of the generator
+C3_QKNORM_FUSED = C3.replace(name="d128_n8k_causal_qknorm_fused", qk_norm=False, qk_norm_fused=True)
 
 ALL = {c.name: c for c in (C1, C2, C3, C5)}
 

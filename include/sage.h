@@ -89,6 +89,15 @@ typedef struct sage_shape {
                            1 = ablation (the SageAttention3 write-up names it
                            beside Eq. 8 as less accurate): the static scale
                            s_P = 1/127 against the running maximum. */
+    int32_t qk_norm;    /* 1 = QK-norm fused into sage_quantize (training use;
+                           the SageBwd method summary trains with QK-norm,
+                           prerequisites "QK-norm"): each row x of Q and K is
+                           replaced by f32(x * r), r = f32(1/sqrt(mean(x^2)
+                           + 1e-6)) (mean exact in float64, IEEE double sqrt
+                           and division), before smoothing and quantisation;
+                           r goes to rq / rk.  sage_bwd's dQ, dK are then
+                           w.r.t. the normalised rows; sage_qk_norm_bwd turns
+                           them into gradients w.r.t. the inputs. */
 } sage_shape;
 /* Supported: D in {64, 128}; bq in {64, 128}; bkv = 64; N a multiple of bq
  * and of bkv (the pages define T_m = N / B_q blocks; a ragged block is
@@ -110,6 +119,9 @@ typedef struct sage_qtensors {
     float* mu_q;      /* T_m*D floats: Q block means (q_smooth; else NULL) */
     float* qk_bias;   /* T_m*N floats: sm_scale * mu_Qi . (K_n - mu_K)
                          (q_smooth; else NULL) */
+    float* rq;        /* N floats: QK-norm factor r of each Q row (qk_norm;
+                         else NULL) */
+    float* rk;        /* N floats: the same for K (qk_norm; else NULL) */
 } sage_qtensors;
 
 /* Output of sage_bwd_pre. */
@@ -183,6 +195,20 @@ size_t sage_bwd_workspace_bytes(const sage_shape* shape);
  */
 int sage_bwd(const sage_shape* shape, const sage_qtensors* qk, const sage_dotensors* dos,
              const float* L, void* workspace, float* dQ, float* dK, float* dV, sage_stream_t stream);
+
+/*
+ * sage_qk_norm_bwd — the gradient through QK-norm (shape->qk_norm = 1), in
+ * place: for each row of Q (K likewise), with r from sage_quantize (`qk`
+ * rq / rk) and x_n = f32(x * r) as the forward formed it,
+ *   dX = r * (dX_n - x_n * mean(dX_n o x_n))       (mean in float64),
+ * turning sage_bwd's dQ and dK (w.r.t. the normalised rows) into gradients
+ * w.r.t. the inputs Q and K ([B,H,N,D] 16-bit, the same tensors
+ * sage_quantize was given).  dQ, dK: [B,H,N,D] float32, read and written.
+ * Errors: SAGE_EINVAL without qk_norm in the shape or for a missing or
+ * misaligned pointer (rq, rk included); nothing launched then.
+ */
+int sage_qk_norm_bwd(const sage_shape* shape, const void* Q, const void* K, const sage_qtensors* qk, float* dQ,
+                     float* dK, sage_stream_t stream);
 
 /* Text for a status code (static storage). */
 const char* sage_status_str(int status);

@@ -68,7 +68,9 @@ def run_gpu(cfg, inputs):
     res = bd.run(sh, Q, K, V, dO)
     torch.cuda.synchronize()
     host = {}
-    for k in ("O", "L", "dQ", "dK", "dV"):
+    for k in ("O", "L", "dQ", "dK", "dV", "dQ_in", "dK_in"):
+        if k not in res:
+            continue
         t = res[k]
         host[k] = (t.float() if t.dtype in (torch.bfloat16, torch.float16) else t).cpu().numpy()
     host["O_bits"] = res["O"].view(torch.int16).cpu().numpy().view(np.uint16)
@@ -104,6 +106,9 @@ def check_quantize(cfg, inputs, g, b, h):
     else:
         vr = bd.unpack_codes(qt["vr"][b, h].view(np.uint16), "R16H", N, D)
         np.testing.assert_array_equal(vr, inputs["v"]["bits"][b, h])
+    if getattr(cfg, "qk_norm_fused", False):
+        np.testing.assert_array_equal(qt["rq"][b, h], qz.rq.astype(np.float32))
+        np.testing.assert_array_equal(qt["rk"][b, h], qz.rk.astype(np.float32))
     if cfg.k_smooth:
         np.testing.assert_array_equal(qt["mu_k"][b, h], qz.mu_k.astype(np.float32))
     if cfg.q_smooth:
@@ -233,5 +238,6 @@ def check_full_chain(cfg, inputs, g, log=None):
             check_fwd(cfg, inputs, g, b, h, qz, allq, log=log)
             check_bwd(cfg, inputs, g, b, h, qz, allk, allq, log=log)
             r = sage.run_head(Q, K, V, dO, shp)
-            for name in ("O", "dQ", "dK", "dV"):
+            names = ("O", "dQ", "dK", "dV") + (("dQ_in", "dK_in") if shp.qk_norm else ())
+            for name in names:
                 close(f"chain_{name}[{b},{h}]", g[name][b, h], r[name], rel_max=CHAIN_REL_L2_MAX, log=log)

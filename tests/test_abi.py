@@ -39,14 +39,14 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_struct_layouts_match_header():
-    assert ctypes.sizeof(bd.c_shape) == 13 * 4
-    assert ctypes.sizeof(bd.c_qtensors) == 12 * 8
+    assert ctypes.sizeof(bd.c_shape) == 14 * 4
+    assert ctypes.sizeof(bd.c_qtensors) == 14 * 8
     assert ctypes.sizeof(bd.c_dotensors) == 4 * 8
 
 
 def _shape(**kw):
     base = dict(B=1, H=2, N=256, D=128, bq=128, bkv=64, dtype=1, causal=0, k_smooth=1, q_smooth=0, sm_scale=0.0,
-                dp_int8=0, p_static=0)
+                dp_int8=0, p_static=0, qk_norm=0)
     base.update(kw)
     return bd.c_shape(**base)
 
@@ -79,6 +79,7 @@ BAD_SHAPES = [
     (dict(causal=2), bd.SAGE_EINVAL),
     (dict(dp_int8=2), bd.SAGE_EINVAL),
     (dict(p_static=-1), bd.SAGE_EINVAL),
+    (dict(qk_norm=3), bd.SAGE_EINVAL),
     (dict(sm_scale=-1.0), bd.SAGE_EINVAL),
     (dict(sm_scale=float("nan")), bd.SAGE_EINVAL),
     (dict(B=70000, H=1), bd.SAGE_EUNSUPPORTED),
@@ -104,7 +105,7 @@ def test_null_shape(lib):
 
 @pytest.mark.parametrize("field", bd.QT_FIELDS)
 def test_missing_or_misaligned_qtensor(lib, field):
-    s = _shape(q_smooth=1)
+    s = _shape(q_smooth=1, qk_norm=1)   # every field required
     for bad in (None, FAKE + 4):
         qt = _qt(**{field: bad})
         assert lib.sage_fwd(ctypes.byref(s), ctypes.byref(qt), FAKE, FAKE, None) == bd.SAGE_EINVAL
@@ -189,3 +190,18 @@ def test_autograd_wrapper_rejects_cpu_tensors():
     x = torch.zeros((1, 1, 64, 64), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         sage_attention(x, x, x)
+
+
+def test_qk_norm_buffers_and_backward_checks(lib):
+    """With qk_norm the quantise call needs rq and rk; sage_qk_norm_bwd needs
+    the flag and every pointer (rejected on the host, nothing launched)."""
+    sh = _shape(qk_norm=1)
+    qt = _qt(rq=None)
+    assert lib.sage_quantize(ctypes.byref(sh), FAKE, FAKE, FAKE, ctypes.byref(qt), FAKE, None) == bd.SAGE_EINVAL
+    full = _qt()
+    plain = _shape()
+    assert lib.sage_qk_norm_bwd(ctypes.byref(plain), FAKE, FAKE, ctypes.byref(full), FAKE, FAKE, None) == bd.SAGE_EINVAL
+    assert lib.sage_qk_norm_bwd(ctypes.byref(sh), FAKE, FAKE, ctypes.byref(_qt(rk=None)), FAKE, FAKE,
+                                None) == bd.SAGE_EINVAL
+    assert lib.sage_qk_norm_bwd(ctypes.byref(sh), FAKE, FAKE, ctypes.byref(full), None, FAKE, None) == bd.SAGE_EINVAL
+    assert lib.sage_qk_norm_bwd(ctypes.byref(sh), FAKE, FAKE, None, FAKE, FAKE, None) == bd.SAGE_EINVAL

@@ -49,6 +49,10 @@ SMALL = [
     # the static-P ablation
     small("n320_d128_bq64_causal_pstatic", 320, 128, 64, True).replace(p_static=True),
     small("n256_d64_qsmooth_pstatic", 256, 64, 128, False, q_smooth=True, sigma=2.0).replace(p_static=True),
+    # QK-norm fused into sage_quantize, and the gradient through it
+    small("n256_d128_causal_qknorm", 256, 128, 128, True, sigma=3.0).replace(qk_norm_fused=True),
+    small("n192_d64_bq64_qsmooth_qknorm", 192, 64, 64, False, q_smooth=True, sigma=2.0).replace(qk_norm_fused=True),
+    small("n256_d64_fp16_causal_qknorm", 256, 64, 128, True, dtype=wl.FP16).replace(qk_norm_fused=True),
 ]
 
 
@@ -98,6 +102,7 @@ FULL = [
     (wl.C5_QSMOOTH, [(0, 5)]),
     (wl.C3_DPINT8, [(1, 3)]),
     (wl.C3_PSTATIC, [(0, 9)]),
+    (wl.C3_QKNORM_FUSED, [(1, 11)]),
 ]
 
 
@@ -142,8 +147,8 @@ def test_smoothing_variants_on_offset_heads(ks, qs):
     gp.report_vs_fpa(cfg, x, g, 0, 0, allq, allk, {"O": O, "dQ": dQ, "dK": dK, "dV": dV})
 
 
-@pytest.mark.parametrize("causal", [False, True])
-def test_autograd_wrapper_matches_the_oracle(causal):
+@pytest.mark.parametrize("causal,qk_norm", [(False, False), (True, False), (True, True)])
+def test_autograd_wrapper_matches_the_oracle(causal, qk_norm):
     """sage_attention (a torch.autograd.Function over the four calls): O and
     the gradients it returns through autograd against the oracle's chain, and
     identical to calling the four entry points directly."""
@@ -151,27 +156,28 @@ def test_autograd_wrapper_matches_the_oracle(causal):
 
     from bit_trainable_attention_block_amd.autograd import sage_attention
     from oracle import sage as osage
-    cfg = small("autograd", 256, 128, 128, causal, H=2)
-    gp.say(f"[gpu] autograd wrapper causal={causal}")
-    gp.CURRENT_CASE[0] = f"autograd_causal{int(causal)}"
+    cfg = small("autograd", 256, 128, 128, causal, H=2, sigma=2.0).replace(qk_norm_fused=qk_norm)
+    gp.say(f"[gpu] autograd wrapper causal={causal} qk_norm={qk_norm}")
+    gp.CURRENT_CASE[0] = f"autograd_causal{int(causal)}_qknorm{int(qk_norm)}"
     x = wl.generate(cfg)
     dev = gp.to_device(x)
     Q, K, V, dO = (dev[n].view(torch.bfloat16).clone() for n in ("q", "k", "v", "do"))
     for t in (Q, K, V):
         t.requires_grad_(True)
-    O = sage_attention(Q, K, V, causal=causal)
+    O = sage_attention(Q, K, V, causal=causal, qk_norm=qk_norm)
     O.backward(dO)
     torch.cuda.synchronize()
     direct = gp.run_gpu(cfg, x)
     np.testing.assert_array_equal(O.detach().view(torch.int16).cpu().numpy().view(np.uint16), direct["O_bits"])
-    for name, t in (("dQ", Q), ("dK", K), ("dV", V)):
+    grads = (("dQ_in", Q), ("dK_in", K), ("dV", V)) if qk_norm else (("dQ", Q), ("dK", K), ("dV", V))
+    for name, t in grads:
         ref16 = torch.from_numpy(direct[name]).to(torch.bfloat16)
         np.testing.assert_array_equal(t.grad.cpu().view(torch.int16).numpy(), ref16.view(torch.int16).numpy())
     shp = osage.Shape.of(cfg)
     for h in range(cfg.H):
         r = osage.run_head(*gp.head_inputs(x, 0, h), shp)
         gp.close(f"O[0,{h}]", O.detach()[0, h].float().cpu().numpy(), r["O"], rel_max=gp.CHAIN_REL_L2_MAX)
-        for name, t in (("dQ", Q), ("dK", K), ("dV", V)):
+        for name, t in grads:
             # bf16 gradients: the 16-bit rounding (2^-9 relative) bounds the
             # difference on top of the float32 chain bar
             gp.close(f"{name}[0,{h}]", t.grad[0, h].float().cpu().numpy(), r[name], rel_max=gp.CHAIN_REL_L2_MAX,
