@@ -90,7 +90,7 @@ struct BwdStage {
     int8_t dot[BQ * D];   // dO codes, C64P
     int8_t dor[(DPI8 ? 1 : 2) * BQ * D];   // dO, R16H; with dp_int8 dO's codes, R32
     float l2[BQ];         // L * log2 e
-    float delta[BQ];
+    float ndelta[BQ];     // -delta (the dP accumulation starts from it)
 };
 
 // Asynchronous copy of query tile qbase (Q codes, dO codes, dO) into a stage.
@@ -274,8 +274,10 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
             struct OpsA {
                 v4i q[KS8];
                 v4i d[KSV];
+                v4f nd;   // -delta of the block's four query rows of this lane group
             };
             OpsA opa[2];
+            v4f ndb[2];   // dp_int8: -delta of the block issued last and of the one before
             auto read_block = [&](int mb, OpsA& o) __attribute__((always_inline)) {
                 const int row = 16 * mb + n16;  // query row (in tile) this lane supplies
 #pragma unroll
@@ -285,15 +287,18 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
                 for (int ks = 0; ks < KSV; ++ks)
                     o.d[ks] = DPI8 ? *reinterpret_cast<const v4i*>(cur.dor + off_r32(row, 64 * ks + 16 * g, D))
                                    : *reinterpret_cast<const v4i*>(cur.dor + 2 * off_r16h(row, 32 * ks + 8 * g, D));
+                o.nd = *reinterpret_cast<const v4f*>(&cur.ndelta[16 * mb + 4 * g]);
             };
             auto mfma_block = [&](int mb, const OpsA& o) __attribute__((always_inline)) {
 #pragma unroll
                 for (int ks = 0; ks < KS8; ++ks) s[mb] = mfma16_i8(o.q[ks], kop[ks], ks == 0 ? magic4 : s[mb]);
 #pragma unroll
                 for (int ks = 0; ks < KSV; ++ks) {
+                    // 16-bit dP accumulates onto -delta: the product yields dP - delta
                     if constexpr (DPI8) dp[mb] = mfma16_i8(o.d[ks], vop[ks], ks == 0 ? magic4 : dp[mb]);
-                    else dp[mb] = mfma16_h<BF16>(o.d[ks], vop[ks], ks == 0 ? v4f{0, 0, 0, 0} : dp[mb]);
+                    else dp[mb] = mfma16_h<BF16>(o.d[ks], vop[ks], ks == 0 ? o.nd : dp[mb]);
                 }
+                if constexpr (DPI8) ndb[mb & 1] = o.nd;
             };
             read_block(0, opa[0]);
             if (MB > 1) read_block(1, opa[1]);
@@ -303,16 +308,16 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
                 if (mb + 2 < MB) read_block(mb + 2, opa[mb & 1]);
                 if (mb + 1 < MB) mfma_block(mb + 1, opa[(mb + 1) & 1]);
                 const v4f l2 = *reinterpret_cast<const v4f*>(&cur.l2[16 * mb + 4 * g]);
-                const v4f dl = *reinterpret_cast<const v4f*>(&cur.delta[16 * mb + 4 * g]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     float x = fmaf(unmagic(s[mb][r]), c2, -l2[r]);
                     if (QSMOOTH) x += bias2;
                     const float pv = __builtin_amdgcn_exp2f(x);
-                    float dpv;
-                    if constexpr (DPI8) dpv = unmagic(dp[mb][r]) * cdp;
-                    else dpv = dp[mb][r];
-                    const float dsv = pv * (dpv - dl[r]);
+                    // dP - delta (16-bit dP already holds it; the INT8 one is scaled here)
+                    float dpd;
+                    if constexpr (DPI8) dpd = fmaf(unmagic(dp[mb][r]), cdp, ndb[mb & 1][r]);
+                    else dpd = dp[mb][r];
+                    const float dsv = pv * dpd;
                     p[mb][r] = pv;
                     ds[mb][r] = dsv;
                     pmax = fmaxf(pmax, pv);
@@ -416,7 +421,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
         if (more && tid < BQ) {
             asm volatile("" : "+v"(nL), "+v"(nd));   // keep the conversion here, after the work
             nxt.l2[tid] = (float)((double)nL * kLog2e_d);
-            nxt.delta[tid] = nd;
+            nxt.ndelta[tid] = -nd;
         }
         wait_vmem();       // the asynchronous copies are not seen by the compiler's waits
         if (QSMOOTH) settle(nbias);
@@ -428,7 +433,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
                                   dorh + (size_t)DOR_B * istart * BQ * D, w, lane);
     if (tid < BQ) {
         st[0].l2[tid] = (float)((double)Lh[istart * BQ + tid] * kLog2e_d);
-        st[0].delta[tid] = dlh[istart * BQ + tid];
+        st[0].ndelta[tid] = -dlh[istart * BQ + tid];
     }
     wait_vmem();       // the asynchronous copies are not seen by the compiler's waits
     // the operands held in registers are complete here, not at their first
