@@ -201,6 +201,10 @@ def report_vs_fpa(cfg, inputs, g, b, h, q_blocks, kv_blocks, ours):
     the oracle's O, dQ, dK, dV on those rows."""
     shp = sage.Shape.of(cfg)
     Q, K, V, dO = (a.astype(np.float64) for a in head_inputs(inputs, b, h))
+    if shp.qk_norm:
+        # the attention inputs are the normalised Q and K; dQ and dK are
+        # gradients with respect to them
+        Q, K = sage.rms_norm(Q, quant=False)[0], sage.rms_norm(K, quant=False)[0]
     qr = np.concatenate([np.arange(i * cfg.bq, (i + 1) * cfg.bq) for i in q_blocks])
     kr = np.concatenate([np.arange(j * cfg.bkv, (j + 1) * cfg.bkv) for j in kv_blocks])
     O_f, dQ_f = fpa_rows(Q, K, V, dO, shp.scale, cfg.causal, qr)
