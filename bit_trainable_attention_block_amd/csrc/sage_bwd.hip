@@ -35,6 +35,7 @@
 // stored at chunk slot c ^ (kr mod BQ/16), which spreads the transpose reads
 // of eight consecutive rows over distinct LDS banks.
 #include <algorithm>
+#include <cstddef>
 #include <type_traits>
 
 #include "sage_device.h"
@@ -93,49 +94,37 @@ struct BwdStage {
     float ndelta[BQ];     // -delta (the dP accumulation starts from it)
 };
 
-// Asynchronous copy of query tile qbase (Q codes, dO codes, dO) into a stage.
-// The three regions are contiguous BQ*D, BQ*D and 2*BQ*D byte runs (BQ*D for
-// the third with dp_int8); each wave instruction moves 1 KiB, and round u of
+// Asynchronous copy of query tile qbase (Q codes, dO codes, dO) into the
+// stage at LDS address `lds`.  The three regions are contiguous BQ*D, BQ*D
+// and 2*BQ*D byte runs (BQ*D for the third with dp_int8), laid out in the
+// same order in the stage; each wave instruction moves 1 KiB, and round u of
 // the eight waves moves the stage's u-th 8 KiB.  When a region is a whole
 // number of rounds (BQ*D a multiple of 8 KiB) the region of a round is known
-// at compile time.
+// at compile time.  voff = 16 * lane.
 template <int BQ, int D, bool DPI8>
-__device__ __forceinline__ void stage_query_tile(BwdStage<BQ, D, DPI8>& st, const int8_t* q, const int8_t* dot,
-                                                 const int8_t* dorb, int w, int lane) {
-    constexpr int QB = BQ * D, TOT = (DPI8 ? 3 : 4) * QB, ROUNDS = (TOT + 8 * 1024 - 1) / (8 * 1024);
+__device__ __forceinline__ void stage_query_tile(unsigned lds, const int8_t* q, const int8_t* dot,
+                                                 const int8_t* dorb, int w, unsigned voff) {
+    constexpr int QB = BQ * D, TOT = (DPI8 ? 3 : 4) * QB, R = 8 * 1024;
+    constexpr int ROUNDS = (TOT + R - 1) / R, FULL = TOT / R;
     static_assert(QB % 1024 == 0, "stage shape");
-    int8_t* dst_dor = st.dor;
+    const int8_t* src[ROUNDS];
+    unsigned dst[ROUNDS];
 #pragma unroll
     for (int u = 0; u < ROUNDS; ++u) {
-        const int c0 = u * 8 * 1024 + w * 1024;
-        if (c0 >= TOT) break;   // the last round of a stage that is not a whole number of rounds
-        const int8_t* src;
-        int8_t* dst;
-        if constexpr (QB % (8 * 1024) == 0) {
-            constexpr int RQ = QB / (8 * 1024);   // rounds per 1-byte region
-            const int off = (u % RQ) * 8 * 1024 + w * 1024;
-            if (u < RQ) {
-                src = q + off;
-                dst = st.q + off;
-            } else if (u < 2 * RQ) {
-                src = dot + off;
-                dst = st.dot + off;
-            } else {
-                const int o2 = (u - 2 * RQ) * 8 * 1024 + w * 1024;
-                src = dorb + o2;
-                dst = dst_dor + o2;
-            }
-        } else if (c0 < QB) {
-            src = q + c0;
-            dst = st.q + c0;
-        } else if (c0 < 2 * QB) {
-            src = dot + (c0 - QB);
-            dst = st.dot + (c0 - QB);
+        const int c0 = u * R + w * 1024;
+        if constexpr (QB % R == 0) {
+            constexpr int RQ = QB / R;   // rounds per 1-byte region
+            const int off = (u % RQ) * R + w * 1024;
+            src[u] = u < RQ ? q + off : u < 2 * RQ ? dot + off : dorb + (u - 2 * RQ) * R + w * 1024;
         } else {
-            src = dorb + (c0 - 2 * QB);
-            dst = dst_dor + (c0 - 2 * QB);
+            src[u] = c0 < QB ? q + c0 : c0 < 2 * QB ? dot + (c0 - QB) : dorb + (c0 - 2 * QB);
         }
-        copy16_to_lds(src + lane * 16, dst);
+        dst[u] = lds + c0;
+    }
+    copy16_rounds<FULL>(src, dst, voff);
+    if constexpr (FULL < ROUNDS) {
+        // the last round of a stage that is not a whole number of rounds
+        if (FULL * R + w * 1024 < TOT) copy16x1_to_lds(src[FULL], dst[FULL], voff);
     }
 }
 
@@ -157,6 +146,8 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
     constexpr int DB = D / 16;    // 16-wide blocks of d
     constexpr int CH = BQ / 16;   // 16-byte chunks per dS key row
     __shared__ __align__(16) BwdStage<BQ, D, DPI8> st[2];
+    using Stage = BwdStage<BQ, D, DPI8>;
+    static_assert(offsetof(Stage, dot) == BQ * D && offsetof(Stage, dor) == 2 * BQ * D, "stage layout");
     __shared__ float red[2][2][4];   // [key block][P | dS][key group]
 
     const int Tn = N / 64, Tm = N / BQ;
@@ -166,6 +157,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int lane = tid & 63, n16 = lane & 15, g = lane >> 4;
+    const unsigned voff = 16u * lane;
     const int kb = w >> 2, kg = w & 3;
     const int j = 2 * jj + kb;        // this wave's key block
     const bool kv_on = j < Tn;        // the second block of a ragged tail may not exist
@@ -231,8 +223,9 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
         }
         if (QSMOOTH && kv_on && more) nbias = qk_bias[((size_t)bh * Tm + i + 1) * N + key];
         if (more)
-            stage_query_tile<BQ, D, DPI8>(nxt, qh + (size_t)(qbase + BQ) * D, doth + (size_t)(qbase + BQ) * D,
-                                          dorh + (size_t)DOR_B * (qbase + BQ) * D, w, lane);
+            stage_query_tile<BQ, D, DPI8>(lds_addr(&nxt), qh + (size_t)(qbase + BQ) * D,
+                                          doth + (size_t)(qbase + BQ) * D, dorh + (size_t)DOR_B * (qbase + BQ) * D,
+                                          w, voff);
 
         // the tile exists and has a visible key (it is stored for the dQ pass)
         const bool tile_on = kv_on && (!CAUSAL || j * 64 <= qbase + BQ - 1);
@@ -429,8 +422,8 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
     };
 
     // ---- prologue: first query tile into st0
-    stage_query_tile<BQ, D, DPI8>(st[0], qh + (size_t)istart * BQ * D, doth + (size_t)istart * BQ * D,
-                                  dorh + (size_t)DOR_B * istart * BQ * D, w, lane);
+    stage_query_tile<BQ, D, DPI8>(lds_addr(&st[0]), qh + (size_t)istart * BQ * D, doth + (size_t)istart * BQ * D,
+                                  dorh + (size_t)DOR_B * istart * BQ * D, w, voff);
     if (tid < BQ) {
         st[0].l2[tid] = (float)((double)Lh[istart * BQ + tid] * kLog2e_d);
         st[0].ndelta[tid] = -dlh[istart * BQ + tid];
@@ -488,6 +481,8 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const int8_t* __restrict__ d
     constexpr int ROUNDS = (DS_BYTES + K_BYTES) / 4096;
     static_assert((DS_BYTES + K_BYTES) % 4096 == 0 && DS_BYTES % 1024 == 0, "stage shape");
     __shared__ __align__(16) DqStage<BQ, D> st[2];
+    using Stage = DqStage<BQ, D>;
+    static_assert(offsetof(Stage, k) == DS_BYTES, "stage layout");
 
     const int Tn = N / 64, Tm = N / BQ;
     int unit, bh;
@@ -500,16 +495,24 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const int8_t* __restrict__ d
     const int lane = tid & 63, n16 = lane & 15, g = lane >> 4;
     const int jend = CAUSAL ? (i + 1) * BQ / 64 : Tn;
 
+    const unsigned voff = 16u * lane;
+    // the stage's ds and k regions are contiguous: round u fills its bytes
+    // [4096 u, 4096 u + 4096)
     auto load = [&](int j, DqStage<BQ, D>& st) __attribute__((always_inline)) {
         const size_t t = (size_t)bh * tph + tile_index<BQ, CAUSAL>(i, j, Tn);
         const int8_t* s1 = dsw + t * DS_BYTES;
         const int8_t* s2 = kt + head + (size_t)j * K_BYTES;
+        const unsigned base = lds_addr(&st);
+        const int8_t* src[ROUNDS];
+        unsigned dst[ROUNDS];
 #pragma unroll
         for (int u = 0; u < ROUNDS; ++u) {
             const int c0 = u * 4096 + w * 1024;
-            if (c0 < DS_BYTES) copy16_to_lds(s1 + c0 + lane * 16, st.ds + c0);
-            else copy16_to_lds(s2 + (c0 - DS_BYTES) + lane * 16, st.k + (c0 - DS_BYTES));
+            if constexpr (DS_BYTES % 4096 == 0) src[u] = u * 4096 < DS_BYTES ? s1 + c0 : s2 + (c0 - DS_BYTES);
+            else src[u] = c0 < DS_BYTES ? s1 + c0 : s2 + (c0 - DS_BYTES);
+            dst[u] = base + c0;
         }
+        copy16_rounds<ROUNDS>(src, dst, voff);
     };
 
     v4f acc[MBq][NB];

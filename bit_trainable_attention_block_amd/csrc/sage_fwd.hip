@@ -20,6 +20,8 @@
 //   s_P = 2^(rm - m) / 127,  l += s_P * sum(127 * 2^(x - rm))
 // and the codes feed the second product straight from registers:
 //   O^T (D x 16 queries) += V^_j^T P^^T  (int32) -> O = O * alpha + f32 * s_P s_V.
+// (l and O are kept multiplied by 127, i.e. scaled by 127 s_P = 2^(rm - m):
+// no division per tile; the factor cancels in O / l and leaves L as log2 127.)
 // The result order of S^T (key 16 kb + 4 g + r in lane group g, register r
 // of key block kb) is the operand order of a 64-key contraction once the V
 // codes are stored permuted (C64P), so no shuffle or LDS round trip is needed.
@@ -50,14 +52,6 @@ constexpr int kWaves = 8;
 constexpr int kQTile = 16 * kWaves;  // queries per workgroup
 constexpr int kKTile = 64;           // keys per stage (= the K/V quantisation block)
 constexpr float kLazy = 8.f;         // log2 slack before the reference maximum moves
-constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23: x + kMagic holds rint(x) in its low byte
-
-// Byte 0 of four magic-rounded floats -> one dword.
-__device__ __forceinline__ int pack_magic(float a, float b, float c, float d) {
-    const uint32_t lo = __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x0c0c0400u);
-    const uint32_t hi = __builtin_amdgcn_perm(__float_as_uint(d), __float_as_uint(c), 0x04000c0cu);
-    return (int)(lo | hi);
-}
 
 // Maximum / sum over the four lane groups holding one query (lanes l, l^16,
 // l^32, l^48): each lane swap returns a lane's own value and its partner's.
@@ -162,15 +156,16 @@ __global__ __launch_bounds__(64 * kWaves, 2) void fwd_kernel(
 
     // asynchronous copy of key tile j (K and V codes: two contiguous runs;
     // with Q-smoothing also the tile's 64 bias values of each Q block)
+    const unsigned voff = 16u * lane;
     auto load = [&](int j, FwdStage<D>& dst) __attribute__((always_inline)) {
         const int8_t* ks_ = k + head + (size_t)j * TILE_BYTES;
         const int8_t* vs_ = vt + head + (size_t)j * TILE_BYTES;
+        const unsigned lk = lds_addr(dst.k), lv = lds_addr(dst.v);
 #pragma unroll
         for (int c0 = 0; c0 < TILE_BYTES; c0 += NT * 16) {
-            if (c0 + w * 1024 < TILE_BYTES) {   // a d=64 tile is half a round
-                copy16_to_lds(ks_ + c0 + w * 1024 + lane * 16, dst.k + c0 + w * 1024);
-                copy16_to_lds(vs_ + c0 + w * 1024 + lane * 16, dst.v + c0 + w * 1024);
-            }
+            if (c0 + w * 1024 < TILE_BYTES)   // a d=64 tile is half a round
+                copy16x2_to_lds(ks_ + c0 + w * 1024, lk + c0 + w * 1024, vs_ + c0 + w * 1024, lv + c0 + w * 1024,
+                                voff);
         }
         if (QSMOOTH && w == kWaves - 1) {
             // lane group r of the first kQTile/64 groups: Q block row r, 16 B
@@ -253,7 +248,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void fwd_kernel(
                 sum = 0.f;
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) {
-                    float c[4];
+                    uint32_t word = 0u;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         float x = QSMOOTH ? fmaf(unmagic(s[kb][r]), c2, bias2[kb][r] - shift)
@@ -264,9 +259,10 @@ __global__ __launch_bounds__(64 * kWaves, 2) void fwd_kernel(
                         }
                         const float e = __builtin_amdgcn_exp2f(x);  // 127 * 2^(x - rm), in [0, 127]
                         sum += e;
-                        c[r] = e + kMagic;                           // rint(e) in the low byte
+                        // byte r of the word = rint(e) (round to nearest even)
+                        word = __builtin_amdgcn_cvt_pk_u8_f32(e, r, word);
                     }
-                    pc[kb] = pack_magic(c[0], c[1], c[2], c[3]);
+                    pc[kb] = (int)word;
                 }
                 sum = qsum4(sum);
             };
@@ -280,7 +276,9 @@ __global__ __launch_bounds__(64 * kWaves, 2) void fwd_kernel(
             // factor do, and those use it consistently.
             // (static scale: the exact running maximum, s_P = 1/127)
             const float m_new = PSTATIC ? fmaxf(m, rm) : ((rm > m + kLazy) ? rm : m);
-            const float sP = PSTATIC ? __fdiv_rn(1.f, 127.f) : __fdiv_rn(__builtin_amdgcn_exp2f(rm - m_new), 127.f);
+            // 127 s_P: l and O both carry the factor 127, which cancels in O / l
+            // and is taken out of L at the end
+            const float sP = PSTATIC ? 1.f : __builtin_amdgcn_exp2f(rm - m_new);
             if (__builtin_expect(__any(m_new != m), 0)) {
                 // rare: a row's reference maximum moved; rescale l and O
                 const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 0 on the first tile
@@ -318,7 +316,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void fwd_kernel(
             pk.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
             *reinterpret_cast<uint2*>(O + 16 * db + 4 * g) = pk;
         }
-        if (g == 0) L[(size_t)bh * N + query] = (m + log2f(l)) * kLn2;
+        if (g == 0) L[(size_t)bh * N + query] = (m + (log2f(l) - kLog2_127)) * kLn2;
     }
 }
 
