@@ -63,6 +63,15 @@ Numeric model (the readings taken where the pages leave a choice open)
   Table 1c, compares dO V^T in INT8 against FP16): dP = (dO^_i V^_j^T) *
   s_dO,i * s_V,j from the same per-block codes the other products use.
 
+* Variant switch Shape.fp8 (not the method, which is INT8; the
+  SageAttention3 write-up compares INT8 and FP8 SageBwd gradients in its
+  INT8-versus-FP8 training table): every quantised operand takes E4M3 codes
+  (OCP 8-bit float: 4 exponent bits with bias 7, 3 mantissa bits, no
+  infinities, largest finite 448) in place of INT8.  The scales use 448 in
+  place of 127 (s = f32(max|X| / 448); forward s_P = f32(f32(exp(rm - m)) /
+  448)) and a code is the float32 quotient rounded to the nearest E4M3 value,
+  ties to even.  The products are sums of the decoded codes, as for INT8.
+
 Quantisation-off mode (quant=False): every quantise/dequantise pair becomes
 the identity (codes = values, scales = 1), nothing is rounded, and the result
 must equal full-precision attention (oracle.fpa) to float64 rounding.
@@ -126,6 +135,18 @@ class Shape:
     # normalisation of Q and K with unit gain before smoothing and
     # quantisation; the gradients then pass back through it
     qk_norm: bool = False
+    # Variant, not the method: E4M3 codes with 448 in place of INT8 and 127
+    # (the SageAttention3 write-up's INT8-versus-FP8 training comparison)
+    fp8: bool = False
+
+    def __post_init__(self):
+        if self.fp8 and (self.dp_int8 or self.p_static):
+            raise ValueError("the E4M3 variant takes neither the INT8 dP ablation nor the static P scale")
+
+    @property
+    def qmax(self) -> int:
+        """Largest code magnitude: 127 (INT8) or 448 (E4M3)."""
+        return 448 if self.fp8 else 127
 
     @property
     def scale(self) -> float:
@@ -145,27 +166,67 @@ class Shape:
         return Shape(N=cfg.N, D=cfg.D, bq=cfg.bq, bkv=cfg.bkv, causal=bool(cfg.causal),
                      k_smooth=bool(cfg.k_smooth), q_smooth=bool(cfg.q_smooth), dtype=int(cfg.dtype),
                      dp_int8=bool(getattr(cfg, "dp_int8", False)), p_static=bool(getattr(cfg, "p_static", False)),
-                     qk_norm=bool(getattr(cfg, "qk_norm_fused", False)))
+                     qk_norm=bool(getattr(cfg, "qk_norm_fused", False)), fp8=bool(getattr(cfg, "fp8", False)))
 
 
 # ---------------------------------------------------------------------------
 # Per-block INT8 quantisation (prerequisites "INT8 quantisation"; SA3 Eq. 7)
 # ---------------------------------------------------------------------------
 
-def quantize_block(X, quant=True):
-    """delta = max|X| / 127, codes = round(X / delta).
+E4M3_MAX = 448.0
 
-    X holds float32-representable values.  Returns (codes as float64 integer
-    values, scale).  Quantisation off: (X, 1.0)."""
+
+def e4m3_round(x):
+    """Nearest E4M3 value of each element (OCP 8-bit float: sign, 4 exponent
+    bits with bias 7, 3 mantissa bits; subnormals below 2^-6 in steps of 2^-9;
+    no infinities, largest finite 448), ties to even; magnitudes beyond 448
+    saturate to 448.  Returns float64."""
+    x = np.asarray(x, dtype=F64)
+    out = np.zeros_like(x)
+    nz = x != 0
+    _, e = np.frexp(x[nz])                   # |x| = m 2^e, 0.5 <= m < 1: leading bit 2^(e-1)
+    step = np.exp2(np.maximum(e - 1, -6) - 3)  # value spacing in x's binade (subnormal: 2^-9)
+    out[nz] = np.rint(x[nz] / step) * step   # exact scaling by a power of two, half-even
+    return np.clip(out, -E4M3_MAX, E4M3_MAX)
+
+
+def e4m3_bits(v):
+    """The byte encoding of E4M3 values (sign bit 7, exponent bits 6-3, mantissa
+    bits 2-0); v must hold representable values (e.g. from e4m3_round)."""
+    v = np.asarray(v, dtype=F64)
+    a = np.abs(v)
+    sign = np.signbit(v).astype(np.uint8) << 7
+    _, e = np.frexp(np.where(a > 0, a, 1.0))
+    normal = a >= 2.0 ** -6
+    ex = np.where(normal, e - 1 + 7, 0)
+    man = np.where(normal, a / np.exp2(e - 1.0) * 8 - 8, a / 2.0 ** -9)
+    return (sign | (ex.astype(np.uint8) << 3) | man.astype(np.uint8)).astype(np.uint8)
+
+
+def round_codes(x, fp8: bool, lo: float):
+    """Codes from scaled float32 quotients: INT8 rint clamped to [lo, 127]
+    (half-even), or E4M3 rounding (whose range ends at 448)."""
+    if fp8:
+        return np.maximum(e4m3_round(x), lo)
+    return np.clip(np.rint(x), lo, 127)
+
+
+def quantize_block(X, quant=True, fp8=False):
+    """delta = max|X| / 127, codes = round(X / delta) (E4M3: 448 and the
+    nearest E4M3 value).
+
+    X holds float32-representable values.  Returns (codes as float64 values,
+    scale).  Quantisation off: (X, 1.0)."""
     X = np.asarray(X, dtype=F64)
     if not quant:
         return X.copy(), 1.0
+    qmax = 448 if fp8 else 127
     x32 = X.astype(F32)
     a = np.max(np.abs(x32)) if x32.size else F32(0)
     if a == 0:
         return np.zeros_like(X), 0.0
-    s = F32(a) / F32(127)                          # float32 / float32: correctly rounded
-    codes = np.clip(np.rint(x32 / s), -127, 127)   # float32 division, then half-even rint
+    s = F32(a) / F32(qmax)                                   # float32 / float32: correctly rounded
+    codes = round_codes((x32 / s).astype(F64), fp8, -qmax)   # float32 division, then the code rounding
     return codes.astype(F64), float(s)
 
 
@@ -249,11 +310,11 @@ def quantize(Q, K, V, sh: Shape, quant=True) -> Quantized:
     Vc = np.zeros((N, D)); sV = np.zeros(sh.Tn)
     for i in range(sh.Tm):
         rows = slice(i * sh.bq, (i + 1) * sh.bq)
-        Qc[rows], sQ[i] = quantize_block(Q_sm[rows], quant)
+        Qc[rows], sQ[i] = quantize_block(Q_sm[rows], quant, sh.fp8)
     for j in range(sh.Tn):
         rows = slice(j * sh.bkv, (j + 1) * sh.bkv)
-        Kc[rows], sK[j] = quantize_block(K_sm[rows], quant)
-        Vc[rows], sV[j] = quantize_block(V[rows], quant)
+        Kc[rows], sK[j] = quantize_block(K_sm[rows], quant, sh.fp8)
+        Vc[rows], sV[j] = quantize_block(V[rows], quant, sh.fp8)
     return Quantized(Qc, sQ, Kc, sK, Vc, sV, mu_k, mu_q, K_sm, rq, rk)
 
 
@@ -299,25 +360,27 @@ def _exp_shift(S, m):
     return np.where(np.isneginf(S), 0.0, E)
 
 
-def per_token_p_quant(P_tilde, rm, m_new, quant=True):
+def per_token_p_quant(P_tilde, rm, m_new, quant=True, fp8=False):
     """Forward step (4), SA3 Eq. 8: s_P = exp(rowmax(S_ij) - m_ij) / 127,
-    P^_ij = P~_ij / s_P, rounded to integers in [0, 127]."""
+    P^_ij = P~_ij / s_P, rounded to integers in [0, 127] (E4M3: 448 and the
+    nearest E4M3 value)."""
     if not quant:
         return np.ones(P_tilde.shape[0]), P_tilde.copy()
+    qmax = 448 if fp8 else 127
     with np.errstate(invalid="ignore"):
         ex = np.where(np.isneginf(rm), 0.0, np.exp(rm - m_new))
-    sP = (np.asarray(ex).astype(F32) / F32(127)).astype(F32)   # float32 division
+    sP = (np.asarray(ex).astype(F32) / F32(qmax)).astype(F32)   # float32 division
     codes = np.zeros_like(P_tilde)
     live = sP > 0
     p32 = P_tilde[live].astype(F32)
-    codes[live] = np.clip(np.rint(p32 / sP[live][:, None]), 0, 127)
+    codes[live] = round_codes((p32 / sP[live][:, None]).astype(F64), fp8, 0)
     return sP.astype(F64), codes
 
 
 def static_p_quant(P_tilde, rm, quant=True):
     """The static alternative to Eq. 8: s_P = 1/127 for every row with a
     visible key, P^ = P~ / s_P rounded to integers in [0, 127] (P~ is taken
-    against the running maximum, so it lies in [0, 1])."""
+    against the running maximum, so it lies in [0, 1]).  INT8 only."""
     if not quant:
         return np.ones(P_tilde.shape[0]), P_tilde.copy()
     sP = np.where(np.isneginf(rm), F32(0), F32(1) / F32(127)).astype(F32)
@@ -356,7 +419,7 @@ def forward(qz: Quantized, sh: Shape, quant=True, q_blocks: Optional[Iterable[in
             if sh.p_static:
                 sP, P_hat = static_p_quant(P_tilde, rm, quant)
             else:
-                sP, P_hat = per_token_p_quant(P_tilde, rm, m_new, quant)
+                sP, P_hat = per_token_p_quant(P_tilde, rm, m_new, quant, sh.fp8)
             with np.errstate(invalid="ignore"):
                 alpha = np.where(np.isneginf(m), 0.0, np.exp(m - m_new))
             l = alpha * l + P_tilde.sum(axis=1)
@@ -389,7 +452,7 @@ def forward_two_pass(qz: Quantized, sh: Shape, quant=True):
         for t, j in enumerate(tiles):
             keys = slice(j * sh.bkv, (j + 1) * sh.bkv)
             P_tilde = _exp_shift(S_all[t], prefix[t])
-            sP, P_hat = per_token_p_quant(P_tilde, rms[t], prefix[t], quant)
+            sP, P_hat = per_token_p_quant(P_tilde, rms[t], prefix[t], quant, sh.fp8)
             to_final = np.exp(prefix[t] - M)
             num += to_final[:, None] * ((P_hat @ qz.Vc[keys]) * (sP[:, None] * qz.sV[j]))
             den += to_final * P_tilde.sum(axis=1)
@@ -415,7 +478,7 @@ def backward_pre(O, dO, sh: Shape, quant=True):
     dOc = np.zeros_like(dO); sdO = np.zeros(sh.Tm)
     for i in range(sh.Tm):
         rows = slice(i * sh.bq, (i + 1) * sh.bq)
-        dOc[rows], sdO[i] = quantize_block(dO[rows], quant)
+        dOc[rows], sdO[i] = quantize_block(dO[rows], quant, sh.fp8)
     return delta, dOc, sdO
 
 
@@ -432,7 +495,7 @@ def backward_tile(qz: Quantized, V, dO, dOc, sdO, L, delta, i: int, j: int, sh: 
     S = logits(qz, i, j, sh)
     P = _exp_shift(S, L[rows])
     # (3) dV_j += M(P^_ij^T, dO^_i) * s_P * s_dO, P quantised per tile
-    P_hat, sPb = quantize_block(P, quant)
+    P_hat, sPb = quantize_block(P, quant, sh.fp8)
     dV = (P_hat.T @ dOc[rows]) * (sPb * sdO[i])
     # (4) dP_ij = dO_i V_j^T from the 16-bit values, no quantisation; the
     # ablation takes it from the INT8 codes of dO_i and V_j with their scales
@@ -442,7 +505,7 @@ def backward_tile(qz: Quantized, V, dO, dOc, sdO, L, delta, i: int, j: int, sh: 
         dP = dO[rows] @ V[keys].T
     # (5) dS_ij = P_ij o (dP_ij - D_i), then per-tile INT8 quantisation
     dS = P * (dP - delta[rows][:, None])
-    dS_hat, sdS = quantize_block(dS, quant)
+    dS_hat, sdS = quantize_block(dS, quant, sh.fp8)
     # (6) dQ_i += M(dS^_ij, K^_j) * s_dS * s_K
     dQ = (dS_hat @ qz.Kc[keys]) * (sdS * qz.sK[j])
     # (7) dK_j += M(dS^_ij^T, Q^_i) * s_dS * s_Q
@@ -503,8 +566,8 @@ def run_head(Q, K, V, dO, sh: Shape, quant=True) -> Dict[str, np.ndarray]:
 
 def run(inputs: Dict[str, np.ndarray], sh: Shape, quant=True) -> Dict[str, np.ndarray]:
     """All heads of [B, H, N, D] float inputs ``q``, ``k``, ``v``, ``do``.
-    Returns stacked outputs; codes as int8, scales and means as float32 when
-    quant is on."""
+    Returns stacked outputs; codes as int8 (E4M3: their bytes as uint8),
+    scales and means as float32 when quant is on."""
     Q, K, V, dO = (np.asarray(inputs[n], dtype=F64) for n in ("q", "k", "v", "do"))
     B, H, N, D = Q.shape
     names = ["Qc", "sQ", "Kc", "sK", "Vc", "sV", "mu_k", "mu_q", "O", "L", "delta", "dOc", "sdO",
@@ -522,7 +585,7 @@ def run(inputs: Dict[str, np.ndarray], sh: Shape, quant=True) -> Dict[str, np.nd
     for n, vals in out.items():
         a = np.stack(vals).reshape((B, H) + np.shape(vals[0]))
         if quant and n in ("Qc", "Kc", "Vc", "dOc"):
-            a = a.astype(np.int8)
+            a = e4m3_bits(a) if sh.fp8 else a.astype(np.int8)
         elif quant and n in ("sQ", "sK", "sV", "mu_k", "mu_q", "L", "delta", "sdO"):
             a = a.astype(F32)
         res[n] = a

@@ -14,6 +14,7 @@ import pytest
 
 import oracle.sage as sage_mod
 from tests import test_oracle_bwd as tb
+from tests import test_oracle_fp8 as tf8
 from tests import test_oracle_fwd as tf
 from tests import test_oracle_quant as tq
 
@@ -28,12 +29,18 @@ MUTATIONS = {
     "dq_wrong_scale_index": ("(sdS * qz.sK[j])", "(sdS * qz.sK[i])"),
     "causal_strict": ("else (k <= q)", "else (k < q)"),
     "missing_dq_scale": ("return dQ * sh.scale, dK * sh.scale, dV", "return dQ, dK * sh.scale, dV"),
-    "round_half_up": ("np.clip(np.rint(x32 / s), -127, 127)", "np.clip(np.floor(x32 / s + 0.5), -127, 127)"),
+    "round_half_up": ("return np.clip(np.rint(x), lo, 127)", "return np.clip(np.floor(x + 0.5), lo, 127)"),
     "drop_dk_bias": ("dK[keys] += t[\"dK\"] + t[\"dKb\"]", "dK[keys] += t[\"dK\"]"),
     "kmean_over_block": ("mu_k = rnd(np.sum(K, axis=0) / N)", "mu_k = rnd(np.sum(K[:sh.bkv], axis=0) / sh.bkv)"),
     "p_scale_wrong_max": ("np.exp(rm - m_new))", "np.exp(m_new - rm))"),
     "dv_uses_p_not_codes": ("dV = (P_hat.T @ dOc[rows])", "dV = (P.T @ dOc[rows])"),
     "lse_log2": ("L[rows] = m + np.log(l)", "L[rows] = m + np.log2(l)"),
+    "e4m3_no_subnormals": ("step = np.exp2(np.maximum(e - 1, -6) - 3)", "step = np.exp2((e - 1) - 3)"),
+    "e4m3_ties_away": ("np.rint(x[nz] / step) * step   # exact scaling by a power of two, half-even",
+                       "np.round(x[nz] / step + 1e-9) * step"),
+    "e4m3_two_mantissa_bits": ("step = np.exp2(np.maximum(e - 1, -6) - 3)", "step = np.exp2(np.maximum(e - 1, -6) - 2)"),
+    "fp8_block_scale_127": ("    qmax = 448 if fp8 else 127\n    x32", "    qmax = 127\n    x32"),
+    "fp8_p_scale_127": ("    qmax = 448 if fp8 else 127\n    with", "    qmax = 127\n    with"),
 }
 
 
@@ -69,6 +76,10 @@ PINS = [
     lambda: tf.test_quantised_forward_close_to_exact(),
     lambda: tf.test_per_token_codes_independent_of_running_max(),
     lambda: [tb.test_quantised_gradients_with_uneven_block_scales(c) for c in (False, True)],
+    lambda: tf8.test_every_finite_encoding_round_trips(),
+    lambda: tf8.test_rounding_matches_the_library_conversion(),
+    lambda: tf8.test_block_codes_reach_448_and_stay_within_half_a_step(),
+    lambda: tf8.test_forward_p_codes_top_out_at_448(),
 ]
 
 
