@@ -332,29 +332,33 @@ def main():
         "roofline": roofline,
         "breakdown": breakdown,
     }
-    # the INT8-dP ablation (not the method): the same step with dP formed from
-    # the INT8 codes of dO and V; reported beside the headline, never as it
-    sha = dataclasses.replace(sh, dp_int8=True)
-    ab_ms = []
-    for k in range(args.warmup + max(3, args.steps // 4)):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
-        ev[0].record(stream)
-        bd.quantize(sha, Q, K, V, out=qt)
-        ev[1].record(stream)
-        bd.fwd(sha, qt, O, L)
-        ev[2].record(stream)
-        bd.bwd_pre(sha, O, dO, out=dot)
-        ev[3].record(stream)
-        bd.bwd(sha, qt, dot, L, dQ, dK, dV, ws=bws)
-        ev[4].record(stream)
-        torch.cuda.synchronize()
-        if k >= args.warmup:
-            ab_ms.append([ev[i].elapsed_time(ev[i + 1]) for i in range(4)])
-    ab = np.mean(np.array(ab_ms), axis=0)
-    breakdown["ablation_dp_int8"] = {
-        "call_ms": {c: round(float(v), 4) for c, v in zip(calls, ab)},
-        "bwd_kernel_tops": round(bwd_ops / (ab[3] * 1e-3) / 1e12, 1),
-        "fwd_bwd_tops": round(total_ops / (float(ab.sum()) * 1e-3) / 1e12, 1)}
+    # Variants (not the method), the same step with one switch flipped;
+    # reported beside the headline, never as it: the INT8-dP ablation (dP
+    # from the INT8 codes of dO and V) and the E4M3 variant (E4M3 codes and
+    # float32 products in place of INT8)
+    for key, sw in (("ablation_dp_int8", {"dp_int8": True}), ("variant_fp8", {"fp8": True})):
+        sha = dataclasses.replace(sh, **sw)
+        ab_ms = []
+        for k in range(args.warmup + max(3, args.steps // 4)):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+            ev[0].record(stream)
+            bd.quantize(sha, Q, K, V, out=qt)
+            ev[1].record(stream)
+            bd.fwd(sha, qt, O, L)
+            ev[2].record(stream)
+            bd.bwd_pre(sha, O, dO, out=dot)
+            ev[3].record(stream)
+            bd.bwd(sha, qt, dot, L, dQ, dK, dV, ws=bws)
+            ev[4].record(stream)
+            torch.cuda.synchronize()
+            if k >= args.warmup:
+                ab_ms.append([ev[i].elapsed_time(ev[i + 1]) for i in range(4)])
+        ab = np.mean(np.array(ab_ms), axis=0)
+        breakdown[key] = {
+            "call_ms": {c: round(float(v), 4) for c, v in zip(calls, ab)},
+            "fwd_kernel_tops": round(fwd_ops / (ab[1] * 1e-3) / 1e12, 1),
+            "bwd_kernel_tops": round(bwd_ops / (ab[3] * 1e-3) / 1e12, 1),
+            "fwd_bwd_tops": round(total_ops / (float(ab.sum()) * 1e-3) / 1e12, 1)}
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg)

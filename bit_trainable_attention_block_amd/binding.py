@@ -32,7 +32,7 @@ class c_shape(ctypes.Structure):
                 ("bq", ctypes.c_int32), ("bkv", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("causal", ctypes.c_int32), ("k_smooth", ctypes.c_int32), ("q_smooth", ctypes.c_int32),
                 ("sm_scale", ctypes.c_float), ("dp_int8", ctypes.c_int32), ("p_static", ctypes.c_int32),
-                ("qk_norm", ctypes.c_int32)]
+                ("qk_norm", ctypes.c_int32), ("fp8", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -108,18 +108,19 @@ class Shape:
     dp_int8: bool = False   # ablation: dP from INT8 codes (see include/sage.h)
     p_static: bool = False  # ablation: static forward P scale 1/127 (see include/sage.h)
     qk_norm: bool = False   # QK-norm fused into sage_quantize (see include/sage.h)
+    fp8: bool = False       # variant: E4M3 codes in place of INT8 (see include/sage.h)
 
     @staticmethod
     def of(cfg) -> "Shape":
         return Shape(B=cfg.B, H=cfg.H, N=cfg.N, D=cfg.D, bq=cfg.bq, bkv=cfg.bkv, dtype=cfg.dtype,
                      causal=bool(cfg.causal), k_smooth=bool(cfg.k_smooth), q_smooth=bool(cfg.q_smooth),
                      dp_int8=bool(getattr(cfg, "dp_int8", False)), p_static=bool(getattr(cfg, "p_static", False)),
-                     qk_norm=bool(getattr(cfg, "qk_norm_fused", False)))
+                     qk_norm=bool(getattr(cfg, "qk_norm_fused", False)), fp8=bool(getattr(cfg, "fp8", False)))
 
     def c(self) -> c_shape:
         return c_shape(self.B, self.H, self.N, self.D, self.bq, self.bkv, self.dtype, int(self.causal),
                        int(self.k_smooth), int(self.q_smooth), float(self.sm_scale), int(self.dp_int8),
-                       int(self.p_static), int(self.qk_norm))
+                       int(self.p_static), int(self.qk_norm), int(self.fp8))
 
     @property
     def torch_dtype(self):

@@ -19,8 +19,9 @@ int check_shape(const sage_shape* s, sage::Dims& d) {
     if (s->B < 0 || s->H < 0 || s->N < 0) return SAGE_EINVAL;
     if (s->causal < 0 || s->causal > 1 || s->k_smooth < 0 || s->k_smooth > 1 || s->q_smooth < 0 ||
         s->q_smooth > 1 || s->dp_int8 < 0 || s->dp_int8 > 1 || s->p_static < 0 || s->p_static > 1 ||
-        s->qk_norm < 0 || s->qk_norm > 1)
+        s->qk_norm < 0 || s->qk_norm > 1 || s->fp8 < 0 || s->fp8 > 1)
         return SAGE_EINVAL;
+    if (s->fp8 && (s->dp_int8 || s->p_static)) return SAGE_EUNSUPPORTED;
     if (!(s->sm_scale >= 0.f) || !std::isfinite(s->sm_scale)) return SAGE_EINVAL;
     if (s->D != 64 && s->D != 128) return SAGE_EUNSUPPORTED;
     if (s->bq != 64 && s->bq != 128) return SAGE_EUNSUPPORTED;
@@ -38,6 +39,7 @@ int check_shape(const sage_shape* s, sage::Dims& d) {
     d.dp_int8 = s->dp_int8 != 0;
     d.p_static = s->p_static != 0;
     d.qk_norm = s->qk_norm != 0;
+    d.fp8 = s->fp8 != 0;
     d.scale = s->sm_scale > 0.f ? (double)s->sm_scale : 1.0 / std::sqrt((double)s->D);
     return SAGE_OK;
 }

@@ -130,7 +130,8 @@ __device__ __forceinline__ void stage_query_tile(unsigned lds, const int8_t* q, 
 
 // Two LDS stages alternate: tile i is read from stage (i - istart) & 1 while
 // the next tile is copied into the other one.
-template <bool BF16, int D, int BQ, bool CAUSAL, bool QSMOOTH, bool DPI8>
+// F8: the E4M3 variant (codes E4M3, 448 in place of 127, float32 products).
+template <bool BF16, int D, int BQ, bool CAUSAL, bool QSMOOTH, bool DPI8, bool F8>
 __global__ __launch_bounds__(512, 1) void bwd_kernel(
     const int8_t* __restrict__ q, const float* __restrict__ sq, const int8_t* __restrict__ k,
     const float* __restrict__ sk, const u16* __restrict__ vr, const float* __restrict__ sv,
@@ -145,6 +146,9 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
     constexpr int KSH = D / 32;   // 16-bit contraction steps over d
     constexpr int DB = D / 16;    // 16-wide blocks of d
     constexpr int CH = BQ / 16;   // 16-byte chunks per dS key row
+    static_assert(!(F8 && DPI8), "the INT8 dP ablation has no E4M3 form");
+    using Acc = typename std::conditional<F8, v4f, v4i>::type;
+    constexpr float kQmax = F8 ? 448.f : 127.f;
     __shared__ __align__(16) BwdStage<BQ, D, DPI8> st[2];
     using Stage = BwdStage<BQ, D, DPI8>;
     static_assert(offsetof(Stage, dot) == BQ * D && offsetof(Stage, dor) == 2 * BQ * D, "stage layout");
@@ -195,6 +199,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
         dkt[db] = v4f{0, 0, 0, 0};
     }
     const v4i magic4 = v4i{kMagicBits, kMagicBits, kMagicBits, kMagicBits};
+    const v4f zero4 = v4f{0.f, 0.f, 0.f, 0.f};
 
     const size_t tph = tiles_per_head<BQ, CAUSAL>(Tm, Tn);
     const int istart = CAUSAL ? (2 * jj * 64) / BQ : 0;
@@ -245,8 +250,8 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
             asm volatile("" ::: "memory");
             pmax = fmaxf(fmaxf(red[kb][0][0], red[kb][0][1]), fmaxf(red[kb][0][2], red[kb][0][3]));
             dsmax = fmaxf(fmaxf(red[kb][1][0], red[kb][1][1]), fmaxf(red[kb][1][2], red[kb][1][3]));
-            sP = __fdiv_rn(pmax, 127.f);
-            sS = __fdiv_rn(dsmax, 127.f);
+            sP = __fdiv_rn(pmax, kQmax);
+            sS = __fdiv_rn(dsmax, kQmax);
         };
         {
             float p[MB][4], ds[MB][4];
@@ -256,7 +261,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
             if (QSMOOTH) bias2 = (float)((double)biasv * kLog2e_d);
             // ---- S and dP for this wave's 16 keys and all BQ queries, one
             // 16-query block ahead of the vector work on the previous block
-            v4i s[MB];
+            Acc s[MB];
             // dP in float32 from 16-bit operands, or with dp_int8 as an INT8
             // product with dP = f32(sum) * f32(s_dO * s_V) (one rounding)
             using DpT = typename std::conditional<DPI8, v4i, v4f>::type;
@@ -283,8 +288,13 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
                 o.nd = *reinterpret_cast<const v4f*>(&cur.ndelta[16 * mb + 4 * g]);
             };
             auto mfma_block = [&](int mb, const OpsA& o) __attribute__((always_inline)) {
+                if constexpr (F8) {
+                    if constexpr (KS8 == 2) s[mb] = mfma16_f8x128(o.q[0], o.q[1], kop[0], kop[1], zero4);
+                    else s[mb] = mfma16_f8x64(o.q[0], kop[0], zero4);
+                } else {
 #pragma unroll
-                for (int ks = 0; ks < KS8; ++ks) s[mb] = mfma16_i8(o.q[ks], kop[ks], ks == 0 ? magic4 : s[mb]);
+                    for (int ks = 0; ks < KS8; ++ks) s[mb] = mfma16_i8(o.q[ks], kop[ks], ks == 0 ? magic4 : s[mb]);
+                }
 #pragma unroll
                 for (int ks = 0; ks < KSV; ++ks) {
                     // 16-bit dP accumulates onto -delta: the product yields dP - delta
@@ -303,7 +313,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
                 const v4f l2 = *reinterpret_cast<const v4f*>(&cur.l2[16 * mb + 4 * g]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    float x = fmaf(unmagic(s[mb][r]), c2, -l2[r]);
+                    float x = fmaf(acc_value(s[mb][r]), c2, -l2[r]);
                     if (QSMOOTH) x += bias2;
                     const float pv = __builtin_amdgcn_exp2f(x);
                     // dP - delta (16-bit dP already holds it; the INT8 one is scaled here)
@@ -344,13 +354,23 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
                 float pc[4], sc[4];
+                if constexpr (F8) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    pc[r] = fmaf(p[mb][r], invP, kMagic);  // rint(P / s_P) in the low byte
-                    sc[r] = fmaf(ds[mb][r], invS, kMagic);
+                    for (int r = 0; r < 4; ++r) {
+                        pc[r] = p[mb][r] * invP;
+                        sc[r] = ds[mb][r] * invS;
+                    }
+                    pop[mb >> 2][mb & 3] = pack_e4m3(pc[0], pc[1], pc[2], pc[3]);
+                    dsop[mb >> 2][mb & 3] = pack_e4m3(sc[0], sc[1], sc[2], sc[3]);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        pc[r] = fmaf(p[mb][r], invP, kMagic);  // rint(P / s_P) in the low byte
+                        sc[r] = fmaf(ds[mb][r], invS, kMagic);
+                    }
+                    pop[mb >> 2][mb & 3] = pack_magic(pc[0], pc[1], pc[2], pc[3]);
+                    dsop[mb >> 2][mb & 3] = pack_magic(sc[0], sc[1], sc[2], sc[3]);
                 }
-                pop[mb >> 2][mb & 3] = pack_magic(pc[0], pc[1], pc[2], pc[3]);
-                dsop[mb >> 2][mb & 3] = pack_magic(sc[0], sc[1], sc[2], sc[3]);
             }
             // ---- dS codes and scale to the workspace (key-major, swizzled)
             const size_t t = (size_t)bh * tph + tile_index<BQ, CAUSAL>(i, j, Tn);
@@ -384,18 +404,31 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
             const float fv = sP * sdoi;
             const float fk = sS * sqi;
             const int kk = n16 >> 1, hf = n16 & 1;
-            v4i accv[DB], acck[DB];
+            Acc accv[DB], acck[DB];
             auto mfma_db = [&](int db) __attribute__((always_inline)) {
+                v4i av[KQ], ak[KQ];
 #pragma unroll
                 for (int kq = 0; kq < KQ; ++kq) {
-                    const v4i av = reinterpret_cast<const v4i*>(cur.dot)[kq * 4 * D + g * D + 16 * db + n16];
+                    av[kq] = reinterpret_cast<const v4i*>(cur.dot)[kq * 4 * D + g * D + 16 * db + n16];
                     // Q^ transposed: rows = d (lane), k = queries 64 kq + 16 (e/4) + 4 g + e%4
                     const int qa = 64 * kq + 16 * (kk >> 2) + 4 * g + (kk & 3);
                     const v2i r1 = lds_read_tr8(cur.q + off_r32(qa, 16 * db, D) + 8 * hf);
                     const v2i r2 = lds_read_tr8(cur.q + off_r32(qa + 32, 16 * db, D) + 8 * hf);
-                    const v4i ak = v4i{r1[0], r1[1], r2[0], r2[1]};
-                    accv[db] = mfma16_i8(av, pop[kq], kq == 0 ? magic4 : accv[db]);
-                    acck[db] = mfma16_i8(ak, dsop[kq], kq == 0 ? magic4 : acck[db]);
+                    ak[kq] = v4i{r1[0], r1[1], r2[0], r2[1]};
+                    if constexpr (!F8) {
+                        accv[db] = mfma16_i8(av[kq], pop[kq], kq == 0 ? magic4 : accv[db]);
+                        acck[db] = mfma16_i8(ak[kq], dsop[kq], kq == 0 ? magic4 : acck[db]);
+                    }
+                }
+                if constexpr (F8) {
+                    // both 64-query chunks in one 16x16x128 product (bq = 128)
+                    if constexpr (KQ == 2) {
+                        accv[db] = mfma16_f8x128(av[0], av[1], pop[0], pop[1], zero4);
+                        acck[db] = mfma16_f8x128(ak[0], ak[1], dsop[0], dsop[1], zero4);
+                    } else {
+                        accv[db] = mfma16_f8x64(av[0], pop[0], zero4);
+                        acck[db] = mfma16_f8x64(ak[0], dsop[0], zero4);
+                    }
                 }
             };
             // one d-block of products ahead of the accumulation of the previous
@@ -405,8 +438,8 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
                 if (db + 1 < DB) mfma_db(db + 1);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    dvt[db][r] = fmaf(unmagic(accv[db][r]), fv, dvt[db][r]);
-                    dkt[db][r] = fmaf(unmagic(acck[db][r]), fk, dkt[db][r]);
+                    dvt[db][r] = fmaf(acc_value(accv[db][r]), fv, dvt[db][r]);
+                    dkt[db][r] = fmaf(acc_value(acck[db][r]), fk, dkt[db][r]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -468,7 +501,7 @@ struct DqStage {
     int8_t k[64 * D];     // K codes of the key block, C64N
 };
 
-template <int D, int BQ, bool CAUSAL>
+template <int D, int BQ, bool CAUSAL, bool F8>
 __global__ __launch_bounds__(256, 2) void dq_kernel(const int8_t* __restrict__ dsw, const float* __restrict__ sds,
                                                    const int8_t* __restrict__ kt, const float* __restrict__ sk,
                                                    float* __restrict__ dQ, int N, int BH, double scale) {
@@ -547,9 +580,15 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const int8_t* __restrict__ d
             const v4i bv = lk[g * D + 16 * nb + n16];   // K^ C64N: column d, k = key 16 g + e
 #pragma unroll
             for (int mb = 0; mb < MBq; ++mb) {
-                const v4i x = mfma16_i8(av[mb], bv, magic4);
+                if constexpr (F8) {
+                    const v4f x = mfma16_f8x64(av[mb], bv, v4f{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[mb][nb][r] = fmaf(unmagic(x[r]), cj, acc[mb][nb][r]);
+                    for (int r = 0; r < 4; ++r) acc[mb][nb][r] = fmaf(x[r], cj, acc[mb][nb][r]);
+                } else {
+                    const v4i x = mfma16_i8(av[mb], bv, magic4);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[mb][nb][r] = fmaf(unmagic(x[r]), cj, acc[mb][nb][r]);
+                }
             }
         }
         wait_vmem();       // the asynchronous copies are not seen by the compiler's waits
@@ -587,14 +626,16 @@ hipError_t bwd_dispatch(const Dims& d, const BwdPtrs& p, hipStream_t s) {
     const sage_qtensors& qk = *p.qk;
     const sage_dotensors& dos = *p.dos;
     const dim3 grid(((d.Tn() + 1) / 2) * d.BH());
-    auto kern = d.dp_int8 ? (d.q_smooth ? bwd_kernel<BF16, D, BQ, CAUSAL, true, true>
-                                        : bwd_kernel<BF16, D, BQ, CAUSAL, false, true>)
-                          : (d.q_smooth ? bwd_kernel<BF16, D, BQ, CAUSAL, true, false>
-                                        : bwd_kernel<BF16, D, BQ, CAUSAL, false, false>);
+    auto kern = d.fp8       ? (d.q_smooth ? bwd_kernel<BF16, D, BQ, CAUSAL, true, false, true>
+                                          : bwd_kernel<BF16, D, BQ, CAUSAL, false, false, true>)
+                : d.dp_int8 ? (d.q_smooth ? bwd_kernel<BF16, D, BQ, CAUSAL, true, true, false>
+                                          : bwd_kernel<BF16, D, BQ, CAUSAL, false, true, false>)
+                            : (d.q_smooth ? bwd_kernel<BF16, D, BQ, CAUSAL, true, false, false>
+                                          : bwd_kernel<BF16, D, BQ, CAUSAL, false, false, false>);
     kern<<<grid, 512, 0, s>>>(qk.q, qk.sq, qk.k, qk.sk, qk.vr, qk.sv, qk.mu_q, qk.qk_bias, dos.delta, dos.dot,
                               dos.sdo, dos.dor, p.L, p.dsw, p.sds, p.dK, p.dV, d.N, d.BH(), d.scale);
-    dq_kernel<D, BQ, CAUSAL><<<dim3(d.Tm() * d.BH()), 256, 0, s>>>(p.dsw, p.sds, qk.kt, qk.sk, p.dQ, d.N, d.BH(),
-                                                                   d.scale);
+    auto dq = d.fp8 ? dq_kernel<D, BQ, CAUSAL, true> : dq_kernel<D, BQ, CAUSAL, false>;
+    dq<<<dim3(d.Tm() * d.BH()), 256, 0, s>>>(p.dsw, p.sds, qk.kt, qk.sk, p.dQ, d.N, d.BH(), d.scale);
     return hipGetLastError();
 }
 

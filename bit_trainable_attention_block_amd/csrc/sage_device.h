@@ -25,6 +25,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr double kLog2e_d = 1.4426950408889634074;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLog2_127 = 6.988684686772166f;  // log2(127)
+constexpr float kLog2_448 = 8.807354922057604f;  // log2(448), the largest E4M3 value
 
 // ---------------------------------------------------------------- dtypes
 template <bool BF16>
@@ -220,6 +221,34 @@ __device__ __forceinline__ float unmagic(int x) { return __int_as_float(x) - kMa
 
 __device__ __forceinline__ v4i mfma16_i8(v4i a, v4i b, v4i c) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+// E4M3 products with float32 accumulation, on the same 16-byte operand chunks
+// (lane group g, byte e) as the INT8 product.  v_mfma_f32_16x16x32_fp8_fp8
+// contracts 8 bytes per lane, so two of them cover a chunk (bytes 0-7, then
+// 8-15).  v_mfma_f32_16x16x128_f8f6f4 (format 0 = E4M3 for both operands, no
+// block scale) contracts 32 bytes per lane: two chunks at once.  In both, A
+// and B pair the same (g, byte) positions, which is all a contraction needs.
+typedef int v8i __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ v4f mfma16_f8x64(v4i a, v4i b, v4f c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(__builtin_bit_cast(long, v2i{a[0], a[1]}),
+                                                   __builtin_bit_cast(long, v2i{b[0], b[1]}), c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(__builtin_bit_cast(long, v2i{a[2], a[3]}),
+                                                      __builtin_bit_cast(long, v2i{b[2], b[3]}), c, 0, 0, 0);
+}
+__device__ __forceinline__ v4f mfma16_f8x128(v4i a0, v4i a1, v4i b0, v4i b1, v4f c) {
+    const v8i a = v8i{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+    const v8i b = v8i{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+// Float value of one accumulator element: INT8 (magic-started int32) or E4M3
+// (float32).
+__device__ __forceinline__ float acc_value(int x) { return unmagic(x); }
+__device__ __forceinline__ float acc_value(float x) { return x; }
+// Four E4M3 codes (nearest value, ties to even) packed into bytes 0..3.
+__device__ __forceinline__ int pack_e4m3(float a, float b, float c, float d) {
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 template <bool BF16>
 __device__ __forceinline__ v4f mfma16_h(v4i a, v4i b, v4f c) {

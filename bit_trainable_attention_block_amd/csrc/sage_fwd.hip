@@ -86,7 +86,8 @@ struct FwdStage {
 // and a row with no visible key in the tile keeps a finite maximum.
 constexpr int kMaskedSum = kMagicBits - (1 << 22) + 1;
 
-template <bool BF16, int D, bool CAUSAL, bool QSMOOTH, bool PSTATIC>
+// F8: the E4M3 variant (codes E4M3, 448 in place of 127, float32 products).
+template <bool BF16, int D, bool CAUSAL, bool QSMOOTH, bool PSTATIC, bool F8>
 __global__ __launch_bounds__(64 * kWaves, 2) void fwd_kernel(
     const int8_t* __restrict__ q, const float* __restrict__ sq, const int8_t* __restrict__ k,
     const float* __restrict__ sk, const int8_t* __restrict__ vt, const float* __restrict__ sv,
@@ -97,6 +98,9 @@ __global__ __launch_bounds__(64 * kWaves, 2) void fwd_kernel(
     constexpr int DB = D / 16;               // 16-row blocks of d (O^T)
     constexpr int NT = 64 * kWaves;
     static_assert(TILE_BYTES % 1024 == 0, "stage shape");
+    static_assert(!(F8 && PSTATIC), "the static P scale is an INT8 ablation");
+    using Acc = typename std::conditional<F8, v4f, v4i>::type;
+    constexpr float kLog2Qmax = F8 ? kLog2_448 : kLog2_127;
     __shared__ __align__(16) FwdStage<D> st[2];
 
     const int Tn = N / kKTile;
@@ -153,6 +157,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void fwd_kernel(
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] = v4f{0, 0, 0, 0};
     const v4i magic4 = v4i{kMagicBits, kMagicBits, kMagicBits, kMagicBits};
+    const v4f zero4 = v4f{0.f, 0.f, 0.f, 0.f};
 
     // asynchronous copy of key tile j (K and V codes: two contiguous runs;
     // with Q-smoothing also the tile's 64 bias values of each Q block)
@@ -195,20 +200,27 @@ __global__ __launch_bounds__(64 * kWaves, 2) void fwd_kernel(
         if (wave_on) {
             const v4i* lv = reinterpret_cast<const v4i*>(cur.v);
             // S^T for the four 16-key blocks of the tile
-            v4i s[4];
+            Acc s[4];
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
+                v4i av[KS];
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const v4i av = *reinterpret_cast<const v4i*>(cur.k + off_r32(16 * kb + n, 64 * ks + 16 * g, D));
-                    s[kb] = mfma16_i8(av, qop[ks], ks == 0 ? magic4 : s[kb]);
+                for (int ks = 0; ks < KS; ++ks)
+                    av[ks] = *reinterpret_cast<const v4i*>(cur.k + off_r32(16 * kb + n, 64 * ks + 16 * g, D));
+                if constexpr (F8) {
+                    // d = 128: both chunks in one 16x16x128 product
+                    if constexpr (KS == 2) s[kb] = mfma16_f8x128(av[0], av[1], qop[0], qop[1], zero4);
+                    else s[kb] = mfma16_f8x64(av[0], qop[0], zero4);
+                } else {
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) s[kb] = mfma16_i8(av[ks], qop[ks], ks == 0 ? magic4 : s[kb]);
                 }
             }
             // one rounding from the exact product of the scales (keeps the
             // logits within an ulp of the definition)
             const float c2 = (float)((double)sqv * (double)sk[(size_t)bh * Tn + j] * scale2);
             float rm, sum;
-            v4i pc;
+            v4i pc;   // P codes: byte r of dword kb = key 16 kb + 4 g + r
             auto codes = [&](auto mask_tag) __attribute__((always_inline)) {
                 constexpr bool MASK = decltype(mask_tag)::value;
                 // Row maximum of this tile (log2 units).  Without Q-smoothing the
@@ -226,11 +238,23 @@ __global__ __launch_bounds__(64 * kWaves, 2) void fwd_kernel(
                         for (int r = 0; r < 4; ++r) {
                             const int key = k0 + 16 * kb + 4 * g + r;
                             bias2[kb][r] = (float)((double)b4[r] * kLog2e_d);
-                            const float v = fmaf(unmagic(s[kb][r]), c2, bias2[kb][r]);
+                            const float v = fmaf(acc_value(s[kb][r]), c2, bias2[kb][r]);
                             if (!(MASK && key > query)) rm = fmaxf(rm, v);
                         }
                     }
                     rm = qmax4(rm);
+                } else if constexpr (F8) {
+                    // float sums: their maximum, times the positive scale.  Every
+                    // row of a wave that reaches here sees key k0 (k0 <= q0).
+                    float fm = -INFINITY;
+#pragma unroll
+                    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int key = k0 + 16 * kb + 4 * g + r;
+                            if (!(MASK && key > query)) fm = fmaxf(fm, s[kb][r]);
+                        }
+                    rm = qmax4(fm) * c2;
                 } else {
                     int im = kMaskedSum;
 #pragma unroll
@@ -244,25 +268,28 @@ __global__ __launch_bounds__(64 * kWaves, 2) void fwd_kernel(
                 }
                 // codes against the tile maximum (per token), or with the
                 // static scale against the exact running maximum
-                const float shift = (PSTATIC ? fmaxf(m, rm) : rm) - kLog2_127;
+                const float shift = (PSTATIC ? fmaxf(m, rm) : rm) - kLog2Qmax;
                 sum = 0.f;
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) {
                     uint32_t word = 0u;
+                    float ev[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        float x = QSMOOTH ? fmaf(unmagic(s[kb][r]), c2, bias2[kb][r] - shift)
-                                          : fmaf(unmagic(s[kb][r]), c2, -shift);
+                        float x = QSMOOTH ? fmaf(acc_value(s[kb][r]), c2, bias2[kb][r] - shift)
+                                          : fmaf(acc_value(s[kb][r]), c2, -shift);
                         if (MASK) {
                             const int key = k0 + 16 * kb + 4 * g + r;
                             if (key > query) x = -INFINITY;
                         }
-                        const float e = __builtin_amdgcn_exp2f(x);  // 127 * 2^(x - rm), in [0, 127]
+                        // 127 * 2^(x - rm), in [0, 127] (E4M3: 448 and [0, 448])
+                        const float e = __builtin_amdgcn_exp2f(x);
                         sum += e;
+                        ev[r] = e;
                         // byte r of the word = rint(e) (round to nearest even)
-                        word = __builtin_amdgcn_cvt_pk_u8_f32(e, r, word);
+                        if constexpr (!F8) word = __builtin_amdgcn_cvt_pk_u8_f32(e, r, word);
                     }
-                    pc[kb] = (int)word;
+                    pc[kb] = F8 ? pack_e4m3(ev[0], ev[1], ev[2], ev[3]) : (int)word;
                 }
                 sum = qsum4(sum);
             };
@@ -276,8 +303,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void fwd_kernel(
             // factor do, and those use it consistently.
             // (static scale: the exact running maximum, s_P = 1/127)
             const float m_new = PSTATIC ? fmaxf(m, rm) : ((rm > m + kLazy) ? rm : m);
-            // 127 s_P: l and O both carry the factor 127, which cancels in O / l
-            // and is taken out of L at the end
+            // 127 s_P (E4M3: 448 s_P): l and O both carry the factor, which
+            // cancels in O / l and is taken out of L at the end
             const float sP = PSTATIC ? 1.f : __builtin_amdgcn_exp2f(rm - m_new);
             if (__builtin_expect(__any(m_new != m), 0)) {
                 // rare: a row's reference maximum moved; rescale l and O
@@ -291,13 +318,16 @@ __global__ __launch_bounds__(64 * kWaves, 2) void fwd_kernel(
             const float beta = sP * sv[(size_t)bh * Tn + j];
             // O^T += V^^T P^^T: one product per 16 rows of d, the 64 keys of the
             // tile as the contraction (V codes C64P, P codes from registers)
-            v4i acc[DB];
+            Acc acc[DB];
 #pragma unroll
-            for (int db = 0; db < DB; ++db) acc[db] = mfma16_i8(lv[g * D + 16 * db + n], pc, magic4);
+            for (int db = 0; db < DB; ++db) {
+                if constexpr (F8) acc[db] = mfma16_f8x64(lv[g * D + 16 * db + n], pc, zero4);
+                else acc[db] = mfma16_i8(lv[g * D + 16 * db + n], pc, magic4);
+            }
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) o[db][r] = fmaf(unmagic(acc[db][r]), beta, o[db][r]);
+                for (int r = 0; r < 4; ++r) o[db][r] = fmaf(acc_value(acc[db][r]), beta, o[db][r]);
         }
         wait_vmem();       // the next tile has landed
         __syncthreads();   // ... for every wave; this stage may be overwritten
@@ -316,7 +346,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void fwd_kernel(
             pk.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
             *reinterpret_cast<uint2*>(O + 16 * db + 4 * g) = pk;
         }
-        if (g == 0) L[(size_t)bh * N + query] = (m + (log2f(l) - kLog2_127)) * kLn2;
+        if (g == 0) L[(size_t)bh * N + query] = (m + (log2f(l) - kLog2Qmax)) * kLn2;
     }
 }
 
@@ -325,9 +355,10 @@ hipError_t fwd_dispatch(const Dims& d, const FwdArgs& a, hipStream_t s) {
     const dim3 grid(((d.N + kQTile - 1) / kQTile) * d.BH());
     const dim3 block(64 * kWaves);
 #define SAGE_FWD_ARGS a.q, a.sq, a.k, a.sk, a.vt, a.sv, a.qk_bias, a.O, a.L, a.N, a.bq, a.scale2
-#define SAGE_FWD(C, QS)                                                                     \
-    (d.p_static ? fwd_kernel<BF16, D, C, QS, true><<<grid, block, 0, s>>>(SAGE_FWD_ARGS)   \
-                : fwd_kernel<BF16, D, C, QS, false><<<grid, block, 0, s>>>(SAGE_FWD_ARGS))
+#define SAGE_FWD(C, QS)                                                                            \
+    (d.fp8        ? fwd_kernel<BF16, D, C, QS, false, true><<<grid, block, 0, s>>>(SAGE_FWD_ARGS)  \
+     : d.p_static ? fwd_kernel<BF16, D, C, QS, true, false><<<grid, block, 0, s>>>(SAGE_FWD_ARGS)  \
+                  : fwd_kernel<BF16, D, C, QS, false, false><<<grid, block, 0, s>>>(SAGE_FWD_ARGS))
     if (d.causal) {
         if (d.q_smooth) SAGE_FWD(true, true);
         else SAGE_FWD(true, false);

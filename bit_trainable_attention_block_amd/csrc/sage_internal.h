@@ -16,6 +16,7 @@ struct Dims {
     bool dp_int8;  // ablation: dP from the INT8 codes of dO and V
     bool p_static; // ablation: static forward P scale 1/127
     bool qk_norm;  // QK-norm fused into the preprocessing
+    bool fp8;      // variant: E4M3 codes, 448 in place of 127
     double scale;  // softmax scale; 1/sqrt(D) in double unless given
     int BH() const { return B * H; }
     int Tm() const { return N / bq; }

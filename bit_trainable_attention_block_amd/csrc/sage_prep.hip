@@ -11,7 +11,9 @@
 //
 // Codes and scales must equal the definition bit for bit:
 //   s = f32(max|x| / 127) with a correctly rounded division, and
-//   code = clamp(rint(f32(x / s)), -127, 127), ties to even.
+//   code = clamp(rint(f32(x / s)), -127, 127), ties to even;
+// in the E4M3 variant s = f32(max|x| / 448) and the code is the nearest E4M3
+// value of f32(x / s), ties to even (v_cvt_pk_fp8_f32 rounds that way).
 // Hence __fdiv_rn / __fsub_rn and no fast-math anywhere in this file.
 #include "sage_device.h"
 #include "sage_internal.h"
@@ -110,23 +112,34 @@ __device__ __forceinline__ void rms_normalize(BlockVals<R, D>& x, float* __restr
     }
 }
 
+// Largest code magnitude: INT8 or E4M3.
+__device__ __forceinline__ float qmax_of(int fp8) { return fp8 ? 448.f : 127.f; }
+
 // Quantise x (values of the block held per thread) with scale s and store
-// the codes row-major into LDS codes[R][D].
+// the codes (INT8, or E4M3 bytes) row-major into LDS codes[R][D].
 template <int R, int D>
 __device__ __forceinline__ void codes_to_lds(const float (&x)[Blk<R, D>::PER_T][8], float s,
-                                             uint8_t* codes) {
+                                             uint8_t* codes, int fp8) {
     using B = Blk<R, D>;
     const int t = threadIdx.x;
     const int cc = t % B::CPR;
 #pragma unroll
     for (int k = 0; k < B::PER_T; ++k) {
         int row = t / B::CPR + k * B::RSTEP;
-        int c[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) c[e] = s > 0.f ? code_i8(__fdiv_rn(x[k][e], s)) : 0;
         uint2 w;
-        w.x = pack4(c[0], c[1], c[2], c[3]);
-        w.y = pack4(c[4], c[5], c[6], c[7]);
+        if (fp8) {
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = s > 0.f ? __fdiv_rn(x[k][e], s) : 0.f;
+            w.x = (uint32_t)pack_e4m3(v[0], v[1], v[2], v[3]);
+            w.y = (uint32_t)pack_e4m3(v[4], v[5], v[6], v[7]);
+        } else {
+            int c[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) c[e] = s > 0.f ? code_i8(__fdiv_rn(x[k][e], s)) : 0;
+            w.x = pack4(c[0], c[1], c[2], c[3]);
+            w.y = pack4(c[4], c[5], c[6], c[7]);
+        }
         *reinterpret_cast<uint2*>(codes + row * D + cc * 8) = w;
     }
 }
@@ -203,7 +216,7 @@ template <bool BF16, int D>
 __global__ __launch_bounds__(kThreads) void quant_v_ksum_kernel(
     const u16* __restrict__ K, const u16* __restrict__ V, int N, int8_t* __restrict__ vt,
     float* __restrict__ sv, u16* __restrict__ vr, double* __restrict__ ws, int k_smooth, int dp_int8,
-    int qk_norm) {
+    int qk_norm, int fp8) {
     constexpr int R = 64;
     using B = Blk<R, D>;
     __shared__ float red[4];
@@ -226,8 +239,8 @@ __global__ __launch_bounds__(kThreads) void quant_v_ksum_kernel(
     }
     if (!dp_int8) store_r16h<R, D>(raw, vr + head, row0);
     const float a = block_max(m, red);
-    const float s = __fdiv_rn(a, 127.f);
-    codes_to_lds<R, D>(x, s, codes);
+    const float s = __fdiv_rn(a, qmax_of(fp8));
+    codes_to_lds<R, D>(x, s, codes, fp8);
     if (threadIdx.x == 0) sv[(size_t)bh * (N / R) + j] = s;
     __syncthreads();
     store_codes<C64P, R, D>(codes, vt + head + (size_t)row0 * D);
@@ -256,7 +269,7 @@ __global__ __launch_bounds__(kThreads) void quant_q_kernel(const u16* __restrict
                                                            int8_t* __restrict__ qt,
                                                            float* __restrict__ sq,
                                                            float* __restrict__ mu_q,
-                                                           float* __restrict__ rq) {
+                                                           float* __restrict__ rq, int fp8) {
     using B = Blk<BQ, D>;
     __shared__ float red[4];
     __shared__ __align__(16) uint8_t codes[BQ * D];
@@ -300,8 +313,8 @@ __global__ __launch_bounds__(kThreads) void quant_q_kernel(const u16* __restrict
 #pragma unroll
         for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[k][e]));
     const float a = block_max(m, red);
-    const float s = __fdiv_rn(a, 127.f);
-    codes_to_lds<BQ, D>(x, s, codes);
+    const float s = __fdiv_rn(a, qmax_of(fp8));
+    codes_to_lds<BQ, D>(x, s, codes, fp8);
     if (threadIdx.x == 0) sq[(size_t)bh * Tm + i] = s;
     __syncthreads();
     store_codes<R32, BQ, D>(codes, q + head + (size_t)row0 * D);
@@ -316,7 +329,8 @@ template <bool BF16, int D>
 __global__ __launch_bounds__(kThreads) void quant_k_kernel(
     const u16* __restrict__ K, int N, int8_t* __restrict__ k, int8_t* __restrict__ kt,
     float* __restrict__ sk, float* __restrict__ mu_k, const double* __restrict__ ws, int k_smooth,
-    const float* __restrict__ mu_q, float* __restrict__ qk_bias, int Tm, double scale, float* __restrict__ rk) {
+    const float* __restrict__ mu_q, float* __restrict__ qk_bias, int Tm, double scale, float* __restrict__ rk,
+    int fp8) {
     constexpr int R = 64;
     using B = Blk<R, D>;
     __shared__ float red[4];
@@ -354,8 +368,8 @@ __global__ __launch_bounds__(kThreads) void quant_k_kernel(
         }
     }
     const float a = block_max(m, red);
-    const float s = __fdiv_rn(a, 127.f);
-    codes_to_lds<R, D>(x, s, codes);
+    const float s = __fdiv_rn(a, qmax_of(fp8));
+    codes_to_lds<R, D>(x, s, codes, fp8);
     if (threadIdx.x == 0) sk[(size_t)bh * (N / R) + j] = s;
     if (qk_bias != nullptr) {
 #pragma unroll
@@ -390,7 +404,7 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const u16* __restrict
                                                            float* __restrict__ delta,
                                                            int8_t* __restrict__ dot,
                                                            float* __restrict__ sdo,
-                                                           u16* __restrict__ dor, int dp_int8) {
+                                                           u16* __restrict__ dor, int dp_int8, int fp8) {
     using B = Blk<BQ, D>;
     __shared__ float red[4];
     __shared__ __align__(16) uint8_t codes[BQ * D];
@@ -422,8 +436,8 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const u16* __restrict
         if (cc == 0) delta[(size_t)bh * N + row0 + threadIdx.x / B::CPR + k * B::RSTEP] = (float)acc;
     }
     const float a = block_max(m, red);
-    const float s = __fdiv_rn(a, 127.f);
-    codes_to_lds<BQ, D>(x, s, codes);
+    const float s = __fdiv_rn(a, qmax_of(fp8));
+    codes_to_lds<BQ, D>(x, s, codes, fp8);
     if (threadIdx.x == 0) sdo[(size_t)bh * Tm + i] = s;
     __syncthreads();
     store_codes<C64P, BQ, D>(codes, dot + head + (size_t)row0 * D);
@@ -480,19 +494,19 @@ hipError_t quantize_impl(const Dims& d, const void* Q, const void* K, const void
     }
     quant_v_ksum_kernel<BF16, D><<<dim3(d.Tn(), BH), blk, 0, s>>>(
         (const u16*)K, (const u16*)V, d.N, out.vt, out.sv, out.vr, ws, d.k_smooth ? 1 : 0, d.dp_int8 ? 1 : 0,
-        d.qk_norm ? 1 : 0);
+        d.qk_norm ? 1 : 0, d.fp8 ? 1 : 0);
     if (d.bq == 128)
         quant_q_kernel<BF16, D, 128><<<dim3(d.Tm(), BH), blk, 0, s>>>((const u16*)Q, d.N, out.q, out.qt,
                                                                       out.sq, d.q_smooth ? out.mu_q : nullptr,
-                                                                      d.qk_norm ? out.rq : nullptr);
+                                                                      d.qk_norm ? out.rq : nullptr, d.fp8 ? 1 : 0);
     else
         quant_q_kernel<BF16, D, 64><<<dim3(d.Tm(), BH), blk, 0, s>>>((const u16*)Q, d.N, out.q, out.qt,
                                                                      out.sq, d.q_smooth ? out.mu_q : nullptr,
-                                                                     d.qk_norm ? out.rq : nullptr);
+                                                                     d.qk_norm ? out.rq : nullptr, d.fp8 ? 1 : 0);
     quant_k_kernel<BF16, D><<<dim3(d.Tn(), BH), blk, 0, s>>>(
         (const u16*)K, d.N, out.k, out.kt, out.sk, out.mu_k, ws, d.k_smooth ? 1 : 0,
         d.q_smooth ? out.mu_q : nullptr, d.q_smooth ? out.qk_bias : nullptr, d.Tm(), d.scale,
-        d.qk_norm ? out.rk : nullptr);
+        d.qk_norm ? out.rk : nullptr, d.fp8 ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -503,11 +517,11 @@ hipError_t bwd_pre_impl(const Dims& d, const void* O, const void* dO, const sage
     if (d.bq == 128)
         bwd_pre_kernel<BF16, D, 128><<<grid, kThreads, 0, s>>>((const u16*)O, (const u16*)dO, d.N,
                                                                out.delta, out.dot, out.sdo, out.dor,
-                                                               d.dp_int8 ? 1 : 0);
+                                                               d.dp_int8 ? 1 : 0, d.fp8 ? 1 : 0);
     else
         bwd_pre_kernel<BF16, D, 64><<<grid, kThreads, 0, s>>>((const u16*)O, (const u16*)dO, d.N,
                                                               out.delta, out.dot, out.sdo, out.dor,
-                                                              d.dp_int8 ? 1 : 0);
+                                                              d.dp_int8 ? 1 : 0, d.fp8 ? 1 : 0);
     return hipGetLastError();
 }
 

@@ -58,6 +58,7 @@ class Config:
     dp_int8: bool = False # ablation: dP from INT8 codes (the method keeps it 16-bit)
     p_static: bool = False  # ablation: static forward P scale 1/127 (the method: per token)
     qk_norm_fused: bool = False  # QK-norm applied by sage_quantize (not by the generator)
+    fp8: bool = False            # variant: E4M3 codes in place of INT8
 
     @property
     def sm_scale(self) -> float:
@@ -99,6 +100,8 @@ C3_DPINT8 = C3.replace(name="d128_n8k_causal_qknorm_dpint8", dp_int8=True)
 C3_PSTATIC = C3.replace(name="d128_n8k_causal_qknorm_pstatic", p_static=True)
 # ... and with raw inputs, QK-norm applied by sage_quantize instead of the generator
 C3_QKNORM_FUSED = C3.replace(name="d128_n8k_causal_qknorm_fused", qk_norm=False, qk_norm_fused=True)
+# E4M3 variant of the same workload (not the method)
+C3_FP8 = C3.replace(name="d128_n8k_causal_qknorm_fp8", fp8=True)
 
 ALL = {c.name: c for c in (C1, C2, C3, C5)}
 

@@ -98,6 +98,18 @@ typedef struct sage_shape {
                            r goes to rq / rk.  sage_bwd's dQ, dK are then
                            w.r.t. the normalised rows; sage_qk_norm_bwd turns
                            them into gradients w.r.t. the inputs. */
+    int32_t fp8;        /* 0 = the method: INT8 codes, s = max|X| / 127.
+                           1 = E4M3 variant (the SageAttention3 write-up's
+                           INT8-versus-FP8 training comparison): every code
+                           tensor (q, qt, k, kt, vt, dot and the dS workspace)
+                           holds E4M3 bytes (OCP: sign, 4 exponent bits with
+                           bias 7, 3 mantissa bits, largest finite 448), the
+                           scales use 448 in place of 127 (block s =
+                           f32(max|X| / 448), code = the nearest E4M3 value of
+                           f32(x / s), ties to even; forward P against 448),
+                           and the products accumulate in float32.  Not with
+                           dp_int8 or p_static (SAGE_EUNSUPPORTED).  All four
+                           calls must agree on it. */
 } sage_shape;
 /* Supported: D in {64, 128}; bq in {64, 128}; bkv = 64; N a multiple of bq
  * and of bkv (the pages define T_m = N / B_q blocks; a ragged block is

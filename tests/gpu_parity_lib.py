@@ -15,6 +15,21 @@ from oracle import fpa, metrics, sage
 # Floating-point bar for O, dQ, dK, dV against the oracle.
 REL_L2_MAX = 1e-3
 COS_MIN = 0.99999
+# The E4M3 variant's relative-L2 bar.  Its matrix instruction does not sum
+# exactly: on random E4M3 operands it is off by up to ~2^-14 of the largest
+# product (measured), where the INT8 one is exact.  The logits then differ
+# from the oracle's exact sums by ~1e-4 relative, and an E4M3 code whose exact
+# quotient lies that close to a rounding midpoint moves by one step, 1/8 of
+# its value (an INT8 step is 1/127 of the block maximum).  Each such move
+# shifts its output row by up to ~1%; they are rare, so they show in the
+# relative L2 (measured up to 2.2e-3) and barely in the cosine, which keeps
+# the method's bar.
+FP8_REL_L2_MAX = 5e-3
+
+
+def bar(cfg):
+    """(relative-L2 maximum, cosine minimum) of one call's outputs."""
+    return (FP8_REL_L2_MAX if getattr(cfg, "fp8", False) else REL_L2_MAX), COS_MIN
 
 
 OUT_DIR = os.environ.get("SAGE_PARITY_OUT", "gpurun_out")
@@ -83,6 +98,12 @@ def head_inputs(inputs, b, h):
     return [inputs[n]["f32"][b, h].astype(np.float64) for n in ("q", "k", "v", "do")]
 
 
+def code_bytes(codes, fp8):
+    """The bytes the GPU stores for the oracle's code values: INT8, or the
+    E4M3 encodings (as int8, the dtype the layouts unpack to)."""
+    return sage.e4m3_bits(codes).view(np.int8) if fp8 else codes.astype(np.int8)
+
+
 def check_quantize(cfg, inputs, g, b, h):
     """Bit-exact codes, scales and means of one head."""
     shp = sage.Shape.of(cfg)
@@ -91,11 +112,12 @@ def check_quantize(cfg, inputs, g, b, h):
     N, D = cfg.N, cfg.D
     qt = g["qt"]
     un = lambda name, kind: bd.unpack_codes(qt[name][b, h], kind, N, D)
-    np.testing.assert_array_equal(un("q", "R32"), qz.Qc.astype(np.int8))
-    np.testing.assert_array_equal(un("qt", "C64P"), qz.Qc.astype(np.int8))
-    np.testing.assert_array_equal(un("k", "R32"), qz.Kc.astype(np.int8))
-    np.testing.assert_array_equal(un("kt", "C64N"), qz.Kc.astype(np.int8))
-    np.testing.assert_array_equal(un("vt", "C64P"), qz.Vc.astype(np.int8))
+    f8 = shp.fp8
+    np.testing.assert_array_equal(un("q", "R32"), code_bytes(qz.Qc, f8))
+    np.testing.assert_array_equal(un("qt", "C64P"), code_bytes(qz.Qc, f8))
+    np.testing.assert_array_equal(un("k", "R32"), code_bytes(qz.Kc, f8))
+    np.testing.assert_array_equal(un("kt", "C64N"), code_bytes(qz.Kc, f8))
+    np.testing.assert_array_equal(un("vt", "C64P"), code_bytes(qz.Vc, f8))
     np.testing.assert_array_equal(qt["sq"][b, h], qz.sQ.astype(np.float32))
     np.testing.assert_array_equal(qt["sk"][b, h], qz.sK.astype(np.float32))
     np.testing.assert_array_equal(qt["sv"][b, h], qz.sV.astype(np.float32))
@@ -126,7 +148,7 @@ def check_bwd_pre(cfg, inputs, g, b, h):
     O = g["O"][b, h].astype(np.float64)
     delta, dOc, sdO = sage.backward_pre(O, dO, shp)
     dot = g["dot"]
-    np.testing.assert_array_equal(bd.unpack_codes(dot["dot"][b, h], "C64P", cfg.N, cfg.D), dOc.astype(np.int8))
+    np.testing.assert_array_equal(bd.unpack_codes(dot["dot"][b, h], "C64P", cfg.N, cfg.D), code_bytes(dOc, shp.fp8))
     np.testing.assert_array_equal(dot["sdo"][b, h], sdO.astype(np.float32))
     np.testing.assert_allclose(dot["delta"][b, h], delta, rtol=1e-6, atol=1e-6)
     if cfg.dp_int8:
@@ -152,7 +174,8 @@ def check_fwd(cfg, inputs, g, b, h, qz, q_blocks, log=None):
     shp = sage.Shape.of(cfg)
     O, L = sage.forward(qz, shp, q_blocks=q_blocks)
     rows = np.concatenate([np.arange(i * cfg.bq, (i + 1) * cfg.bq) for i in q_blocks])
-    close(f"O[{b},{h}]", g["O"][b, h][rows], O[rows], log=log)
+    rel, cmin = bar(cfg)
+    close(f"O[{b},{h}]", g["O"][b, h][rows], O[rows], rel_max=rel, cos_min=cmin, log=log)
     np.testing.assert_allclose(g["L"][b, h][rows], L[rows], rtol=2e-5, atol=2e-5)
     return O
 
@@ -167,9 +190,10 @@ def check_bwd(cfg, inputs, g, b, h, qz, kv_blocks, q_blocks, log=None):
     dQ, dK, dV = sage.backward(qz, V, dO, dOc, sdO, L, delta_gpu, shp, kv_blocks=kv_blocks, q_blocks=q_blocks)
     kr = np.concatenate([np.arange(j * cfg.bkv, (j + 1) * cfg.bkv) for j in kv_blocks])
     qr = np.concatenate([np.arange(i * cfg.bq, (i + 1) * cfg.bq) for i in q_blocks])
-    close(f"dK[{b},{h}]", g["dK"][b, h][kr], dK[kr], log=log)
-    close(f"dV[{b},{h}]", g["dV"][b, h][kr], dV[kr], log=log)
-    close(f"dQ[{b},{h}]", g["dQ"][b, h][qr], dQ[qr], log=log)
+    rel, cmin = bar(cfg)
+    close(f"dK[{b},{h}]", g["dK"][b, h][kr], dK[kr], rel_max=rel, cos_min=cmin, log=log)
+    close(f"dV[{b},{h}]", g["dV"][b, h][kr], dV[kr], rel_max=rel, cos_min=cmin, log=log)
+    close(f"dQ[{b},{h}]", g["dQ"][b, h][qr], dQ[qr], rel_max=rel, cos_min=cmin, log=log)
     return dQ, dK, dV
 
 
@@ -224,7 +248,8 @@ def report_vs_fpa(cfg, inputs, g, b, h, q_blocks, kv_blocks, ours):
 # the two sides' O land on different sides of a rounding boundary, delta =
 # rowsum(dO o O) moves by up to one 16-bit ulp of O times dO, which shifts a
 # whole row of dS and can move dS codes (the SageBwd pages note that forward
-# output error reaches the backward pass through delta).
+# output error reaches the backward pass through delta).  The E4M3 variant
+# takes twice it, for the reason given at FP8_REL_L2_MAX.
 CHAIN_REL_L2_MAX = 5e-3
 
 
@@ -244,4 +269,5 @@ def check_full_chain(cfg, inputs, g, log=None):
             r = sage.run_head(Q, K, V, dO, shp)
             names = ("O", "dQ", "dK", "dV") + (("dQ_in", "dK_in") if shp.qk_norm else ())
             for name in names:
-                close(f"chain_{name}[{b},{h}]", g[name][b, h], r[name], rel_max=CHAIN_REL_L2_MAX, log=log)
+                close(f"chain_{name}[{b},{h}]", g[name][b, h], r[name],
+                      rel_max=CHAIN_REL_L2_MAX * (2 if getattr(cfg, "fp8", False) else 1), log=log)

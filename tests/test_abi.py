@@ -39,14 +39,14 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_struct_layouts_match_header():
-    assert ctypes.sizeof(bd.c_shape) == 14 * 4
+    assert ctypes.sizeof(bd.c_shape) == 15 * 4
     assert ctypes.sizeof(bd.c_qtensors) == 14 * 8
     assert ctypes.sizeof(bd.c_dotensors) == 4 * 8
 
 
 def _shape(**kw):
     base = dict(B=1, H=2, N=256, D=128, bq=128, bkv=64, dtype=1, causal=0, k_smooth=1, q_smooth=0, sm_scale=0.0,
-                dp_int8=0, p_static=0, qk_norm=0)
+                dp_int8=0, p_static=0, qk_norm=0, fp8=0)
     base.update(kw)
     return bd.c_shape(**base)
 
@@ -80,6 +80,9 @@ BAD_SHAPES = [
     (dict(dp_int8=2), bd.SAGE_EINVAL),
     (dict(p_static=-1), bd.SAGE_EINVAL),
     (dict(qk_norm=3), bd.SAGE_EINVAL),
+    (dict(fp8=2), bd.SAGE_EINVAL),
+    (dict(fp8=1, dp_int8=1), bd.SAGE_EUNSUPPORTED),   # INT8-only ablations have no E4M3 form
+    (dict(fp8=1, p_static=1), bd.SAGE_EUNSUPPORTED),
     (dict(sm_scale=-1.0), bd.SAGE_EINVAL),
     (dict(sm_scale=float("nan")), bd.SAGE_EINVAL),
     (dict(B=70000, H=1), bd.SAGE_EUNSUPPORTED),

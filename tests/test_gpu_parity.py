@@ -53,6 +53,14 @@ SMALL = [
     small("n256_d128_causal_qknorm", 256, 128, 128, True, sigma=3.0).replace(qk_norm_fused=True),
     small("n192_d64_bq64_qsmooth_qknorm", 192, 64, 64, False, q_smooth=True, sigma=2.0).replace(qk_norm_fused=True),
     small("n256_d64_fp16_causal_qknorm", 256, 64, 128, True, dtype=wl.FP16).replace(qk_norm_fused=True),
+    # the E4M3 variant: d=128 (16x16x128 products) and d=64, bq 64 and 128,
+    # ragged, Q-smoothing, fp16, QK-norm
+    wl.C1.replace(name="tiny_fp8", fp8=True),
+    small("n256_d128_causal_fp8", 256, 128, 128, True).replace(fp8=True),
+    small("n192_d64_bq64_fp8", 192, 64, 64, False).replace(fp8=True),
+    small("n320_d128_bq64_causal_qsmooth_fp8", 320, 128, 64, True, q_smooth=True).replace(fp8=True),
+    small("n256_d64_fp16_causal_qknorm_fp8", 256, 64, 128, True, dtype=wl.FP16).replace(fp8=True,
+                                                                                        qk_norm_fused=True),
 ]
 
 
@@ -103,6 +111,7 @@ FULL = [
     (wl.C3_DPINT8, [(1, 3)]),
     (wl.C3_PSTATIC, [(0, 9)]),
     (wl.C3_QKNORM_FUSED, [(1, 11)]),
+    (wl.C3_FP8, [(0, 2)]),
 ]
 
 
