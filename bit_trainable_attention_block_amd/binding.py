@@ -63,6 +63,7 @@ SIGNATURES = {
     "sage_qk_norm_bwd": (ctypes.c_int, [ctypes.POINTER(c_shape), _P, _P, ctypes.POINTER(c_qtensors), _P, _P, _P]),
     # include/sage_probe.h (measurement aid)
     "sage_probe_mfma_i8": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _P, _P]),
+    "sage_probe_fp8_products": (ctypes.c_int, [_P, _P, _P, _P, _P]),
 }
 
 _lib = None
@@ -251,6 +252,14 @@ def probe_mfma_i8(blocks: int, iters: int, clk: torch.Tensor, stream=None):
     each wave issuing iters x 8 INT8 16x16x64 products; clk (3 int64 on the
     device) receives the shader cycles and 100 MHz ticks of workgroup 0."""
     _check(load().sage_probe_mfma_i8(blocks, iters, _ptr(clk), _stream(stream)), "sage_probe_mfma_i8")
+
+
+def probe_fp8_products(a, b, c32, c128, stream=None):
+    """Measurement aid (include/sage_probe.h): one wave of the two E4M3 matrix
+    products on a, b (64 x 32 bytes each, device) into c32, c128 (64 x 4
+    floats each, device)."""
+    _check(load().sage_probe_fp8_products(_ptr(a), _ptr(b), _ptr(c32), _ptr(c128), _stream(stream)),
+           "sage_probe_fp8_products")
 
 
 def run(sh: Shape, Q, K, V, dO, stream=None):

@@ -168,6 +168,11 @@ int sage_probe_mfma_i8(int blocks, int iters, unsigned long long* clk, hipStream
     return finish(sage::launch_probe_mfma_i8(blocks, iters, clk, stream));
 }
 
+int sage_probe_fp8_products(const int8_t* a, const int8_t* b, float* c32, float* c128, hipStream_t stream) {
+    if (!ptrs_ok(a, b, c32, c128)) return SAGE_EINVAL;
+    return finish(sage::launch_probe_fp8_products(a, b, c32, c128, stream));
+}
+
 const char* sage_version(void) { return "sage-mi355x 0.1 (gfx950)"; }
 
 }  // extern "C"

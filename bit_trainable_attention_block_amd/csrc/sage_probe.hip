@@ -1,5 +1,6 @@
-// Measurement aid: the achieved rate of the INT8 16x16x64 matrix product and
-// the shader clock under that load (declared in include/sage_probe.h).
+// Measurement aids (declared in include/sage_probe.h): the achieved rate of
+// the INT8 16x16x64 matrix product and the shader clock under that load; the
+// results of the two E4M3 matrix products on given operands.
 #include "sage_device.h"
 #include "sage_internal.h"
 
@@ -35,7 +36,28 @@ __global__ __launch_bounds__(512, 2) void probe_mfma_i8_kernel(int iters, unsign
     }
 }
 
+// One wave: lane l's 32 E4M3 bytes of a and b feed both E4M3 products, the
+// 16x16x32 one (the first 8 bytes) and the 16x16x128 one (all 32); lane l
+// writes its 4 result registers of each.
+__global__ __launch_bounds__(64) void probe_fp8_products_kernel(const v4i* __restrict__ a, const v4i* __restrict__ b,
+                                                                v4f* __restrict__ c32, v4f* __restrict__ c128) {
+    const int l = threadIdx.x;
+    const v4i a0 = a[2 * l], a1 = a[2 * l + 1], b0 = b[2 * l], b1 = b[2 * l + 1];
+    const v4f z = v4f{0.f, 0.f, 0.f, 0.f};
+    c32[l] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(__builtin_bit_cast(long, v2i{a0[0], a0[1]}),
+                                                        __builtin_bit_cast(long, v2i{b0[0], b0[1]}), z, 0, 0, 0);
+    c128[l] = mfma16_f8x128(a0, a1, b0, b1, z);
+}
+
 }  // namespace
+
+hipError_t launch_probe_fp8_products(const int8_t* a, const int8_t* b, float* c32, float* c128,
+                                     hipStream_t stream) {
+    probe_fp8_products_kernel<<<dim3(1), dim3(64), 0, stream>>>(
+        reinterpret_cast<const v4i*>(a), reinterpret_cast<const v4i*>(b), reinterpret_cast<v4f*>(c32),
+        reinterpret_cast<v4f*>(c128));
+    return hipGetLastError();
+}
 
 hipError_t launch_probe_mfma_i8(int blocks, int iters, unsigned long long* clk, hipStream_t stream) {
     probe_mfma_i8_kernel<<<dim3(blocks), dim3(512), 0, stream>>>(iters, clk);

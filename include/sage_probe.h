@@ -22,12 +22,31 @@
 #define SAGE_PROBE_H
 
 #include <hip/hip_runtime.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
 #endif
 
 int sage_probe_mfma_i8(int blocks, int iters, unsigned long long* clk, hipStream_t stream);
+
+/*
+ * sage_probe_fp8_products runs one wave of the two E4M3 matrix products the
+ * E4M3 variant uses (sage_shape.fp8), so that their lane layout and their
+ * summation can be checked against exact products:
+ *   a, b  device pointers, 64 * 32 bytes each (16-byte aligned): lane l's 32
+ *         E4M3 bytes at offset 32 l.  Lane l supplies row l % 16 of A and
+ *         column l % 16 of B; in v_mfma_f32_16x16x32_fp8_fp8 its first 8
+ *         bytes carry contraction indices 8 (l / 16) + e, and in
+ *         v_mfma_f32_16x16x128_f8f6f4 (E4M3, no block scale) all 32 bytes
+ *         carry 32 (l / 16) + e.
+ *   c32, c128  device pointers, 64 * 4 floats each: lane l's result
+ *         registers j = 0..3 (row 4 (l / 16) + j, column l % 16) of each
+ *         product, accumulated from zero.  Owned by the caller.
+ *   Returns 0, SAGE_EINVAL for a NULL or misaligned pointer (nothing
+ *   launched), or SAGE_EHIP.  Asynchronous on `stream`.
+ */
+int sage_probe_fp8_products(const int8_t* a, const int8_t* b, float* c32, float* c128, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -184,6 +184,13 @@ def test_probe_rejects_bad_arguments(lib):
         assert lib.sage_probe_mfma_i8(blocks, iters, ptr, None) == bd.SAGE_EINVAL
 
 
+def test_fp8_probe_rejects_bad_arguments(lib):
+    buf = (ctypes.c_uint8 * 8192)()
+    base = ctypes.addressof(buf) + (-ctypes.addressof(buf)) % 16
+    for a, b, c, d in ((None, base, base, base), (base, base + 4, base, base), (base, base, base, None)):
+        assert lib.sage_probe_fp8_products(a, b, c, d, None) == bd.SAGE_EINVAL
+
+
 def test_autograd_wrapper_rejects_cpu_tensors():
     """The training wrapper is argument marshalling only: on CPU tensors it
     raises before touching the library (there is no CPU fallback)."""
