@@ -194,6 +194,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the INT8-dP and E4M3 legs (profiler runs: only the method's kernels launch)")
     ap.add_argument("--traffic-from", default="",
                     help="summarise rocprofv3 FETCH_SIZE/WRITE_SIZE runs in this directory into "
                          "profiles/traffic.json (no GPU needed) and exit")
@@ -336,7 +338,8 @@ def main():
     # reported beside the headline, never as it: the INT8-dP ablation (dP
     # from the INT8 codes of dO and V) and the E4M3 variant (E4M3 codes and
     # float32 products in place of INT8)
-    for key, sw in (("ablation_dp_int8", {"dp_int8": True}), ("variant_fp8", {"fp8": True})):
+    variants = () if args.no_variants else (("ablation_dp_int8", {"dp_int8": True}), ("variant_fp8", {"fp8": True}))
+    for key, sw in variants:
         sha = dataclasses.replace(sh, **sw)
         ab_ms = []
         for k in range(args.warmup + max(3, args.steps // 4)):

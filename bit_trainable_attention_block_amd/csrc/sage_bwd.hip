@@ -32,8 +32,10 @@
 // dS workspace layout, per tile (BQ queries x 64 keys, BQ * 64 bytes): key
 // row kr (0..63) holds BQ bytes; query q = 16 mb + 4 g + r of the tile sits
 // at position p = (BQ/4) g + 4 mb + r, and the 16-byte chunk c of a row is
-// stored at chunk slot c ^ (kr mod BQ/16), which spreads the transpose reads
-// of eight consecutive rows over distinct LDS banks.
+// stored at chunk slot c ^ (kr mod BQ/16) ^ (bit 4 of kr).  A transpose read
+// takes eight consecutive rows in each lane group: the first term spreads
+// them over distinct LDS banks, the second gives rows 16 apart (the lane
+// groups served together) the other half of the slots.
 #include <algorithm>
 #include <cstddef>
 #include <type_traits>
@@ -85,6 +87,14 @@ __device__ __forceinline__ void xcd_coords(int units, int BH, int& unit, int& bh
     }
 }
 
+// Q codes in a backward stage: the R32 16-byte chunk at byte offset `off` is
+// stored at qswz(off), which flips chunk bit 3 where chunk bit 4 is set (bit
+// 4 of a chunk index is bit 4 of its row).  The transposed reads of the dK
+// product take rows r and r + 16 of a chunk column in lane groups that the
+// LDS serves together; unswizzled both rows land on the same banks.  The
+// row-major reads of the S product stay on 16 consecutive chunks.
+__device__ __forceinline__ int qswz(int off) { return off ^ (((off >> 8) & 1) << 7); }
+
 template <int BQ, int D, bool DPI8>
 struct BwdStage {
     int8_t q[BQ * D];     // Q codes, R32
@@ -95,7 +105,8 @@ struct BwdStage {
 };
 
 // Asynchronous copy of query tile qbase (Q codes, dO codes, dO) into the
-// stage at LDS address `lds`.  The three regions are contiguous BQ*D, BQ*D
+// stage at LDS address `lds`; the Q codes land swizzled (qswz), which the
+// copy does by reading lane l's chunk from qswz(16 l) (voff_q).  The three regions are contiguous BQ*D, BQ*D
 // and 2*BQ*D byte runs (BQ*D for the third with dp_int8), laid out in the
 // same order in the stage; each wave instruction moves 1 KiB, and round u of
 // the eight waves moves the stage's u-th 8 KiB.  When a region is a whole
@@ -103,12 +114,12 @@ struct BwdStage {
 // at compile time.  voff = 16 * lane.
 template <int BQ, int D, bool DPI8>
 __device__ __forceinline__ void stage_query_tile(unsigned lds, const int8_t* q, const int8_t* dot,
-                                                 const int8_t* dorb, int w, unsigned voff) {
+                                                 const int8_t* dorb, int w, unsigned voff, unsigned voff_q) {
     constexpr int QB = BQ * D, TOT = (DPI8 ? 3 : 4) * QB, R = 8 * 1024;
     constexpr int ROUNDS = (TOT + R - 1) / R, FULL = TOT / R;
     static_assert(QB % 1024 == 0, "stage shape");
     const int8_t* src[ROUNDS];
-    unsigned dst[ROUNDS];
+    unsigned dst[ROUNDS], vo[ROUNDS];
 #pragma unroll
     for (int u = 0; u < ROUNDS; ++u) {
         const int c0 = u * R + w * 1024;
@@ -116,15 +127,17 @@ __device__ __forceinline__ void stage_query_tile(unsigned lds, const int8_t* q, 
             constexpr int RQ = QB / R;   // rounds per 1-byte region
             const int off = (u % RQ) * R + w * 1024;
             src[u] = u < RQ ? q + off : u < 2 * RQ ? dot + off : dorb + (u - 2 * RQ) * R + w * 1024;
+            vo[u] = u < RQ ? voff_q : voff;
         } else {
             src[u] = c0 < QB ? q + c0 : c0 < 2 * QB ? dot + (c0 - QB) : dorb + (c0 - 2 * QB);
+            vo[u] = c0 < QB ? voff_q : voff;
         }
         dst[u] = lds + c0;
     }
-    copy16_rounds<FULL>(src, dst, voff);
+    copy16_rounds<FULL>(src, dst, vo);
     if constexpr (FULL < ROUNDS) {
         // the last round of a stage that is not a whole number of rounds
-        if (FULL * R + w * 1024 < TOT) copy16x1_to_lds(src[FULL], dst[FULL], voff);
+        if (FULL * R + w * 1024 < TOT) copy16x1_to_lds(src[FULL], dst[FULL], vo[FULL]);
     }
 }
 
@@ -161,7 +174,14 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int lane = tid & 63, n16 = lane & 15, g = lane >> 4;
-    const unsigned voff = 16u * lane;
+    const unsigned voff = 16u * lane, voff_q = (unsigned)qswz(16 * lane);
+    // this lane's Q chunk offsets in a stage (swizzled): the S product reads
+    // row 16 mb + n16, chunk column 4 ks + g, at qa_lane[mb & 1] + (mb / 2)
+    // 32 D + 2048 ks; the dK product's transposed reads take query row
+    // 64 kq + 16 (kk / 4) + 4 g + kk % 4 (+ 32), bytes 8 hf.., of chunk column
+    // db at tr_lane + 64 D kq (+ 32 D) + 512 db (kk = n16 / 2, hf = n16 % 2)
+    const int qa_lane[2] = {qswz(off_r32(n16, 16 * g, D)), qswz(off_r32(16 + n16, 16 * g, D))};
+    const int tr_lane = qswz((16 * ((n16 >> 1) >> 2) + 4 * g + ((n16 >> 1) & 3)) << 4) + 8 * (n16 & 1);
     const int kb = w >> 2, kg = w & 3;
     const int j = 2 * jj + kb;        // this wave's key block
     const bool kv_on = j < Tn;        // the second block of a ragged tail may not exist
@@ -201,6 +221,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
     const v4i magic4 = v4i{kMagicBits, kMagicBits, kMagicBits, kMagicBits};
     const v4f zero4 = v4f{0.f, 0.f, 0.f, 0.f};
 
+    const double skj_s2 = (double)skj * scale * kLog2e_d;   // s_K * scale * log2 e
     const size_t tph = tiles_per_head<BQ, CAUSAL>(Tm, Tn);
     const int istart = CAUSAL ? (2 * jj * 64) / BQ : 0;
     const float* Lh = L + (size_t)bh * N;
@@ -230,7 +251,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
         if (more)
             stage_query_tile<BQ, D, DPI8>(lds_addr(&nxt), qh + (size_t)(qbase + BQ) * D,
                                           doth + (size_t)(qbase + BQ) * D, dorh + (size_t)DOR_B * (qbase + BQ) * D,
-                                          w, voff);
+                                          w, voff, voff_q);
 
         // the tile exists and has a visible key (it is stored for the dQ pass)
         const bool tile_on = kv_on && (!CAUSAL || j * 64 <= qbase + BQ - 1);
@@ -256,7 +277,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
         {
             float p[MB][4], ds[MB][4];
             float pmax = 0.f, dsmax = 0.f;
-            const float c2 = (float)((double)sqi * (double)skj * scale * kLog2e_d);  // one rounding
+            const float c2 = (float)((double)sqi * skj_s2);  // one rounding from float64
             float bias2 = 0.f;
             if (QSMOOTH) bias2 = (float)((double)biasv * kLog2e_d);
             // ---- S and dP for this wave's 16 keys and all BQ queries, one
@@ -280,7 +301,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
                 const int row = 16 * mb + n16;  // query row (in tile) this lane supplies
 #pragma unroll
                 for (int ks = 0; ks < KS8; ++ks)
-                    o.q[ks] = *reinterpret_cast<const v4i*>(cur.q + off_r32(row, 64 * ks + 16 * g, D));
+                    o.q[ks] = *reinterpret_cast<const v4i*>(cur.q + qa_lane[mb & 1] + (mb >> 1) * 32 * D + ks * 2048);
 #pragma unroll
                 for (int ks = 0; ks < KSV; ++ks)
                     o.d[ks] = DPI8 ? *reinterpret_cast<const v4i*>(cur.dor + off_r32(row, 64 * ks + 16 * g, D))
@@ -378,7 +399,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
                 int8_t* drow = dsw + t * (BQ * 64) + kr * BQ;
 #pragma unroll
                 for (int kq = 0; kq < KQ; ++kq) {
-                    const int slot = (KQ * g + kq) ^ (kr & (CH - 1));
+                    const int slot = (KQ * g + kq) ^ (kr & (CH - 1)) ^ ((kr >> 4) & 1);
                     *reinterpret_cast<v4i*>(drow + slot * 16) = dsop[kq];
                 }
                 if (kg == 0 && lane == 0) sds[t] = sS;
@@ -403,7 +424,6 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
             // ---- dV^T += dO^^T P^,  dK^T += Q^^T dS^
             const float fv = sP * sdoi;
             const float fk = sS * sqi;
-            const int kk = n16 >> 1, hf = n16 & 1;
             Acc accv[DB], acck[DB];
             auto mfma_db = [&](int db) __attribute__((always_inline)) {
                 v4i av[KQ], ak[KQ];
@@ -411,9 +431,8 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
                 for (int kq = 0; kq < KQ; ++kq) {
                     av[kq] = reinterpret_cast<const v4i*>(cur.dot)[kq * 4 * D + g * D + 16 * db + n16];
                     // Q^ transposed: rows = d (lane), k = queries 64 kq + 16 (e/4) + 4 g + e%4
-                    const int qa = 64 * kq + 16 * (kk >> 2) + 4 * g + (kk & 3);
-                    const v2i r1 = lds_read_tr8(cur.q + off_r32(qa, 16 * db, D) + 8 * hf);
-                    const v2i r2 = lds_read_tr8(cur.q + off_r32(qa + 32, 16 * db, D) + 8 * hf);
+                    const v2i r1 = lds_read_tr8(cur.q + tr_lane + kq * 64 * D + db * 512);
+                    const v2i r2 = lds_read_tr8(cur.q + tr_lane + kq * 64 * D + 32 * D + db * 512);
                     ak[kq] = v4i{r1[0], r1[1], r2[0], r2[1]};
                     if constexpr (!F8) {
                         accv[db] = mfma16_i8(av[kq], pop[kq], kq == 0 ? magic4 : accv[db]);
@@ -456,7 +475,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
 
     // ---- prologue: first query tile into st0
     stage_query_tile<BQ, D, DPI8>(lds_addr(&st[0]), qh + (size_t)istart * BQ * D, doth + (size_t)istart * BQ * D,
-                                  dorh + (size_t)DOR_B * istart * BQ * D, w, voff);
+                                  dorh + (size_t)DOR_B * istart * BQ * D, w, voff, voff_q);
     if (tid < BQ) {
         st[0].l2[tid] = (float)((double)Lh[istart * BQ + tid] * kLog2e_d);
         st[0].ndelta[tid] = -dlh[istart * BQ + tid];
@@ -537,15 +556,16 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const int8_t* __restrict__ d
         const int8_t* s2 = kt + head + (size_t)j * K_BYTES;
         const unsigned base = lds_addr(&st);
         const int8_t* src[ROUNDS];
-        unsigned dst[ROUNDS];
+        unsigned dst[ROUNDS], vo[ROUNDS];
 #pragma unroll
         for (int u = 0; u < ROUNDS; ++u) {
             const int c0 = u * 4096 + w * 1024;
             if constexpr (DS_BYTES % 4096 == 0) src[u] = u * 4096 < DS_BYTES ? s1 + c0 : s2 + (c0 - DS_BYTES);
             else src[u] = c0 < DS_BYTES ? s1 + c0 : s2 + (c0 - DS_BYTES);
             dst[u] = base + c0;
+            vo[u] = voff;
         }
-        copy16_rounds<ROUNDS>(src, dst, voff);
+        copy16_rounds<ROUNDS>(src, dst, vo);
     };
 
     v4f acc[MBq][NB];
@@ -570,7 +590,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const int8_t* __restrict__ d
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int krow = 16 * g + 8 * h + (n16 >> 1);
-                const int slot = c ^ (krow & (CH - 1));
+                const int slot = c ^ (krow & (CH - 1)) ^ ((krow >> 4) & 1);
                 r[h] = lds_read_tr8(cur.ds + krow * BQ + slot * 16 + 8 * (n16 & 1));
             }
             av[mb] = v4i{r[0][0], r[0][1], r[1][0], r[1][1]};

@@ -146,9 +146,9 @@ __device__ __forceinline__ unsigned lds_addr(const T* p) {
     return (unsigned)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) T*)(p));
 }
 // The same copies issued in groups with one save and restore of M0 and
-// wave-uniform addresses: copy c moves lane l's 16 bytes at src_c + voff
-// (src_c uniform, held in scalar registers; voff the lane's byte offset) to
-// LDS bytes [lds_c + 16 l, lds_c + 16 l + 16).  The address arithmetic of a
+// wave-uniform addresses: copy c moves lane l's 16 bytes at src_c + voff_c
+// (src_c uniform, held in scalar registers; voff_c the lane's byte offset,
+// normally 16 l) to LDS bytes [lds_c + 16 l, lds_c + 16 l + 16).  The address arithmetic of a
 // group is scalar, outside the vector instruction stream.
 __device__ __forceinline__ void copy16x1_to_lds(const void* s0, unsigned l0, unsigned voff) {
     unsigned saved;
@@ -160,46 +160,48 @@ __device__ __forceinline__ void copy16x1_to_lds(const void* s0, unsigned l0, uns
         : "s"(l0), "s"(s0), "v"(voff)
         : "memory");
 }
-__device__ __forceinline__ void copy16x2_to_lds(const void* s0, unsigned l0, const void* s1, unsigned l1,
-                                                unsigned voff) {
+__device__ __forceinline__ void copy16x2_to_lds(const void* s0, unsigned l0, unsigned v0, const void* s1, unsigned l1,
+                                                unsigned v1) {
     unsigned saved;
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
         "s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %5, %3\n\ts_nop 0\n\t"
-        "s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %5, %4\n\ts_nop 0\n\t"
+        "s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %6, %4\n\ts_nop 0\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
-        : "s"(l0), "s"(l1), "s"(s0), "s"(s1), "v"(voff)
+        : "s"(l0), "s"(l1), "s"(s0), "s"(s1), "v"(v0), "v"(v1)
         : "memory");
 }
-__device__ __forceinline__ void copy16x4_to_lds(const void* s0, unsigned l0, const void* s1, unsigned l1,
-                                                const void* s2, unsigned l2, const void* s3, unsigned l3,
-                                                unsigned voff) {
+__device__ __forceinline__ void copy16x4_to_lds(const void* s0, unsigned l0, unsigned v0, const void* s1, unsigned l1,
+                                                unsigned v1, const void* s2, unsigned l2, unsigned v2,
+                                                const void* s3, unsigned l3, unsigned v3) {
     unsigned saved;
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
         "s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %9, %5\n\ts_nop 0\n\t"
-        "s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %9, %6\n\ts_nop 0\n\t"
-        "s_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %9, %7\n\ts_nop 0\n\t"
-        "s_mov_b32 m0, %4\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %9, %8\n\ts_nop 0\n\t"
+        "s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %10, %6\n\ts_nop 0\n\t"
+        "s_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %11, %7\n\ts_nop 0\n\t"
+        "s_mov_b32 m0, %4\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %12, %8\n\ts_nop 0\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
-        : "s"(l0), "s"(l1), "s"(l2), "s"(l3), "s"(s0), "s"(s1), "s"(s2), "s"(s3), "v"(voff)
+        : "s"(l0), "s"(l1), "s"(l2), "s"(l3), "s"(s0), "s"(s1), "s"(s2), "s"(s3), "v"(v0), "v"(v1), "v"(v2),
+          "v"(v3)
         : "memory");
 }
-// Copies of rounds [0, N) given as (source, LDS address) lists, four, two or
-// one per statement.
+// Copies of rounds [0, N) given as (source, LDS address, lane offset)
+// lists, four, two or one per statement.
 template <int N>
-__device__ __forceinline__ void copy16_rounds(const int8_t* const* src, const unsigned* dst, unsigned voff) {
+__device__ __forceinline__ void copy16_rounds(const int8_t* const* src, const unsigned* dst, const unsigned* vo) {
     int u = 0;
 #pragma unroll
     for (; u + 4 <= N; u += 4)
-        copy16x4_to_lds(src[u], dst[u], src[u + 1], dst[u + 1], src[u + 2], dst[u + 2], src[u + 3], dst[u + 3],
-                        voff);
+        copy16x4_to_lds(src[u], dst[u], vo[u], src[u + 1], dst[u + 1], vo[u + 1], src[u + 2], dst[u + 2], vo[u + 2],
+                        src[u + 3], dst[u + 3], vo[u + 3]);
     if constexpr (N % 4 >= 2) {
-        copy16x2_to_lds(src[N / 4 * 4], dst[N / 4 * 4], src[N / 4 * 4 + 1], dst[N / 4 * 4 + 1], voff);
+        constexpr int b = N / 4 * 4;
+        copy16x2_to_lds(src[b], dst[b], vo[b], src[b + 1], dst[b + 1], vo[b + 1]);
     }
-    if constexpr (N % 2 == 1) copy16x1_to_lds(src[N - 1], dst[N - 1], voff);
+    if constexpr (N % 2 == 1) copy16x1_to_lds(src[N - 1], dst[N - 1], vo[N - 1]);
 }
 // The compiler does not count the copies above either, so a register loaded
 // from global memory before some copies and first used after them would get

@@ -152,6 +152,9 @@ __global__ __launch_bounds__(64 * kWaves, 2) void fwd_kernel(
         for (int ks = 0; ks < KS; ++ks) qop[ks] = v4i{0, 0, 0, 0};
     }
 
+    // the product s_Q * scale * log2 e in float64; each tile multiplies in
+    // its s_K and rounds once to float32
+    const double sq_s2 = (double)sqv * scale2;
     float m = -INFINITY, l = 0.f;
     v4f o[DB];
 #pragma unroll
@@ -169,8 +172,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void fwd_kernel(
 #pragma unroll
         for (int c0 = 0; c0 < TILE_BYTES; c0 += NT * 16) {
             if (c0 + w * 1024 < TILE_BYTES)   // a d=64 tile is half a round
-                copy16x2_to_lds(ks_ + c0 + w * 1024, lk + c0 + w * 1024, vs_ + c0 + w * 1024, lv + c0 + w * 1024,
-                                voff);
+                copy16x2_to_lds(ks_ + c0 + w * 1024, lk + c0 + w * 1024, voff, vs_ + c0 + w * 1024,
+                                lv + c0 + w * 1024, voff);
         }
         if (QSMOOTH && w == kWaves - 1) {
             // lane group r of the first kQTile/64 groups: Q block row r, 16 B
@@ -216,9 +219,9 @@ __global__ __launch_bounds__(64 * kWaves, 2) void fwd_kernel(
                     for (int ks = 0; ks < KS; ++ks) s[kb] = mfma16_i8(av[ks], qop[ks], ks == 0 ? magic4 : s[kb]);
                 }
             }
-            // one rounding from the exact product of the scales (keeps the
-            // logits within an ulp of the definition)
-            const float c2 = (float)((double)sqv * (double)sk[(size_t)bh * Tn + j] * scale2);
+            // one rounding to float32 from the float64 product of the scales
+            // (keeps the logits within an ulp of the definition)
+            const float c2 = (float)(sq_s2 * (double)sk[(size_t)bh * Tn + j]);
             float rm, sum;
             v4i pc;   // P codes: byte r of dword kb = key 16 kb + 4 g + r
             auto codes = [&](auto mask_tag) __attribute__((always_inline)) {
@@ -269,7 +272,6 @@ __global__ __launch_bounds__(64 * kWaves, 2) void fwd_kernel(
                 // codes against the tile maximum (per token), or with the
                 // static scale against the exact running maximum
                 const float shift = (PSTATIC ? fmaxf(m, rm) : rm) - kLog2Qmax;
-                sum = 0.f;
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) {
                     uint32_t word = 0u;
@@ -284,7 +286,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void fwd_kernel(
                         }
                         // 127 * 2^(x - rm), in [0, 127] (E4M3: 448 and [0, 448])
                         const float e = __builtin_amdgcn_exp2f(x);
-                        sum += e;
+                        sum = (kb == 0 && r == 0) ? e : sum + e;
                         ev[r] = e;
                         // byte r of the word = rint(e) (round to nearest even)
                         if constexpr (!F8) word = __builtin_amdgcn_cvt_pk_u8_f32(e, r, word);

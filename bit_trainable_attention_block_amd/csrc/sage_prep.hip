@@ -67,17 +67,21 @@ __device__ __forceinline__ float block_max(float m, float* red) {
 
 // Column sums in float64 over the thread's rows, reduced across the RSTEP
 // threads sharing a column chunk; result for column c in dsum[c].
+// red holds kThreads rows of 9 doubles (8 sums and a pad, so that the
+// column reads below fall on distinct LDS banks).
+constexpr int kRedStride = 9;
+
 template <int R, int D>
 __device__ __forceinline__ void block_colsum(const double (&part)[8], double* red, double* dsum) {
     using B = Blk<R, D>;
     const int t = threadIdx.x;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) red[c * kThreads + t] = part[c];
+    for (int c = 0; c < 8; ++c) red[t * kRedStride + c] = part[c];
     __syncthreads();
     if (t < D) {
         const int cc = t / 8, c = t % 8;
         double s = 0.0;
-        for (int r = 0; r < B::RSTEP; ++r) s += red[c * kThreads + r * B::CPR + cc];
+        for (int r = 0; r < B::RSTEP; ++r) s += red[(r * B::CPR + cc) * kRedStride + c];
         dsum[t] = s;
     }
     __syncthreads();
@@ -112,11 +116,17 @@ __device__ __forceinline__ void rms_normalize(BlockVals<R, D>& x, float* __restr
     }
 }
 
+// Row stride of the LDS code buffers: 16 bytes of padding per row, so the
+// R32 gather (16-byte chunks of consecutive rows in consecutive lanes) steps
+// through the LDS banks instead of hitting every row at the same bank.
+template <int D>
+constexpr int CStride = D + 16;
+
 // Largest code magnitude: INT8 or E4M3.
 __device__ __forceinline__ float qmax_of(int fp8) { return fp8 ? 448.f : 127.f; }
 
 // Quantise x (values of the block held per thread) with scale s and store
-// the codes (INT8, or E4M3 bytes) row-major into LDS codes[R][D].
+// the codes (INT8, or E4M3 bytes) row-major into LDS codes[R][CStride<D>].
 template <int R, int D>
 __device__ __forceinline__ void codes_to_lds(const float (&x)[Blk<R, D>::PER_T][8], float s,
                                              uint8_t* codes, int fp8) {
@@ -140,7 +150,7 @@ __device__ __forceinline__ void codes_to_lds(const float (&x)[Blk<R, D>::PER_T][
             w.x = pack4(c[0], c[1], c[2], c[3]);
             w.y = pack4(c[4], c[5], c[6], c[7]);
         }
-        *reinterpret_cast<uint2*>(codes + row * D + cc * 8) = w;
+        *reinterpret_cast<uint2*>(codes + row * CStride<D> + cc * 8) = w;
     }
 }
 
@@ -163,7 +173,7 @@ __device__ __forceinline__ void store_codes(const uint8_t* codes, int8_t* __rest
         if constexpr (L == R32) {
             const int g = oc / (2 * D), rem = oc % (2 * D);
             const int col16 = rem / 32, r = rem % 32;
-            out = *reinterpret_cast<const v4i*>(codes + (32 * g + r) * D + col16 * 16);
+            out = *reinterpret_cast<const v4i*>(codes + (32 * g + r) * CStride<D> + col16 * 16);
         } else {
             constexpr int GR = 64;                     // rows per group
             constexpr int PARTS = GR / 16;             // h or g values
@@ -176,7 +186,7 @@ __device__ __forceinline__ void store_codes(const uint8_t* codes, int8_t* __rest
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
                     const int row = grp * GR + col_layout_row<L>(part, 4 * q + b);
-                    acc |= (uint32_t)codes[row * D + col] << (8 * b);
+                    acc |= (uint32_t)codes[row * CStride<D> + col] << (8 * b);
                 }
                 w[q] = acc;
             }
@@ -220,8 +230,8 @@ __global__ __launch_bounds__(kThreads) void quant_v_ksum_kernel(
     constexpr int R = 64;
     using B = Blk<R, D>;
     __shared__ float red[4];
-    __shared__ __align__(16) uint8_t codes[R * D];
-    __shared__ double dred[8 * kThreads];
+    __shared__ __align__(16) uint8_t codes[R * CStride<D>];
+    __shared__ double dred[kRedStride * kThreads];
     __shared__ double dsum[D];
     const int j = blockIdx.x, bh = blockIdx.y;
     const size_t head = (size_t)bh * N * D;
@@ -272,8 +282,8 @@ __global__ __launch_bounds__(kThreads) void quant_q_kernel(const u16* __restrict
                                                            float* __restrict__ rq, int fp8) {
     using B = Blk<BQ, D>;
     __shared__ float red[4];
-    __shared__ __align__(16) uint8_t codes[BQ * D];
-    __shared__ double dred[8 * kThreads];
+    __shared__ __align__(16) uint8_t codes[BQ * CStride<D>];
+    __shared__ double dred[kRedStride * kThreads];
     __shared__ double dsum[D];
     __shared__ float mu[D];
     const int i = blockIdx.x, bh = blockIdx.y;
@@ -334,7 +344,7 @@ __global__ __launch_bounds__(kThreads) void quant_k_kernel(
     constexpr int R = 64;
     using B = Blk<R, D>;
     __shared__ float red[4];
-    __shared__ __align__(16) uint8_t codes[R * D];
+    __shared__ __align__(16) uint8_t codes[R * CStride<D>];
     __shared__ float mu[D];
     __shared__ float ksm[R][D + 1];
     const int j = blockIdx.x, bh = blockIdx.y;
@@ -407,7 +417,7 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const u16* __restrict
                                                            u16* __restrict__ dor, int dp_int8, int fp8) {
     using B = Blk<BQ, D>;
     __shared__ float red[4];
-    __shared__ __align__(16) uint8_t codes[BQ * D];
+    __shared__ __align__(16) uint8_t codes[BQ * CStride<D>];
     const int i = blockIdx.x, bh = blockIdx.y;
     const size_t head = (size_t)bh * N * D;
     const int row0 = i * BQ;
