@@ -66,6 +66,21 @@ def main(path):
                 if t in d:
                     c, r = t1.get(s, {}).get(t, (float("nan"), float("nan")))
                     print(f"| {s} | {t} | {d[t]['cos']:.4f} | {d[t]['rel_l2']:.4f} | {c:.4f} | {r:.4f} |")
+    fp8_products(cases)
+
+
+def fp8_products(cases):
+    """The E4M3 product probe: summation error over the largest product."""
+    rows = [(c, r) for c, rs in cases.items() if c.startswith("fp8_products_") for r in rs]
+    if not rows:
+        return
+    print()
+    print("| E4M3 product probe operands | instruction | max error / largest product |")
+    print("|---|---|---|")
+    for c, r in rows:
+        inst = {"k32": "v_mfma_f32_16x16x32_fp8_fp8", "k128": "v_mfma_f32_16x16x128_f8f6f4"}.get(r["tensor"],
+                                                                                             r["tensor"])
+        print(f"| {c[len('fp8_products_'):]} | {inst} | {r['max_err_over_max_product']:.2e} |")
 
 
 if __name__ == "__main__":

@@ -16,8 +16,8 @@ from oracle import fpa, metrics, sage
 REL_L2_MAX = 1e-3
 COS_MIN = 0.99999
 # The E4M3 variant's relative-L2 bar.  Its matrix instruction does not sum
-# exactly: on random E4M3 operands it is off by up to ~2^-14 of the largest
-# product (measured), where the INT8 one is exact.  The logits then differ
+# exactly: on random E4M3 operands it is off by up to ~1.3e-4 of the largest
+# product (tests/test_gpu_fp8_products.py), where the INT8 one is exact.  The logits then differ
 # from the oracle's exact sums by ~1e-4 relative, and an E4M3 code whose exact
 # quotient lies that close to a rounding midpoint moves by one step, 1/8 of
 # its value (an INT8 step is 1/127 of the block maximum).  Each such move
