@@ -25,7 +25,7 @@ class SageAttentionFunction(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, Q, K, V, causal: bool, k_smooth: bool, q_smooth: bool, sm_scale: float, bq: int,
-                qk_norm: bool):
+                qk_norm: bool, fp8: bool):
         if not (Q.is_cuda and K.is_cuda and V.is_cuda):
             raise ValueError("sage_attention: Q, K, V must be GPU tensors")
         if Q.dtype not in (torch.bfloat16, torch.float16) or K.dtype != Q.dtype or V.dtype != Q.dtype:
@@ -36,7 +36,7 @@ class SageAttentionFunction(torch.autograd.Function):
         sh = bd.Shape(B=B, H=H, N=N, D=D, bq=bq, bkv=64,
                       dtype=bd.SAGE_BF16 if Q.dtype == torch.bfloat16 else bd.SAGE_FP16,
                       causal=bool(causal), k_smooth=bool(k_smooth), q_smooth=bool(q_smooth),
-                      sm_scale=float(sm_scale), qk_norm=bool(qk_norm))
+                      sm_scale=float(sm_scale), qk_norm=bool(qk_norm), fp8=bool(fp8))
         Q, K, V = Q.contiguous(), K.contiguous(), V.contiguous()
         qt = bd.quantize(sh, Q, K, V)
         O, L = bd.fwd(sh, qt)
@@ -59,12 +59,13 @@ class SageAttentionFunction(torch.autograd.Function):
             Q, K = ctx.saved_tensors[2:]
             bd.qk_norm_bwd(sh, Q, K, ctx.qt, dQ, dK)
         ctx.qt = None
-        return dQ.to(O.dtype), dK.to(O.dtype), dV.to(O.dtype), None, None, None, None, None, None
+        return dQ.to(O.dtype), dK.to(O.dtype), dV.to(O.dtype), None, None, None, None, None, None, None
 
 
 def sage_attention(Q, K, V, causal: bool = False, k_smooth: bool = True, q_smooth: bool = False,
-                   sm_scale: float = 0.0, bq: int = 128, qk_norm: bool = False):
+                   sm_scale: float = 0.0, bq: int = 128, qk_norm: bool = False, fp8: bool = False):
     """SageBwd INT8 attention with gradients (sm_scale 0 selects 1/sqrt(D)).
     qk_norm=True applies QK-norm (unit gain) to Q and K inside sage_quantize
-    and returns gradients w.r.t. the un-normalised inputs."""
-    return SageAttentionFunction.apply(Q, K, V, causal, k_smooth, q_smooth, sm_scale, bq, qk_norm)
+    and returns gradients w.r.t. the un-normalised inputs.  fp8=True runs the
+    E4M3 variant (E4M3 codes in place of INT8; see include/sage.h)."""
+    return SageAttentionFunction.apply(Q, K, V, causal, k_smooth, q_smooth, sm_scale, bq, qk_norm, fp8)
