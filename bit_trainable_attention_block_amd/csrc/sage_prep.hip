@@ -272,8 +272,9 @@ __global__ __launch_bounds__(kThreads) void quant_v_ksum_kernel(
     }
 }
 
-// Q blocks (BQ rows): optional Q-smoothing, codes -> q (R32) and qt (C64P).
-template <bool BF16, int D, int BQ>
+// Q blocks (BQ rows): optional Q-smoothing (QS, mu_q set), codes -> q (R32)
+// and qt (C64P).  Only with QS does the block hold the column-sum scratch.
+template <bool BF16, int D, int BQ, bool QS>
 __global__ __launch_bounds__(kThreads) void quant_q_kernel(const u16* __restrict__ Q, int N,
                                                            int8_t* __restrict__ q,
                                                            int8_t* __restrict__ qt,
@@ -283,9 +284,9 @@ __global__ __launch_bounds__(kThreads) void quant_q_kernel(const u16* __restrict
     using B = Blk<BQ, D>;
     __shared__ float red[4];
     __shared__ __align__(16) uint8_t codes[BQ * CStride<D>];
-    __shared__ double dred[kRedStride * kThreads];
-    __shared__ double dsum[D];
-    __shared__ float mu[D];
+    __shared__ double dred[QS ? kRedStride * kThreads : 1];
+    __shared__ double dsum[QS ? D : 1];
+    __shared__ float mu[QS ? D : 1];
     const int i = blockIdx.x, bh = blockIdx.y;
     const size_t head = (size_t)bh * N * D;
     const int row0 = i * BQ;
@@ -298,7 +299,7 @@ __global__ __launch_bounds__(kThreads) void quant_q_kernel(const u16* __restrict
     for (int k = 0; k < B::PER_T; ++k) unpack8<BF16>(raw[k], x[k]);
     if (rq != nullptr) rms_normalize<BQ, D>(x, rq + (size_t)bh * N, row0);
 
-    if (mu_q != nullptr) {
+    if constexpr (QS) {
         double part[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
         for (int k = 0; k < B::PER_T; ++k)
@@ -334,8 +335,9 @@ __global__ __launch_bounds__(kThreads) void quant_q_kernel(const u16* __restrict
 // K blocks (64 rows): mu_K = f32(sum / N); K_sm = f32(K - mu_K); codes -> k
 // (R32) and kt (C64N).  With Q-smoothing, also the logit bias of these keys
 // for every query block: bias[i][n] = scale * sum_c mu_Q[i][c] * K_sm[n][c]
-// (float64 accumulation, rounded once).
-template <bool BF16, int D>
+// (float64 accumulation, rounded once).  QS: Q-smoothing on (qk_bias set);
+// only then does the block hold its smoothed rows in LDS.
+template <bool BF16, int D, bool QS>
 __global__ __launch_bounds__(kThreads) void quant_k_kernel(
     const u16* __restrict__ K, int N, int8_t* __restrict__ k, int8_t* __restrict__ kt,
     float* __restrict__ sk, float* __restrict__ mu_k, const double* __restrict__ ws, int k_smooth,
@@ -346,11 +348,14 @@ __global__ __launch_bounds__(kThreads) void quant_k_kernel(
     __shared__ float red[4];
     __shared__ __align__(16) uint8_t codes[R * CStride<D>];
     __shared__ float mu[D];
-    __shared__ float ksm[R][D + 1];
+    __shared__ float ksm[QS ? R : 1][QS ? D + 1 : 1];
     const int j = blockIdx.x, bh = blockIdx.y;
     const size_t head = (size_t)bh * N * D;
     const int row0 = j * R;
 
+    // the block's rows are requested first; the mean arrives meanwhile
+    v4i raw[B::PER_T];
+    load_block<R, D>(K + head + (size_t)row0 * D, raw);
     if (threadIdx.x < D) {
         float mv = 0.f;
         if (k_smooth) {
@@ -361,9 +366,7 @@ __global__ __launch_bounds__(kThreads) void quant_k_kernel(
     }
     __syncthreads();
 
-    v4i raw[B::PER_T];
     float x[B::PER_T][8];
-    load_block<R, D>(K + head + (size_t)row0 * D, raw);
     const int cc = threadIdx.x % B::CPR;
 #pragma unroll
     for (int kk = 0; kk < B::PER_T; ++kk) unpack8<BF16>(raw[kk], x[kk]);
@@ -381,7 +384,7 @@ __global__ __launch_bounds__(kThreads) void quant_k_kernel(
     const float s = __fdiv_rn(a, qmax_of(fp8));
     codes_to_lds<R, D>(x, s, codes, fp8);
     if (threadIdx.x == 0) sk[(size_t)bh * (N / R) + j] = s;
-    if (qk_bias != nullptr) {
+    if constexpr (QS) {
 #pragma unroll
         for (int kk = 0; kk < B::PER_T; ++kk) {
             int row = threadIdx.x / B::CPR + kk * B::RSTEP;
@@ -393,7 +396,7 @@ __global__ __launch_bounds__(kThreads) void quant_k_kernel(
     store_codes<R32, R, D>(codes, k + head + (size_t)row0 * D);
     store_codes<C64N, R, D>(codes, kt + head + (size_t)row0 * D);
 
-    if (qk_bias != nullptr) {
+    if constexpr (QS) {
         // thread -> (key n = t % 64, query blocks i = t / 64 + 4 * step)
         const int n = threadIdx.x & 63;
         for (int i = threadIdx.x >> 6; i < Tm; i += 4) {
@@ -505,15 +508,12 @@ hipError_t quantize_impl(const Dims& d, const void* Q, const void* K, const void
     quant_v_ksum_kernel<BF16, D><<<dim3(d.Tn(), BH), blk, 0, s>>>(
         (const u16*)K, (const u16*)V, d.N, out.vt, out.sv, out.vr, ws, d.k_smooth ? 1 : 0, d.dp_int8 ? 1 : 0,
         d.qk_norm ? 1 : 0, d.fp8 ? 1 : 0);
-    if (d.bq == 128)
-        quant_q_kernel<BF16, D, 128><<<dim3(d.Tm(), BH), blk, 0, s>>>((const u16*)Q, d.N, out.q, out.qt,
-                                                                      out.sq, d.q_smooth ? out.mu_q : nullptr,
-                                                                      d.qk_norm ? out.rq : nullptr, d.fp8 ? 1 : 0);
-    else
-        quant_q_kernel<BF16, D, 64><<<dim3(d.Tm(), BH), blk, 0, s>>>((const u16*)Q, d.N, out.q, out.qt,
-                                                                     out.sq, d.q_smooth ? out.mu_q : nullptr,
-                                                                     d.qk_norm ? out.rq : nullptr, d.fp8 ? 1 : 0);
-    quant_k_kernel<BF16, D><<<dim3(d.Tn(), BH), blk, 0, s>>>(
+    auto qq = d.bq == 128 ? (d.q_smooth ? quant_q_kernel<BF16, D, 128, true> : quant_q_kernel<BF16, D, 128, false>)
+                          : (d.q_smooth ? quant_q_kernel<BF16, D, 64, true> : quant_q_kernel<BF16, D, 64, false>);
+    qq<<<dim3(d.Tm(), BH), blk, 0, s>>>((const u16*)Q, d.N, out.q, out.qt, out.sq, d.q_smooth ? out.mu_q : nullptr,
+                                        d.qk_norm ? out.rq : nullptr, d.fp8 ? 1 : 0);
+    auto kq = d.q_smooth ? quant_k_kernel<BF16, D, true> : quant_k_kernel<BF16, D, false>;
+    kq<<<dim3(d.Tn(), BH), blk, 0, s>>>(
         (const u16*)K, d.N, out.k, out.kt, out.sk, out.mu_k, ws, d.k_smooth ? 1 : 0,
         d.q_smooth ? out.mu_q : nullptr, d.q_smooth ? out.qk_bias : nullptr, d.Tm(), d.scale,
         d.qk_norm ? out.rk : nullptr, d.fp8 ? 1 : 0);
