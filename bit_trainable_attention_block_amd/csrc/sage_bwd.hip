@@ -113,13 +113,23 @@ struct BwdStage {
 // number of rounds (BQ*D a multiple of 8 KiB) the region of a round is known
 // at compile time.  voff = 16 * lane.
 template <int BQ, int D, bool DPI8>
-__device__ __forceinline__ void stage_query_tile(unsigned lds, const int8_t* q, const int8_t* dot,
-                                                 const int8_t* dorb, int w, unsigned voff, unsigned voff_q) {
-    constexpr int QB = BQ * D, TOT = (DPI8 ? 3 : 4) * QB, R = 8 * 1024;
-    constexpr int ROUNDS = (TOT + R - 1) / R, FULL = TOT / R;
+struct StagePlan {
+    static constexpr int QB = BQ * D, TOT = (DPI8 ? 3 : 4) * QB, R = 8 * 1024;
+    static constexpr int ROUNDS = (TOT + R - 1) / R, FULL = TOT / R;
     static_assert(QB % 1024 == 0, "stage shape");
     const int8_t* src[ROUNDS];
     unsigned dst[ROUNDS], vo[ROUNDS];
+};
+
+template <int BQ, int D, bool DPI8>
+__device__ __forceinline__ void plan_query_tile(StagePlan<BQ, D, DPI8>& pl, unsigned lds, const int8_t* q,
+                                                const int8_t* dot, const int8_t* dorb, int w, unsigned voff,
+                                                unsigned voff_q) {
+    using P = StagePlan<BQ, D, DPI8>;
+    constexpr int QB = P::QB, TOT = P::TOT, R = P::R, ROUNDS = P::ROUNDS;
+    const int8_t** src = pl.src;
+    unsigned* dst = pl.dst;
+    unsigned* vo = pl.vo;
 #pragma unroll
     for (int u = 0; u < ROUNDS; ++u) {
         const int c0 = u * R + w * 1024;
@@ -134,11 +144,36 @@ __device__ __forceinline__ void stage_query_tile(unsigned lds, const int8_t* q, 
         }
         dst[u] = lds + c0;
     }
-    copy16_rounds<FULL>(src, dst, vo);
-    if constexpr (FULL < ROUNDS) {
-        // the last round of a stage that is not a whole number of rounds
-        if (FULL * R + w * 1024 < TOT) copy16x1_to_lds(src[FULL], dst[FULL], vo[FULL]);
-    }
+}
+
+// Round u of a planned stage copy (one instruction per wave).  The plan's
+// source and LDS addresses are wave-uniform; where the compiler has kept one
+// in a vector register across the products, readfirstlane brings it back to a
+// scalar register for the copy (a no-op for one already there).
+__device__ __forceinline__ const int8_t* uniform_ptr(const int8_t* p) {
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    return reinterpret_cast<const int8_t*>(((uint64_t)hi << 32) | lo);
+}
+template <int BQ, int D, bool DPI8>
+__device__ __forceinline__ void issue_round(const StagePlan<BQ, D, DPI8>& pl, int u, int w) {
+    using P = StagePlan<BQ, D, DPI8>;
+    // the last round of a stage that is not a whole number of rounds covers
+    // only some waves
+    if (u < P::FULL || P::FULL * P::R + w * 1024 < P::TOT)
+        copy16x1_to_lds(uniform_ptr(pl.src[u]), __builtin_amdgcn_readfirstlane(pl.dst[u]), pl.vo[u]);
+}
+
+// The whole stage at once.
+template <int BQ, int D, bool DPI8>
+__device__ __forceinline__ void stage_query_tile(unsigned lds, const int8_t* q, const int8_t* dot,
+                                                 const int8_t* dorb, int w, unsigned voff, unsigned voff_q) {
+    using P = StagePlan<BQ, D, DPI8>;
+    StagePlan<BQ, D, DPI8> pl;
+    plan_query_tile<BQ, D, DPI8>(pl, lds, q, dot, dorb, w, voff, voff_q);
+    copy16_rounds<P::FULL>(pl.src, pl.dst, pl.vo);
+    if constexpr (P::FULL < P::ROUNDS) issue_round<BQ, D, DPI8>(pl, P::FULL, w);
 }
 
 // Two LDS stages alternate: tile i is read from stage (i - istart) & 1 while
@@ -235,6 +270,12 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
     float nbias = 0.f;
     if (QSMOOTH && kv_on) nbias = qk_bias[((size_t)bh * Tm + istart) * N + key];
 
+    // dS codes and scale of the last tile, not yet stored
+    v4i pend_ds[KQ];
+    size_t pend_t = 0;
+    float pend_s = 0.f;
+    bool pend_on = false;
+
     // One query tile, read from `cur`; the next one is copied into `nxt`.
     auto step = [&](int i, BwdStage<BQ, D, DPI8>& cur, BwdStage<BQ, D, DPI8>& nxt) __attribute__((always_inline)) {
         const int qbase = i * BQ;
@@ -248,10 +289,34 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
             nd = dlh[qbase + BQ + tid];
         }
         if (QSMOOTH && kv_on && more) nbias = qk_bias[((size_t)bh * Tm + i + 1) * N + key];
-        if (more)
-            stage_query_tile<BQ, D, DPI8>(lds_addr(&nxt), qh + (size_t)(qbase + BQ) * D,
-                                          doth + (size_t)(qbase + BQ) * D, dorh + (size_t)DOR_B * (qbase + BQ) * D,
-                                          w, voff, voff_q);
+        // the previous tile's dS codes and scale go out now, ahead of this
+        // tile's copies, so that the wait for the copies at the end of this
+        // tile does not also wait for the stores to complete
+        if (pend_on) {
+            int8_t* drow = dsw + pend_t * (BQ * 64) + kr * BQ;
+#pragma unroll
+            for (int kq = 0; kq < KQ; ++kq) {
+                const int slot = (KQ * g + kq) ^ (kr & (CH - 1)) ^ ((kr >> 4) & 1);
+                *reinterpret_cast<v4i*>(drow + slot * 16) = pend_ds[kq];
+            }
+            if (kg == 0 && lane == 0) sds[pend_t] = pend_s;
+        }
+        // the next tile's copies: one round per 16-query block of the S and
+        // dP products below, so that no wave stalls on the load path at once.
+        // On the last tile the current tile is copied again into the idle
+        // stage (every wave finished reading it before the barrier that ended
+        // the previous tile): the copies stay unconditional, and no branch
+        // splits the product loop (a branch there lets the compiler sink all
+        // the vector work below all the products).
+        using Plan = StagePlan<BQ, D, DPI8>;
+        Plan pl;
+        const int qnext = more ? qbase + BQ : qbase;
+        plan_query_tile<BQ, D, DPI8>(pl, lds_addr(&nxt), qh + (size_t)qnext * D, doth + (size_t)qnext * D,
+                                     dorh + (size_t)DOR_B * qnext * D, w, voff, voff_q);
+        auto issue_rounds_of_block = [&](int mb) __attribute__((always_inline)) {
+#pragma unroll
+            for (int u = mb * Plan::ROUNDS / MB; u < (mb + 1) * Plan::ROUNDS / MB; ++u) issue_round<BQ, D, DPI8>(pl, u, w);
+        };
 
         // the tile exists and has a visible key (it is stored for the dQ pass)
         const bool tile_on = kv_on && (!CAUSAL || j * 64 <= qbase + BQ - 1);
@@ -331,6 +396,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
             for (int mb = 0; mb < MB; ++mb) {
                 if (mb + 2 < MB) read_block(mb + 2, opa[mb & 1]);
                 if (mb + 1 < MB) mfma_block(mb + 1, opa[(mb + 1) & 1]);
+                issue_rounds_of_block(mb);
                 const v4f l2 = *reinterpret_cast<const v4f*>(&cur.l2[16 * mb + 4 * g]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -393,17 +459,13 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
                     dsop[mb >> 2][mb & 3] = pack_magic(sc[0], sc[1], sc[2], sc[3]);
                 }
             }
-            // ---- dS codes and scale to the workspace (key-major, swizzled)
-            const size_t t = (size_t)bh * tph + tile_index<BQ, CAUSAL>(i, j, Tn);
-            if (tile_on) {
-                int8_t* drow = dsw + t * (BQ * 64) + kr * BQ;
+            // ---- dS codes and scale for the workspace (key-major, swizzled),
+            // stored at the start of the next tile
+            pend_t = (size_t)bh * tph + tile_index<BQ, CAUSAL>(i, j, Tn);
+            pend_on = tile_on;
+            pend_s = sS;
 #pragma unroll
-                for (int kq = 0; kq < KQ; ++kq) {
-                    const int slot = (KQ * g + kq) ^ (kr & (CH - 1)) ^ ((kr >> 4) & 1);
-                    *reinterpret_cast<v4i*>(drow + slot * 16) = dsop[kq];
-                }
-                if (kg == 0 && lane == 0) sds[t] = sS;
-            }
+            for (int kq = 0; kq < KQ; ++kq) pend_ds[kq] = dsop[kq];
             if (QSMOOTH) {
                 // dK bias (dS^T 1) mu_Q^T from the unquantised dS
                 float cs = 0.f;
@@ -492,6 +554,15 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
     for (int i = istart; i < Tm; ++i) {
         const int b = (i - istart) & 1;
         step(i, st[b], st[b ^ 1]);
+    }
+    if (pend_on) {
+        int8_t* drow = dsw + pend_t * (BQ * 64) + kr * BQ;
+#pragma unroll
+        for (int kq = 0; kq < KQ; ++kq) {
+            const int slot = (KQ * g + kq) ^ (kr & (CH - 1)) ^ ((kr >> 4) & 1);
+            *reinterpret_cast<v4i*>(drow + slot * 16) = pend_ds[kq];
+        }
+        if (kg == 0 && lane == 0) sds[pend_t] = pend_s;
     }
 
     // ---- write dV and dK (lane = key, 4 consecutive d per block)
