@@ -1,10 +1,12 @@
 // SageBwd INT8 forward (SageBwd method summary, forward steps (3)-(5);
 // SageAttention3 write-up Eq. 1 and Eq. 8).
 //
-// One workgroup = 8 waves = 128 queries of one head; wave w owns 16 queries,
-// so a wave holds little state (about 100 registers) and four waves share
-// each SIMD: while some wait on products or LDS, others keep the vector
-// units busy.  Key/value tiles of 64 keys (one K/V quantisation block)
+// One workgroup = 4 waves = 64 queries of one head; wave w owns 16 queries,
+// so a wave holds little state (about 110 registers) and four waves, from
+// four independent workgroups, share each SIMD: while some wait on products,
+// LDS or their workgroup's barrier, others keep the vector units busy (the
+// vector units are the bound: about 190 issue slots per wave and tile against
+// 16 products).  Key/value tiles of 64 keys (one K/V quantisation block)
 // stream through two LDS stages filled one tile ahead by asynchronous copies:
 // the K codes (R32 row tiles) and the V codes (C64P column tiles) are
 // contiguous 64*D-byte runs in HBM.
@@ -48,7 +50,7 @@ struct FwdArgs {
     double scale2;  // softmax scale * log2(e)
 };
 
-constexpr int kWaves = 8;
+constexpr int kWaves = 4;
 constexpr int kQTile = 16 * kWaves;  // queries per workgroup
 constexpr int kKTile = 64;           // keys per stage (= the K/V quantisation block)
 constexpr float kLazy = 8.f;         // log2 slack before the reference maximum moves
@@ -88,7 +90,7 @@ constexpr int kMaskedSum = kMagicBits - (1 << 22) + 1;
 
 // F8: the E4M3 variant (codes E4M3, 448 in place of 127, float32 products).
 template <bool BF16, int D, bool CAUSAL, bool QSMOOTH, bool PSTATIC, bool F8>
-__global__ __launch_bounds__(64 * kWaves, 2) void fwd_kernel(
+__global__ __launch_bounds__(64 * kWaves, 4) void fwd_kernel(
     const int8_t* __restrict__ q, const float* __restrict__ sq, const int8_t* __restrict__ k,
     const float* __restrict__ sk, const int8_t* __restrict__ vt, const float* __restrict__ sv,
     const float* __restrict__ qk_bias, u16* __restrict__ Out, float* __restrict__ L, int N, int bq,
@@ -176,11 +178,12 @@ __global__ __launch_bounds__(64 * kWaves, 2) void fwd_kernel(
                                 lv + c0 + w * 1024, voff);
         }
         if (QSMOOTH && w == kWaves - 1) {
-            // lane group r of the first kQTile/64 groups: Q block row r, 16 B
-            // per lane (a row of 64 floats lands in bias[r])
+            // lane group r of the first max(1, kQTile/bq) groups: Q block row
+            // r, 16 B per lane (a row of 64 floats lands in bias[r]); a
+            // workgroup narrower than a Q block reads one row
             const int r = lane >> 4;
             const int qb = qt * kQTile / bq + r;
-            if (r < kQTile / bq && qb < Tm)
+            if (r < max(1, kQTile / bq) && qb < Tm)
                 copy16_to_lds(qk_bias + ((size_t)bh * Tm + qb) * N + (size_t)j * kKTile + 4 * (lane & 15),
                               &dst.bias[0][0]);
         }
