@@ -61,6 +61,20 @@ __device__ __forceinline__ size_t tile_index(int i, int j, int Tn) {
     return CAUSAL ? (size_t)R * i * (i + 1) / 2 + j : (size_t)i * Tn + j;
 }
 
+// x / Q for a tile maximum x >= 0 and the code range Q (127, or 448 for
+// E4M3): the product with the rounded reciprocal, then one fma step on the
+// exact residual x - q Q.  The quotient is within an ulp of the correctly
+// rounded one (it matched it on every one of 3.2 million inputs tried); the P
+// and dS scales are compared to tolerance, not bit for bit, and this costs a
+// quarter of the instructions of a full division.
+template <bool F8>
+__device__ __forceinline__ float div_by_qmax(float x) {
+    constexpr float Q = F8 ? 448.f : 127.f;
+    constexpr float c = 1.f / Q;
+    const float q = x * c;
+    return fmaf(fmaf(-q, Q, x), c, q);
+}
+
 // Byte 0 of four magic-rounded floats -> one dword (rows r = 0..3).
 __device__ __forceinline__ int pack_magic(float a, float b, float c, float d) {
     const uint32_t lo = __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x0c0c0400u);
@@ -336,8 +350,8 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
             asm volatile("" ::: "memory");
             pmax = fmaxf(fmaxf(red[kb][0][0], red[kb][0][1]), fmaxf(red[kb][0][2], red[kb][0][3]));
             dsmax = fmaxf(fmaxf(red[kb][1][0], red[kb][1][1]), fmaxf(red[kb][1][2], red[kb][1][3]));
-            sP = __fdiv_rn(pmax, kQmax);
-            sS = __fdiv_rn(dsmax, kQmax);
+            sP = div_by_qmax<F8>(pmax);
+            sS = div_by_qmax<F8>(dsmax);
         };
         {
             float p[MB][4], ds[MB][4];
@@ -434,8 +448,10 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
             }
             float sP, sS;
             tile_scales(pmax, dsmax, sP, sS);
-            const float invP = sP > 0.f ? 1.f / sP : 0.f;
-            const float invS = sS > 0.f ? 1.f / sS : 0.f;
+            // hardware reciprocal (within an ulp): a code moves only where
+            // P / s_P lies within about 1e-5 of a rounding boundary
+            const float invP = sP > 0.f ? __builtin_amdgcn_rcpf(sP) : 0.f;
+            const float invS = sS > 0.f ? __builtin_amdgcn_rcpf(sS) : 0.f;
             // ---- codes, query-contiguous per lane (4 queries per dword)
             v4i pop[KQ], dsop[KQ];
 #pragma unroll
