@@ -1,6 +1,6 @@
 """Accuracy summary from the GPU parity run's metrics log (not a test module).
 
-    python -m tests.accuracy_report gpurun_out/parity_metrics.jsonl > profiles/accuracy_d128_workloads.md
+    python -m tests.accuracy_report $SAGE_PARITY_OUT/parity_metrics.jsonl > profiles/accuracy_d128_workloads.md
 
 For every full-size workload: the GPU against the oracle (the parity gate),
 and the GPU and the oracle each against full-precision float64 attention on

@@ -4,6 +4,7 @@ from __future__ import annotations
 
 import json
 import os
+import tempfile
 
 import numpy as np
 import torch
@@ -32,7 +33,9 @@ def bar(cfg):
     return (FP8_REL_L2_MAX if getattr(cfg, "fp8", False) else REL_L2_MAX), COS_MIN
 
 
-OUT_DIR = os.environ.get("SAGE_PARITY_OUT", "gpurun_out")
+# where the metrics log and failing-case dumps go (set SAGE_PARITY_OUT to keep
+# them with a run's other output)
+OUT_DIR = os.environ.get("SAGE_PARITY_OUT", os.path.join(tempfile.gettempdir(), "sage_parity"))
 
 
 def say(msg):
