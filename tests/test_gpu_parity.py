@@ -32,7 +32,7 @@ def small(name, N, D, bq, causal, dtype=wl.BF16, k_smooth=True, q_smooth=False, 
 SMALL = [
     wl.C1,
     wl.C1.replace(name="tiny_causal", causal=True),
-    small("n192_d64_bq64_causal", 192, 64, 64, True),            # ragged against the 128-query workgroup
+    small("n192_d64_bq64_causal", 192, 64, 64, True),            # ragged against the backward's 128-key workgroup
     small("n320_d128_bq64_causal_qsmooth", 320, 128, 64, True, q_smooth=True),
     # K-smoothing off is only well conditioned without a common K offset: with
     # one, dQ cancels K's mean and a single dS code rounded the other way at a
