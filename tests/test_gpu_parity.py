@@ -33,6 +33,9 @@ SMALL = [
     wl.C1,
     wl.C1.replace(name="tiny_causal", causal=True),
     small("n192_d64_bq64_causal", 192, 64, 64, True),            # ragged against the backward's 128-key workgroup
+    # a single 64-token block: one forward tile, one key block of two
+    small("n64_d64_bq64_causal", 64, 64, 64, True),
+    small("n64_d128_bq64", 64, 128, 64, False, q_smooth=True),
     small("n320_d128_bq64_causal_qsmooth", 320, 128, 64, True, q_smooth=True),
     # K-smoothing off is only well conditioned without a common K offset: with
     # one, dQ cancels K's mean and a single dS code rounded the other way at a
