@@ -42,6 +42,8 @@ SMALL = [
     # .5 boundary moves dQ by ~1e-3 (the method keeps K-smoothing on for this).
     small("n384_d128_nosmooth", 384, 128, 128, False, k_smooth=False, k_offset=0.0),
     small("n256_d64_fp16_causal", 256, 64, 128, True, dtype=wl.FP16),
+    small("n320_d128_fp16_bq64_causal", 320, 128, 64, True, dtype=wl.FP16),
+    small("n256_d128_fp16_qsmooth_b2h3", 256, 128, 128, False, dtype=wl.FP16, q_smooth=True, B=2, H=3),
     small("n256_d128_qsmooth", 256, 128, 128, False, q_smooth=True, sigma=3.0),
     small("n512_d128_causal_b2", 512, 128, 128, True, B=2, H=1),
     # the INT8-dP ablation: ragged, bq=64 with d=64, Q-smoothing, fp16
@@ -61,6 +63,7 @@ SMALL = [
     wl.C1.replace(name="tiny_fp8", fp8=True),
     small("n256_d128_causal_fp8", 256, 128, 128, True).replace(fp8=True),
     small("n192_d64_bq64_fp8", 192, 64, 64, False).replace(fp8=True),
+    small("n256_d128_fp16_causal_fp8", 256, 128, 128, True, dtype=wl.FP16).replace(fp8=True),
     small("n320_d128_bq64_causal_qsmooth_fp8", 320, 128, 64, True, q_smooth=True).replace(fp8=True),
     small("n256_d64_fp16_causal_qknorm_fp8", 256, 64, 128, True, dtype=wl.FP16).replace(fp8=True,
                                                                                         qk_norm_fused=True),
