@@ -59,6 +59,74 @@ def measured_traffic(call: str):
         return None
 
 
+SQ_FILE = os.path.join(ROOT, "profiles", "sq_utilisation.json")
+SQ_KERNELS = ("fwd_kernel", "bwd_kernel", "dq_kernel")
+
+
+def sq_from(directory):
+    """Write profiles/sq_utilisation.json (and print its table rows) from
+    rocprofv3 --pmc runs of one bench step under `directory` holding the SQ
+    counters below.  Derived per kernel, with T = GRBM_GUI_ACTIVE / 8 (the
+    counter is summed over the eight XCDs), 1024 SIMDs and 256 CUs: VALU issue
+    busy = 4 cycles x SQ_INSTS_VALU (MFMA included) per SIMD over T; MFMA busy
+    = SQ_VALU_MFMA_BUSY_CYCLES per SIMD over T; LDS busy = SQ_LDS_IDX_ACTIVE
+    per CU over T; instructions per 64 unmasked (query, key) pairs of the
+    d=128 N=8192 causal workload."""
+    import csv
+    import glob
+    from bit_trainable_attention_block_amd import workloads as wl
+    sums = {}
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(path)):
+            name = r["Kernel_Name"].replace("sage::(anonymous namespace)::", "").replace("void ", "")
+            name = name.split("(")[0].split("<")[0].strip()
+            if name in SQ_KERNELS:
+                d = sums.setdefault(name, {})
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    cfg = wl.C3
+    pairs64 = cfg.attention_ops()[0] / (4 * cfg.D) / 64
+    out = {}
+    for k in SQ_KERNELS:
+        v = sums[k]
+        T = v["GRBM_GUI_ACTIVE"] / 8
+        out[k] = {
+            "cycles": T,
+            "valu_issue_busy": 4 * v["SQ_INSTS_VALU"] / (1024 * T),
+            "mfma_busy": v["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * T),
+            "mfma_valu_coexec": v["SQ_VALU_MFMA_COEXEC_CYCLES"] / (1024 * T),
+            "lds_busy": v["SQ_LDS_IDX_ACTIVE"] / (256 * T),
+            "waves_waiting_on_dependency": v["SQ_WAIT_INST_ANY"] / v["SQ_WAVE_CYCLES"],
+            "waves_issuing": v["SQ_ACTIVE_INST_ANY"] / v["SQ_WAVE_CYCLES"],
+            "valu_per_64_pairs": (v["SQ_INSTS_VALU"] - v["SQ_INSTS_MFMA"]) / pairs64,
+            "mfma_per_64_pairs": v["SQ_INSTS_MFMA"] / pairs64,
+            "exp_per_64_pairs": v["SQ_INSTS_VALU_TRANS_F32"] / pairs64,
+            "salu_per_64_pairs": v["SQ_INSTS_SALU"] / pairs64,
+        }
+    doc = {"source_hash": kernel_source_hash(), "workload": "d128_n8k_causal_qknorm", "kernels": out}
+    os.makedirs(os.path.dirname(SQ_FILE), exist_ok=True)
+    with open(SQ_FILE, "w") as f:
+        json.dump(doc, f, indent=1)
+    for k, d in out.items():
+        print(f"| `{k}` | {d['cycles']/1e6:.3f} | {d['valu_issue_busy']:.0%} | {d['mfma_busy']:.1%} | "
+              f"{d['mfma_valu_coexec']:.1%} | {d['lds_busy']:.1%} | {d['waves_waiting_on_dependency']:.0%} | "
+              f"{d['waves_issuing']:.0%} | {d['valu_per_64_pairs']:.1f} | {d['mfma_per_64_pairs']:.2f} | "
+              f"{d['exp_per_64_pairs']:.2f} | {d['salu_per_64_pairs']:.1f} |")
+
+
+def measured_sq(kernel: str):
+    """The committed shader-pipe figures of `kernel` (profiles/sq_utilisation.json),
+    or None when absent or taken on different kernel sources."""
+    try:
+        with open(SQ_FILE) as f:
+            t = json.load(f)
+        if t.get("source_hash") != kernel_source_hash():
+            return None
+        d = t["kernels"][kernel]
+        return {"valu_issue_busy": round(d["valu_issue_busy"], 3), "mfma_busy": round(d["mfma_busy"], 3)}
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 # kernels of each C-ABI call (by name prefix in the counter output)
 CALL_KERNELS = {
     "sage_quantize": ("zero_f64_kernel", "quant_v_ksum_kernel", "quant_q_kernel", "quant_k_kernel"),
@@ -230,12 +298,18 @@ def main():
     ap.add_argument("--traffic-from", default="",
                     help="summarise rocprofv3 FETCH_SIZE/WRITE_SIZE runs in this directory into "
                          "profiles/traffic.json (no GPU needed) and exit")
+    ap.add_argument("--sq-from", default="",
+                    help="summarise rocprofv3 SQ counter runs in this directory into "
+                         "profiles/sq_utilisation.json (no GPU needed) and exit")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run one plain device-to-device copy of this many MiB (the known-size "
                          "reference that scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
     if args.traffic_from:
         traffic_from(args.traffic_from, 1024 << 20)
+        return
+    if args.sq_from:
+        sq_from(args.sq_from)
         return
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
@@ -330,7 +404,10 @@ def main():
     roofline = {"bound": "mfma", "kernel": "sage_bwd", "achieved": round(bwd_tops, 2), "peak": INT8_PEAK_TOPS,
                 "unit": "TFLOP/s", "frac": round(bwd_tops / INT8_PEAK_TOPS, 4),
                 "traffic": traffic,
-                "mixed_ceiling": round(5.0 / (4.0 / INT8_PEAK_TOPS + 1.0 / BF16_PEAK_TFLOPS), 1)}
+                "mixed_ceiling": round(5.0 / (4.0 / INT8_PEAK_TOPS + 1.0 / BF16_PEAK_TFLOPS), 1),
+                # bwd_kernel's shader-pipe use from the committed SQ counter summary
+                # (null once the kernels have changed since it was taken)
+                "counters": measured_sq("bwd_kernel")}
 
     fwd_path_ms = call_ms["sage_quantize"] + call_ms["sage_fwd"]
     bwd_path_ms = call_ms["sage_bwd_pre"] + call_ms["sage_bwd"]
