@@ -10,8 +10,9 @@ the logsumexp L are kept for the backward (about 3 bytes per element plus
 the 16-bit copy of V: the backward recomputes S and P from the codes, it
 does not keep them).  Backward: sage_bwd_pre on the incoming dO, then
 sage_bwd.  The library computes every step; this module only allocates the
-buffers, passes pointers and the current stream, and casts the float32
-gradients to the input dtype.  Without libsage.so the calls raise.
+buffers and passes pointers and the current stream; sage_cast_grads rounds
+the float32 gradients to the input dtype.  Without libsage.so the calls
+raise.
 """
 from __future__ import annotations
 
@@ -59,7 +60,8 @@ class SageAttentionFunction(torch.autograd.Function):
             Q, K = ctx.saved_tensors[2:]
             bd.qk_norm_bwd(sh, Q, K, ctx.qt, dQ, dK)
         ctx.qt = None
-        return dQ.to(O.dtype), dK.to(O.dtype), dV.to(O.dtype), None, None, None, None, None, None, None
+        dQ, dK, dV = bd.cast_grads(sh, dQ, dK, dV)   # float32 -> the input dtype, in the library
+        return dQ, dK, dV, None, None, None, None, None, None, None
 
 
 def sage_attention(Q, K, V, causal: bool = False, k_smooth: bool = True, q_smooth: bool = False,

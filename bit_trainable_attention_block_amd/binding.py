@@ -61,6 +61,7 @@ SIGNATURES = {
     "sage_last_hip_error": (ctypes.c_int, []),
     "sage_version": (ctypes.c_char_p, []),
     "sage_qk_norm_bwd": (ctypes.c_int, [ctypes.POINTER(c_shape), _P, _P, ctypes.POINTER(c_qtensors), _P, _P, _P]),
+    "sage_cast_grads": (ctypes.c_int, [ctypes.POINTER(c_shape), _P, _P, _P, _P, _P, _P, _P]),
     # include/sage_probe.h (measurement aid)
     "sage_probe_mfma_i8": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _P, _P]),
     "sage_probe_fp8_products": (ctypes.c_int, [_P, _P, _P, _P, _P]),
@@ -245,6 +246,18 @@ def qk_norm_bwd(sh: Shape, Q, K, qt, dQ, dK, stream=None):
     _check(load().sage_qk_norm_bwd(ctypes.byref(cs), _ptr(Q), _ptr(K), ctypes.byref(_qstruct(qt)), _ptr(dQ),
                                    _ptr(dK), _stream(stream)), "sage_qk_norm_bwd")
     return dQ, dK
+
+
+def cast_grads(sh: Shape, dQ=None, dK=None, dV=None, stream=None):
+    """The float32 gradients (any subset) rounded to the shape's 16-bit I/O
+    dtype by the library (nearest, ties to even); returns the 16-bit tensors
+    (None where the input was None)."""
+    out = [None if t is None else torch.empty(t.shape, dtype=sh.torch_dtype, device=t.device)
+           for t in (dQ, dK, dV)]
+    cs = sh.c()
+    _check(load().sage_cast_grads(ctypes.byref(cs), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(out[0]), _ptr(out[1]),
+                                  _ptr(out[2]), _stream(stream)), "sage_cast_grads")
+    return tuple(out)
 
 
 def probe_mfma_i8(blocks: int, iters: int, clk: torch.Tensor, stream=None):

@@ -151,6 +151,21 @@ int sage_qk_norm_bwd(const sage_shape* shape, const void* Q, const void* K, cons
     return finish(sage::launch_qk_norm_bwd(d, Q, K, qk->rq, qk->rk, dQ, dK, reinterpret_cast<hipStream_t>(stream)));
 }
 
+int sage_cast_grads(const sage_shape* shape, const float* dQ, const float* dK, const float* dV, void* dQ16,
+                    void* dK16, void* dV16, sage_stream_t stream) {
+    sage::Dims d;
+    int st = check_shape(shape, d);
+    if (st != SAGE_OK) return st;
+    const float* src[3] = {dQ, dK, dV};
+    void* dst[3] = {dQ16, dK16, dV16};
+    for (int t = 0; t < 3; ++t) {
+        if ((src[t] == nullptr) != (dst[t] == nullptr)) return SAGE_EINVAL;
+        if (src[t] != nullptr && !ptrs_ok(src[t], dst[t])) return SAGE_EINVAL;
+    }
+    if (empty(d) || (dQ == nullptr && dK == nullptr && dV == nullptr)) return SAGE_OK;
+    return finish(sage::launch_cast_grads(d, src, dst, reinterpret_cast<hipStream_t>(stream)));
+}
+
 const char* sage_status_str(int status) {
     switch (status) {
         case SAGE_OK: return "ok";

@@ -573,4 +573,47 @@ hipError_t launch_bwd_pre(const Dims& d, const void* O, const void* dO, const sa
     return d.D == 128 ? bwd_pre_impl<false, 128>(d, O, dO, out, s) : bwd_pre_impl<false, 64>(d, O, dO, out, s);
 }
 
+
+namespace {
+
+// Eight float32 gradient elements per thread -> eight 16-bit values (two
+// 16-byte loads, one 16-byte store); tensor t = blockIdx.y.  n8 = elements / 8.
+struct CastArgs {
+    const float* src[3];
+    u16* dst[3];
+};
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void cast_grads_kernel(CastArgs a, size_t n8) {
+    const float* src = a.src[blockIdx.y];
+    u16* dst = a.dst[blockIdx.y];
+    if (src == nullptr) return;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += (size_t)gridDim.x * blockDim.x) {
+        const float4 lo = reinterpret_cast<const float4*>(src)[2 * i];
+        const float4 hi = reinterpret_cast<const float4*>(src)[2 * i + 1];
+        const float x[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        v4i out;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            out[e] = (int)((uint32_t)from_f32<BF16>(x[2 * e]) | ((uint32_t)from_f32<BF16>(x[2 * e + 1]) << 16));
+        reinterpret_cast<v4i*>(dst)[i] = out;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_cast_grads(const Dims& d, const float* const src[3], void* const dst[3], hipStream_t s) {
+    CastArgs a;
+    for (int t = 0; t < 3; ++t) {
+        a.src[t] = src[t];
+        a.dst[t] = static_cast<u16*>(dst[t]);
+    }
+    const size_t n8 = (size_t)d.BH() * d.head_elems() / 8;   // D is 64 or 128: whole groups of eight
+    const size_t want = (n8 + 255) / 256;
+    const dim3 grid((unsigned)(want < 8192 ? want : 8192), 3);
+    if (d.bf16) cast_grads_kernel<true><<<grid, 256, 0, s>>>(a, n8);
+    else cast_grads_kernel<false><<<grid, 256, 0, s>>>(a, n8);
+    return hipGetLastError();
+}
+
 }  // namespace sage

@@ -222,6 +222,23 @@ int sage_bwd(const sage_shape* shape, const sage_qtensors* qk, const sage_dotens
 int sage_qk_norm_bwd(const sage_shape* shape, const void* Q, const void* K, const sage_qtensors* qk, float* dQ,
                      float* dK, sage_stream_t stream);
 
+/*
+ * sage_cast_grads — the 16-bit form of the gradients: each float32 element
+ * of dQ, dK and dV rounded to the shape's I/O dtype (bf16 or fp16) to
+ * nearest, ties to even; infinities and NaNs stay infinities and (quiet)
+ * NaNs, fp16 overflow gives infinity.  The pages fix no gradient dtype
+ * (their training runs in BF16, SageBwd method summary, training setup);
+ * sage_bwd's outputs stay float32, and this is the optional cast of them.
+ * dQ, dK, dV: [B,H,N,D] float32 inputs (sage_bwd's, or sage_qk_norm_bwd's
+ * in-place results); dQ16, dK16, dV16: [B,H,N,D] 16-bit outputs, written
+ * once.  Each input/output pair may be left out (both NULL; all three left
+ * out, or an empty shape, is a no-op); all pointers given must be 16-byte
+ * aligned.  Errors: SAGE_EINVAL for a pair with one NULL or a misaligned
+ * pointer; nothing launched then.
+ */
+int sage_cast_grads(const sage_shape* shape, const float* dQ, const float* dK, const float* dV, void* dQ16,
+                    void* dK16, void* dV16, sage_stream_t stream);
+
 /* Text for a status code (static storage). */
 const char* sage_status_str(int status);
 /* HIP error code of the most recent SAGE_EHIP in this thread (0 if none). */

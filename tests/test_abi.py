@@ -98,6 +98,7 @@ def test_bad_shapes_rejected_by_every_call(lib, kw, code):
     assert lib.sage_fwd(ctypes.byref(s), ctypes.byref(qt), FAKE, FAKE, None) == code
     assert lib.sage_bwd_pre(ctypes.byref(s), FAKE, FAKE, ctypes.byref(dot), None) == code
     assert lib.sage_bwd(ctypes.byref(s), ctypes.byref(qt), ctypes.byref(dot), FAKE, FAKE, FAKE, FAKE, FAKE, None) == code
+    assert lib.sage_cast_grads(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == code
     assert lib.sage_quantize_workspace_bytes(ctypes.byref(s)) == 0
     assert lib.sage_bwd_workspace_bytes(ctypes.byref(s)) == 0
 
@@ -152,6 +153,22 @@ def test_empty_problem_is_a_no_op(lib):
         assert lib.sage_fwd(ctypes.byref(s), None, None, None, None) == bd.SAGE_OK
         assert lib.sage_bwd_pre(ctypes.byref(s), None, None, None, None) == bd.SAGE_OK
         assert lib.sage_bwd(ctypes.byref(s), None, None, None, None, None, None, None, None) == bd.SAGE_OK
+
+
+def test_cast_grads_checks(lib):
+    s = ctypes.byref(_shape())
+    f = lib.sage_cast_grads
+    assert f(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == bd.SAGE_EINVAL
+    # a pair with one side missing, or a misaligned side
+    assert f(s, FAKE, None, None, None, None, None, None) == bd.SAGE_EINVAL
+    assert f(s, None, None, None, FAKE, None, None, None) == bd.SAGE_EINVAL
+    assert f(s, FAKE, FAKE, None, FAKE, FAKE, FAKE, None) == bd.SAGE_EINVAL
+    assert f(s, FAKE + 4, None, None, FAKE, None, None, None) == bd.SAGE_EINVAL
+    assert f(s, None, FAKE, None, None, FAKE + 2, None, None) == bd.SAGE_EINVAL
+    # nothing to convert, or an empty problem: no launch
+    assert f(s, None, None, None, None, None, None, None) == bd.SAGE_OK
+    for kw in (dict(B=0), dict(H=0), dict(N=0)):
+        assert f(ctypes.byref(_shape(**kw)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == bd.SAGE_OK
 
 
 def test_workspace_size_and_strings(lib):

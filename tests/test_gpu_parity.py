@@ -198,6 +198,12 @@ def test_autograd_wrapper_matches_the_oracle(causal, qk_norm, fp8):
             # bf16 gradients: the 16-bit rounding (2^-9 relative) bounds the
             # difference on top of the float32 chain bar
             gp.close(f"{name}[0,{h}]", t.grad[0, h].float().cpu().numpy(), r[name], rel_max=chain, cos_min=0.9999)
+            # the RNE-cast gradients against the oracle's own RNE cast: the two
+            # differ by one 16-bit ulp only where a float32 difference of ~1e-5
+            # straddles a rounding boundary
+            ref_rne = torch.from_numpy(np.ascontiguousarray(r[name], dtype=np.float32)).to(torch.bfloat16).float()
+            gp.close(f"{name}_rne[0,{h}]", t.grad[0, h].float().cpu().numpy(), ref_rne.numpy().astype(np.float64),
+                     rel_max=chain, cos_min=0.9999)
 
 
 @pytest.mark.parametrize("fp8", [False, True])
