@@ -63,8 +63,8 @@ SQ_FILE = os.path.join(ROOT, "profiles", "sq_utilisation.json")
 SQ_KERNELS = ("fwd_kernel", "bwd_kernel", "dq_kernel")
 
 
-def sq_from(directory):
-    """Write profiles/sq_utilisation.json (and print its table rows) from
+def sq_from(directory, out_path=SQ_FILE):
+    """Write profiles/sq_utilisation.json (or out_path; and print its table rows) from
     rocprofv3 --pmc runs of one bench step under `directory` holding the SQ
     counters below.  Derived per kernel, with T = GRBM_GUI_ACTIVE / 8 (the
     counter is summed over the eight XCDs), 1024 SIMDs and 256 CUs: VALU issue
@@ -103,14 +103,15 @@ def sq_from(directory):
             "salu_per_64_pairs": v["SQ_INSTS_SALU"] / pairs64,
         }
     doc = {"source_hash": kernel_source_hash(), "workload": "d128_n8k_causal_qknorm", "kernels": out}
-    os.makedirs(os.path.dirname(SQ_FILE), exist_ok=True)
-    with open(SQ_FILE, "w") as f:
+    os.makedirs(os.path.dirname(out_path), exist_ok=True)
+    with open(out_path, "w") as f:
         json.dump(doc, f, indent=1)
     for k, d in out.items():
         print(f"| `{k}` | {d['cycles']/1e6:.3f} | {d['valu_issue_busy']:.0%} | {d['mfma_busy']:.1%} | "
               f"{d['mfma_valu_coexec']:.1%} | {d['lds_busy']:.1%} | {d['waves_waiting_on_dependency']:.0%} | "
               f"{d['waves_issuing']:.0%} | {d['valu_per_64_pairs']:.1f} | {d['mfma_per_64_pairs']:.2f} | "
               f"{d['exp_per_64_pairs']:.2f} | {d['salu_per_64_pairs']:.1f} |")
+    return doc
 
 
 def measured_sq(kernel: str):

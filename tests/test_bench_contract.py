@@ -11,3 +11,42 @@ def test_more_than_one_gpu_is_refused_with_a_message():
                        text=True, timeout=300, cwd=ROOT)
     assert r.returncode == 2
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_sq_summary_derivation(tmp_path):
+    """bench.sq_from on a synthetic counter file: the derived figures follow
+    from the counters by the stated formulas (T = GRBM_GUI_ACTIVE / 8 XCDs,
+    1024 SIMDs, 256 CUs, 4 cycles per VALU issue, per 64 unmasked pairs of the
+    d=128 N=8192 causal workload: 2*16*8192^2/2/64 = 16 777 216 groups)."""
+    import csv
+    import json
+    sys.path.insert(0, ROOT)
+    import bench
+    T = 1_000_000.0
+    counters = {"GRBM_GUI_ACTIVE": 8 * T, "SQ_INSTS_VALU": 0.5 * 1024 * T / 4 + 16_777_216.0,
+                "SQ_INSTS_MFMA": 16_777_216.0, "SQ_VALU_MFMA_BUSY_CYCLES": 0.25 * 1024 * T,
+                "SQ_VALU_MFMA_COEXEC_CYCLES": 0.1 * 1024 * T, "SQ_LDS_IDX_ACTIVE": 0.3 * 256 * T,
+                "SQ_WAIT_INST_ANY": 20.0, "SQ_ACTIVE_INST_ANY": 30.0, "SQ_WAVE_CYCLES": 100.0,
+                "SQ_INSTS_VALU_TRANS_F32": 2 * 16_777_216.0, "SQ_INSTS_SALU": 3 * 16_777_216.0}
+    d = tmp_path / "sq"
+    d.mkdir()
+    with open(d / "x_counter_collection.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for i, k in enumerate(bench.SQ_KERNELS):
+            for c, v in counters.items():
+                # two rows per counter (e.g. two passes' shares) sum to the value
+                w.writerow([i, f"void sage::(anonymous namespace)::{k}<true>(int)", c, v / 2])
+                w.writerow([i, f"void sage::(anonymous namespace)::{k}<true>(int)", c, v / 2])
+    out = tmp_path / "sq.json"
+    doc = bench.sq_from(str(d), str(out))
+    assert json.load(open(out)) == json.loads(json.dumps(doc))
+    for k in bench.SQ_KERNELS:
+        r = doc["kernels"][k]
+        assert abs(r["cycles"] - T) < 1e-6
+        assert abs(r["valu_issue_busy"] - (0.5 + 4 * 16_777_216.0 / (1024 * T))) < 1e-9
+        assert abs(r["mfma_busy"] - 0.25) < 1e-12 and abs(r["mfma_valu_coexec"] - 0.1) < 1e-12
+        assert abs(r["lds_busy"] - 0.3) < 1e-12
+        assert abs(r["waves_waiting_on_dependency"] - 0.2) < 1e-12 and abs(r["waves_issuing"] - 0.3) < 1e-12
+        assert abs(r["valu_per_64_pairs"] - 0.5 * 1024 * T / 4 / 16_777_216.0) < 1e-9
+        assert r["mfma_per_64_pairs"] == 1.0 and r["exp_per_64_pairs"] == 2.0 and r["salu_per_64_pairs"] == 3.0
