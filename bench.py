@@ -288,6 +288,55 @@ def copy_gbps(mib=512, reps=5):
     return 2 * n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
 
+def sweep(steps, warmup):
+    """One JSON line per full-size workload (not the default headline line):
+    the four calls' mean times (HIP events on the launch stream) and the
+    forward, backward and whole-step TOPS in the FlashAttention convention."""
+    import numpy as np
+    import torch
+    from bit_trainable_attention_block_amd import binding as bd
+    from bit_trainable_attention_block_amd import workloads as wl
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    bd.load()
+    stream = torch.cuda.current_stream()
+    for cfg in (wl.C2, wl.C2_CAUSAL, wl.C3, *wl.C4, wl.C5, wl.C5_QSMOOTH):
+        sh = bd.Shape.of(cfg)
+        x = wl.generate(cfg)
+        Q, K, V, dO = (torch.from_numpy(x[n]["bits"].view(np.int16)).to("cuda").view(sh.torch_dtype)
+                       for n in ("q", "k", "v", "do"))
+        del x
+        qt, dot, bws = bd.alloc_qtensors(sh), bd.alloc_dotensors(sh), bd.bwd_workspace(sh)
+        O = torch.empty(Q.shape, dtype=sh.torch_dtype, device="cuda")
+        L = torch.empty(Q.shape[:3], dtype=torch.float32, device="cuda")
+        dQ, dK, dV = (torch.empty(Q.shape, dtype=torch.float32, device="cuda") for _ in range(3))
+        calls = (lambda: bd.quantize(sh, Q, K, V, out=qt), lambda: bd.fwd(sh, qt, O, L),
+                 lambda: bd.bwd_pre(sh, O, dO, out=dot), lambda: bd.bwd(sh, qt, dot, L, dQ, dK, dV, ws=bws))
+        for _ in range(warmup):
+            for c in calls:
+                c()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+        for k in range(steps):
+            for i, c in enumerate(calls):
+                ev[k][i].record(stream)
+                c()
+            ev[k][4].record(stream)
+        torch.cuda.synchronize()
+        ms = np.mean([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in ev], axis=0)
+        fwd_ops, bwd_ops = cfg.attention_ops()
+        print(json.dumps({"workload": cfg.name, "B": cfg.B, "H": cfg.H, "N": cfg.N, "D": cfg.D,
+                          "causal": cfg.causal, "q_smooth": cfg.q_smooth,
+                          "call_ms": dict(zip(("sage_quantize", "sage_fwd", "sage_bwd_pre", "sage_bwd"),
+                                              (round(float(v), 4) for v in ms))),
+                          "fwd_kernel_tops": round(fwd_ops / (ms[1] * 1e-3) / 1e12, 1),
+                          "bwd_kernel_tops": round(bwd_ops / (ms[3] * 1e-3) / 1e12, 1),
+                          "step_tops": round((fwd_ops + bwd_ops) / (float(ms.sum()) * 1e-3) / 1e12, 1)}),
+              flush=True)
+        del Q, K, V, dO, qt, dot, bws, O, L, dQ, dK, dV
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -302,6 +351,8 @@ def main():
     ap.add_argument("--sq-from", default="",
                     help="summarise rocprofv3 SQ counter runs in this directory into "
                          "profiles/sq_utilisation.json (no GPU needed) and exit")
+    ap.add_argument("--sweep", action="store_true",
+                    help="one JSON line of call times and TOPS per full-size workload, then exit")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run one plain device-to-device copy of this many MiB (the known-size "
                          "reference that scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -311,6 +362,9 @@ def main():
         return
     if args.sq_from:
         sq_from(args.sq_from)
+        return
+    if args.sweep and args.gpus == 1:
+        sweep(args.steps, args.warmup)
         return
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "

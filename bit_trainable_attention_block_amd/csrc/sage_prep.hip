@@ -397,13 +397,29 @@ __global__ __launch_bounds__(kThreads) void quant_k_kernel(
     store_codes<C64N, R, D>(codes, kt + head + (size_t)row0 * D);
 
     if constexpr (QS) {
-        // thread -> (key n = t % 64, query blocks i = t / 64 + 4 * step)
+        // thread -> (key n = t % 64, query blocks i = t / 64 + 4 r + 32 pass,
+        // r = 0..7): eight independent float64 sums per thread, each taken over
+        // c in order; the wave's mu_Q rows are wave-uniform reads
+        constexpr int RB = 8;
         const int n = threadIdx.x & 63;
-        for (int i = threadIdx.x >> 6; i < Tm; i += 4) {
-            const float* mq = mu_q + ((size_t)bh * Tm + i) * D;
-            double acc = 0.0;
-            for (int c = 0; c < D; ++c) acc += (double)mq[c] * (double)ksm[n][c];
-            qk_bias[((size_t)bh * Tm + i) * N + row0 + n] = (float)(acc * scale);
+        const int wq = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        for (int i0 = wq; i0 < Tm; i0 += 4 * RB) {
+            const float* mq[RB];
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+                const int i = i0 + 4 * r < Tm ? i0 + 4 * r : i0;   // rows past the end repeat i0, not stored
+                mq[r] = mu_q + ((size_t)bh * Tm + i) * D;
+            }
+            double acc[RB] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+#pragma unroll 8
+            for (int c = 0; c < D; ++c) {
+                const double kv = (double)ksm[n][c];
+#pragma unroll
+                for (int r = 0; r < RB; ++r) acc[r] += (double)mq[r][c] * kv;
+            }
+#pragma unroll
+            for (int r = 0; r < RB; ++r)
+                if (i0 + 4 * r < Tm) qk_bias[((size_t)bh * Tm + i0 + 4 * r) * N + row0 + n] = (float)(acc[r] * scale);
         }
     }
 }
