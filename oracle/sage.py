@@ -563,30 +563,3 @@ def run_head(Q, K, V, dO, sh: Shape, quant=True) -> Dict[str, np.ndarray]:
         out["dK_in"] = rms_norm_backward(K, qz.rk, dK, quant)
     return out
 
-
-def run(inputs: Dict[str, np.ndarray], sh: Shape, quant=True) -> Dict[str, np.ndarray]:
-    """All heads of [B, H, N, D] float inputs ``q``, ``k``, ``v``, ``do``.
-    Returns stacked outputs; codes as int8 (E4M3: their bytes as uint8),
-    scales and means as float32 when quant is on."""
-    Q, K, V, dO = (np.asarray(inputs[n], dtype=F64) for n in ("q", "k", "v", "do"))
-    B, H, N, D = Q.shape
-    names = ["Qc", "sQ", "Kc", "sK", "Vc", "sV", "mu_k", "mu_q", "O", "L", "delta", "dOc", "sdO",
-             "dQ", "dK", "dV"]
-    out = {n: [] for n in names}
-    for b in range(B):
-        for h in range(H):
-            r = run_head(Q[b, h], K[b, h], V[b, h], dO[b, h], sh, quant)
-            qz = r["qz"]
-            for n in ("Qc", "sQ", "Kc", "sK", "Vc", "sV", "mu_k", "mu_q"):
-                out[n].append(getattr(qz, n))
-            for n in ("O", "L", "delta", "dOc", "sdO", "dQ", "dK", "dV"):
-                out[n].append(r[n])
-    res = {}
-    for n, vals in out.items():
-        a = np.stack(vals).reshape((B, H) + np.shape(vals[0]))
-        if quant and n in ("Qc", "Kc", "Vc", "dOc"):
-            a = e4m3_bits(a) if sh.fp8 else a.astype(np.int8)
-        elif quant and n in ("sQ", "sK", "sV", "mu_k", "mu_q", "L", "delta", "sdO"):
-            a = a.astype(F32)
-        res[n] = a
-    return res

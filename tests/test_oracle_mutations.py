@@ -1,9 +1,9 @@
 """Plant plausible mistakes in a copy of the oracle and check the pins catch them.
 
-Each mutation edits one line of oracle/sage.py's source text, loads the edited
-copy as a separate module, swaps its functions into ``oracle.sage`` for the
-duration of the test, and runs a few pins, at least one of which must fail.
-Nothing here touches a GPU.
+Each mutation edits one line of oracle/sage.py's (or oracle/metrics.py's)
+source text, loads the edited copy as a separate module, swaps its functions
+into ``oracle.sage`` (``oracle.metrics``) for the duration of the test, and
+runs a few pins, at least one of which must fail.  Nothing here touches a GPU.
 """
 import inspect
 import sys
@@ -12,13 +12,16 @@ import types
 import numpy as np
 import pytest
 
+import oracle.metrics as metrics_mod
 import oracle.sage as sage_mod
 from tests import test_oracle_bwd as tb
 from tests import test_oracle_fp8 as tf8
 from tests import test_oracle_fwd as tf
+from tests import test_oracle_metrics as tm
 from tests import test_oracle_quant as tq
 
 SRC = inspect.getsource(sage_mod)
+METRICS_SRC = inspect.getsource(metrics_mod)
 
 MUTATIONS = {
     "drop_qsmooth_bias": ("S = S + qsmooth_bias(qz, i, j, sh)[None, :]", "S = S"),
@@ -83,14 +86,15 @@ PINS = [
 ]
 
 
-def _catches(mod):
-    saved = {k: getattr(sage_mod, k) for k in dir(sage_mod) if not k.startswith("__")}
+def _catches(mod, target=sage_mod, pins=None):
+    pins = PINS if pins is None else pins
+    saved = {k: getattr(target, k) for k in dir(target) if not k.startswith("__")}
     try:
         for k in saved:
             if hasattr(mod, k):
-                setattr(sage_mod, k, getattr(mod, k))
+                setattr(target, k, getattr(mod, k))
         caught = []
-        for idx, pin in enumerate(PINS):
+        for idx, pin in enumerate(pins):
             try:
                 with np.errstate(all="ignore"):
                     pin()
@@ -99,7 +103,7 @@ def _catches(mod):
         return caught
     finally:
         for k, v in saved.items():
-            setattr(sage_mod, k, v)
+            setattr(target, k, v)
 
 
 @pytest.mark.slow
@@ -110,3 +114,35 @@ def test_pins_catch_planted_mistake(name):
 
 def test_unmutated_copy_passes_all_pins():
     assert _catches(_load("oracle_sage_clean", SRC)) == []
+
+
+# Mistakes in the metrics the GPU gate relies on (cosine and relative L2) and
+# in the two reported ones.
+METRIC_MUTATIONS = {
+    "cos_numerator_self_dot": ("np.dot(a, b) / den", "np.dot(a, a) / den"),
+    "cos_no_sqrt": ("den = np.sqrt(np.dot(a, a) * np.dot(b, b))", "den = np.dot(a, a) * np.dot(b, b)"),
+    "cos_zero_branch": ("else float(np.array_equal(a, b))", "else 1.0"),
+    "rel_l2_divides_by_x": ("np.linalg.norm(a - b) / nb)", "np.linalg.norm(a - b) / np.linalg.norm(a))"),
+    "rel_l2_squared": ("np.linalg.norm(a - b) / nb)", "np.linalg.norm(a - b) ** 2 / nb)"),
+    "rel_l1_abs_outside": ("np.sum(np.abs(a - b)) / sb", "np.abs(np.sum(a - b)) / sb"),
+    "rel_l1_divides_by_x": ("sb = np.sum(np.abs(b))", "sb = np.sum(np.abs(a))"),
+    "rmse_no_sqrt": ("np.sqrt(np.mean((a - b) ** 2))", "np.mean((a - b) ** 2)"),
+    "rmse_sum": ("np.sqrt(np.mean((a - b) ** 2))", "np.sqrt(np.sum((a - b) ** 2))"),
+}
+
+METRIC_PINS = [getattr(tm, n) for n in dir(tm) if n.startswith("test_") and n not in (
+    "test_positive_rescale", "test_relative_errors_of_a_proportional_perturbation")]
+METRIC_PINS += [lambda: [tm.test_positive_rescale(c) for c in (0.25, 3.0)],
+                lambda: [tm.test_relative_errors_of_a_proportional_perturbation(e) for e in (1e-3, -0.2)]]
+
+
+@pytest.mark.parametrize("name", sorted(METRIC_MUTATIONS))
+def test_metric_pins_catch_planted_mistake(name):
+    old, new = METRIC_MUTATIONS[name]
+    assert METRICS_SRC.count(old) == 1, name
+    mod = _load("oracle_metrics_" + name, METRICS_SRC.replace(old, new))
+    assert _catches(mod, metrics_mod, METRIC_PINS), f"no pin caught the planted mistake {name!r}"
+
+
+def test_unmutated_metrics_pass_all_pins():
+    assert _catches(_load("oracle_metrics_clean", METRICS_SRC), metrics_mod, METRIC_PINS) == []
