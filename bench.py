@@ -247,28 +247,59 @@ def cpu_baseline(cfg):
             "host_cpus": os.cpu_count(), "affinity_cpus": cpus, "blas_threads": 1}
 
 
-def mfma_probe(iters=4000):
-    """Achieved rate of v_mfma_i32_16x16x64_i8 on this device (two 8-wave
-    workgroups per CU, register operands) and the shader clock under it."""
+def mfma_probe(kind="i8", iters=4000):
+    """Achieved rate of v_mfma_i32_16x16x64_i8 (kind "i8") or
+    v_mfma_f32_16x16x32_bf16 ("bf16") on this device (two 8-wave workgroups
+    per CU, register operands) and the shader clock under it."""
     import torch
 
     from bit_trainable_attention_block_amd import binding as bd
+    probe, ops_each, name, spec = {
+        "i8": (bd.probe_mfma_i8, 32768, "v_mfma_i32_16x16x64_i8", INT8_PEAK_TOPS),
+        "bf16": (bd.probe_mfma_bf16, 16384, "v_mfma_f32_16x16x32_bf16", BF16_PEAK_TFLOPS)}[kind]
     blocks = 2 * torch.cuda.get_device_properties(0).multi_processor_count
     clk = torch.zeros(3, dtype=torch.int64, device="cuda")
-    bd.probe_mfma_i8(blocks, 200, clk)
+    probe(blocks, 200, clk)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    bd.probe_mfma_i8(blocks, iters, clk)
+    probe(blocks, iters, clk)
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1)
-    ops = blocks * 8 * iters * 8 * 32768
+    ops = blocks * 8 * iters * 8 * ops_each
     c = [int(v) for v in clk.cpu().tolist()]
     tops = ops / (ms * 1e-3) / 1e12
-    return {"kernel": "v_mfma_i32_16x16x64_i8", "tops": round(tops, 1),
+    return {"kernel": name, "tops": round(tops, 1),
             "clock_ghz": round(c[0] / (c[1] / 100e6) / 1e9, 3) if c[1] else None,
-            "frac_of_spec": round(tops / INT8_PEAK_TOPS, 4)}
+            "frac_of_spec": round(tops / spec, 4)}
+
+
+def bwd_work(cfg):
+    """Algorithmic work of one sage_bwd launch, by dtype: per unmasked
+    (query, key) pair 2*D operations for each of the four INT8 products (S
+    recompute, dV, dK, dQ) and 2*D for the BF16 dP product."""
+    pairs = float(cfg.B * cfg.H) * cfg.N * cfg.N * (0.5 if cfg.causal else 1.0)
+    return {"int8_ops": 8.0 * cfg.D * pairs, "bf16_flops": 2.0 * cfg.D * pairs}
+
+
+def mixed_ceiling_tops(work):
+    """Rate (TOP/s) at which that work would run with each product at its own
+    dtype's published dense peak: INT8 at 5.0 POP/s, BF16 at 2.5 PFLOP/s."""
+    ideal_s = work["int8_ops"] / (INT8_PEAK_TOPS * 1e12) + work["bf16_flops"] / (BF16_PEAK_TFLOPS * 1e12)
+    return (work["int8_ops"] + work["bf16_flops"]) / ideal_s / 1e12
+
+
+# Algorithmic HBM bytes per (token, channel) element of the HBM-bound calls,
+# what the method itself must move: sage_quantize reads Q once and K twice
+# (the token mean, then the codes) and V once in 16 bits, and writes one code
+# byte each of Q, K and V (11 B); sage_bwd_pre reads O and dO in 16 bits and
+# writes dO's codes (5 B) plus delta (4 B per row).
+QUANT_ALGO_BYTES = 11.0
+
+
+def bwd_pre_algo_bytes(D):
+    return 5.0 + 4.0 / D
 
 
 def copy_gbps(mib=512, reps=5):
@@ -451,15 +482,22 @@ def main():
     tops = total_ops / (ms_per_step * 1e-3) / 1e12
 
     # dominant kernel: the backward (MFMA-bound).  Algorithmic work per launch:
-    # 10*D INT8-equivalent ops per unmasked (query, key) pair of the B*H heads
-    # (S, dV, dK, dQ in INT8 and dP in bf16 counted as ops), halved for causal.
+    # 8*D INT8 operations (S, dV, dK, dQ) and 2*D BF16 flops (dP) per unmasked
+    # (query, key) pair of the B*H heads.  The peak prices each product at its
+    # own dtype's published dense rate (INT8 5.0 POP/s, BF16 2.5 PFLOP/s), so
+    # `frac` is the fraction of the time the matrix cores would need.
     bwd_ms = call_ms["sage_bwd"]
     bwd_tops = bwd_ops / (bwd_ms * 1e-3) / 1e12
+    work = bwd_work(cfg)
+    peak = mixed_ceiling_tops(work)
     traffic = measured_traffic("sage_bwd")
-    roofline = {"bound": "mfma", "kernel": "sage_bwd", "achieved": round(bwd_tops, 2), "peak": INT8_PEAK_TOPS,
-                "unit": "TFLOP/s", "frac": round(bwd_tops / INT8_PEAK_TOPS, 4),
+    roofline = {"bound": "mfma", "kernel": "sage_bwd", "achieved": round(bwd_tops, 2), "peak": round(peak, 1),
+                "unit": "TOP/s", "frac": round(bwd_tops / peak, 4),
                 "traffic": traffic,
-                "mixed_ceiling": round(5.0 / (4.0 / INT8_PEAK_TOPS + 1.0 / BF16_PEAK_TFLOPS), 1),
+                "peak_basis": "INT8 ops at 5.0 POP/s plus BF16 flops at 2.5 PFLOP/s (published dense)",
+                "work_per_launch": {k: v for k, v in work.items()},
+                # the same achieved rate priced wholly at the INT8 peak
+                "frac_of_int8_peak": round(bwd_tops / INT8_PEAK_TOPS, 4),
                 # bwd_kernel's shader-pipe use from the committed SQ counter summary
                 # (null once the kernels have changed since it was taken)
                 "counters": measured_sq("bwd_kernel")}
@@ -477,21 +515,33 @@ def main():
         "pct_int8_peak_fwd_bwd": round(100 * tops / INT8_PEAK_TOPS, 2),
         "pct_int8_peak_fwd_kernel": round(100 * fwd_ops / (call_ms["sage_fwd"] * 1e-3) / 1e12 / INT8_PEAK_TOPS, 2),
         # the backward against its mixed ceiling (4 INT8 products + 1 BF16 one)
-        "pct_mixed_ceiling_bwd_kernel": round(100 * bwd_tops / roofline["mixed_ceiling"], 2),
+        "pct_mixed_ceiling_bwd_kernel": round(100 * bwd_tops / peak, 2),
     }
-    # second denominator: the INT8 product rate this device achieves, and the
-    # HBM-bound calls against a plain copy (algorithmic bytes per call:
-    # quantise 15 B and the backward pre-pass 7 + 4/D B per (token, channel))
-    probe = mfma_probe()
+    # second denominators: the INT8 and BF16 product rates this device
+    # achieves (the backward's measured mixed ceiling prices each product at
+    # its probed rate), and the HBM-bound calls' algorithmic bytes per second
+    # against the 8 TB/s figure and a plain copy timed here
+    probe = mfma_probe("i8")
+    probe_bf16 = mfma_probe("bf16")
     breakdown["mfma_probe"] = probe
+    breakdown["mfma_probe_bf16"] = probe_bf16
     breakdown["pct_measured_i8_fwd_bwd"] = round(100 * tops / probe["tops"], 2)
+    measured_mixed = (work["int8_ops"] + work["bf16_flops"]) / (
+        work["int8_ops"] / probe["tops"] + work["bf16_flops"] / probe_bf16["tops"])
+    breakdown["bwd_kernel_pct_measured_mixed"] = round(100 * bwd_tops / measured_mixed, 2)
     elems = cfg.B * cfg.H * cfg.N * cfg.D
     cp = copy_gbps()
-    q_gbps = 15 * elems / (call_ms["sage_quantize"] * 1e-3) / 1e9
-    p_gbps = (7 + 4 / cfg.D) * elems / (call_ms["sage_bwd_pre"] * 1e-3) / 1e9
-    breakdown["hbm"] = {"copy_gbps": round(cp, 1), "sage_quantize_gbps": round(q_gbps, 1),
+    q_gbps = QUANT_ALGO_BYTES * elems / (call_ms["sage_quantize"] * 1e-3) / 1e9
+    p_gbps = bwd_pre_algo_bytes(cfg.D) * elems / (call_ms["sage_bwd_pre"] * 1e-3) / 1e9
+    breakdown["hbm"] = {"algo_bytes_per_elem": {"sage_quantize": QUANT_ALGO_BYTES,
+                                                "sage_bwd_pre": round(bwd_pre_algo_bytes(cfg.D), 4)},
+                        "copy_gbps": round(cp, 1),
+                        "sage_quantize_gbps": round(q_gbps, 1),
+                        "sage_quantize_pct_hbm_peak": round(100 * q_gbps / HBM_PEAK_GBS, 1),
                         "sage_quantize_pct_copy": round(100 * q_gbps / cp, 1),
-                        "sage_bwd_pre_gbps": round(p_gbps, 1), "sage_bwd_pre_pct_copy": round(100 * p_gbps / cp, 1)}
+                        "sage_bwd_pre_gbps": round(p_gbps, 1),
+                        "sage_bwd_pre_pct_hbm_peak": round(100 * p_gbps / HBM_PEAK_GBS, 1),
+                        "sage_bwd_pre_pct_copy": round(100 * p_gbps / cp, 1)}
 
     out = {
         "metric": METRIC, "value": round(tops, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,

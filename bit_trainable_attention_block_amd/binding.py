@@ -64,6 +64,7 @@ SIGNATURES = {
     "sage_cast_grads": (ctypes.c_int, [ctypes.POINTER(c_shape), _P, _P, _P, _P, _P, _P, _P]),
     # include/sage_probe.h (measurement aid)
     "sage_probe_mfma_i8": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _P, _P]),
+    "sage_probe_mfma_bf16": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _P, _P]),
     "sage_probe_fp8_products": (ctypes.c_int, [_P, _P, _P, _P, _P]),
 }
 
@@ -265,6 +266,12 @@ def probe_mfma_i8(blocks: int, iters: int, clk: torch.Tensor, stream=None):
     each wave issuing iters x 8 INT8 16x16x64 products; clk (3 int64 on the
     device) receives the shader cycles and 100 MHz ticks of workgroup 0."""
     _check(load().sage_probe_mfma_i8(blocks, iters, _ptr(clk), _stream(stream)), "sage_probe_mfma_i8")
+
+
+def probe_mfma_bf16(blocks: int, iters: int, clk: torch.Tensor, stream=None):
+    """Measurement aid (include/sage_probe.h): as probe_mfma_i8, on the BF16
+    16x16x32 product."""
+    _check(load().sage_probe_mfma_bf16(blocks, iters, _ptr(clk), _stream(stream)), "sage_probe_mfma_bf16")
 
 
 def probe_fp8_products(a, b, c32, c128, stream=None):

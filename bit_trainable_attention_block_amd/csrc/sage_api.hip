@@ -183,6 +183,11 @@ int sage_probe_mfma_i8(int blocks, int iters, unsigned long long* clk, hipStream
     return finish(sage::launch_probe_mfma_i8(blocks, iters, clk, stream));
 }
 
+int sage_probe_mfma_bf16(int blocks, int iters, unsigned long long* clk, hipStream_t stream) {
+    if (blocks < 1 || iters < 1 || clk == nullptr || !aligned(clk, 8)) return SAGE_EINVAL;
+    return finish(sage::launch_probe_mfma_bf16(blocks, iters, clk, stream));
+}
+
 int sage_probe_fp8_products(const int8_t* a, const int8_t* b, float* c32, float* c128, hipStream_t stream) {
     if (!ptrs_ok(a, b, c32, c128)) return SAGE_EINVAL;
     return finish(sage::launch_probe_fp8_products(a, b, c32, c128, stream));

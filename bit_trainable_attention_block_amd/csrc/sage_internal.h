@@ -37,6 +37,7 @@ hipError_t launch_qk_norm_bwd(const Dims& d, const void* Q, const void* K, const
                               float* dQ, float* dK, hipStream_t s);
 hipError_t launch_cast_grads(const Dims& d, const float* const src[3], void* const dst[3], hipStream_t s);
 hipError_t launch_probe_mfma_i8(int blocks, int iters, unsigned long long* clk, hipStream_t s);
+hipError_t launch_probe_mfma_bf16(int blocks, int iters, unsigned long long* clk, hipStream_t s);
 hipError_t launch_probe_fp8_products(const int8_t* a, const int8_t* b, float* c32, float* c128,
                                      hipStream_t stream);
 

@@ -1,6 +1,7 @@
-// Measurement aids (declared in include/sage_probe.h): the achieved rate of
-// the INT8 16x16x64 matrix product and the shader clock under that load; the
-// results of the two E4M3 matrix products on given operands.
+// Measurement aids (declared in include/sage_probe.h): the achieved rates of
+// the INT8 16x16x64 and the BF16 16x16x32 matrix products and the shader
+// clock under that load; the results of the two E4M3 matrix products on
+// given operands.
 #include "sage_device.h"
 #include "sage_internal.h"
 
@@ -36,6 +37,37 @@ __global__ __launch_bounds__(512, 2) void probe_mfma_i8_kernel(int iters, unsign
     }
 }
 
+// The same shape of load on v_mfma_f32_16x16x32_bf16 (16 384 flops each).
+// The operands are small normal bf16 values (1 + k/128), so the float32
+// accumulators stay finite and exact enough for any iters the caller allows.
+__global__ __launch_bounds__(512, 2) void probe_mfma_bf16_kernel(int iters, unsigned long long* clk) {
+    const int lane = threadIdx.x & 63;
+    const uint32_t one = 0x3F803F80u;   // two bf16 1.0
+    const v4i a = v4i{(int)(one + lane), (int)(one + 2 * lane), (int)one, (int)(one + 3)};
+    const v4i b = v4i{(int)(one + 5), (int)one, (int)(one + (lane & 7)), (int)(one + 1)};
+    v4f acc[kChains];
+#pragma unroll
+    for (int u = 0; u < kChains; ++u) acc[u] = v4f{(float)u, 0.f, 0.f, 0.f};
+    const bool timer = blockIdx.x == 0 && threadIdx.x == 0;
+    unsigned long long t0 = 0, r0 = 0;
+    if (timer) {
+        t0 = __builtin_readcyclecounter();
+        r0 = __builtin_amdgcn_s_memrealtime();
+    }
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int u = 0; u < kChains; ++u) acc[u] = mfma16_h<true>(a, b, acc[u]);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int u = 0; u < kChains; ++u) s += acc[u][0] + acc[u][1] + acc[u][2] + acc[u][3];
+    if (s == -1.f) clk[2] = 1ull;   // keeps the products live
+    if (timer) {
+        clk[0] = __builtin_readcyclecounter() - t0;
+        clk[1] = __builtin_amdgcn_s_memrealtime() - r0;
+    }
+}
+
 // One wave: lane l's 32 E4M3 bytes of a and b feed both E4M3 products, the
 // 16x16x32 one (the first 8 bytes) and the 16x16x128 one (all 32); lane l
 // writes its 4 result registers of each.
@@ -61,6 +93,11 @@ hipError_t launch_probe_fp8_products(const int8_t* a, const int8_t* b, float* c3
 
 hipError_t launch_probe_mfma_i8(int blocks, int iters, unsigned long long* clk, hipStream_t stream) {
     probe_mfma_i8_kernel<<<dim3(blocks), dim3(512), 0, stream>>>(iters, clk);
+    return hipGetLastError();
+}
+
+hipError_t launch_probe_mfma_bf16(int blocks, int iters, unsigned long long* clk, hipStream_t stream) {
+    probe_mfma_bf16_kernel<<<dim3(blocks), dim3(512), 0, stream>>>(iters, clk);
     return hipGetLastError();
 }
 

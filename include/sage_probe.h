@@ -31,6 +31,16 @@ extern "C" {
 int sage_probe_mfma_i8(int blocks, int iters, unsigned long long* clk, hipStream_t stream);
 
 /*
+ * sage_probe_mfma_bf16 is the same measurement on the BF16 matrix product
+ * the backward's dP = dO V^T runs on: each wave issues `iters` rounds of 8
+ * independent v_mfma_f32_16x16x32_bf16 products (16 384 floating-point
+ * operations each) on register operands, beside the published 2.5 PFLOP/s
+ * dense BF16 figure.  Divide blocks * 8 * iters * 8 * 16384 operations by the
+ * elapsed time.  clk, return values and errors as for sage_probe_mfma_i8.
+ */
+int sage_probe_mfma_bf16(int blocks, int iters, unsigned long long* clk, hipStream_t stream);
+
+/*
  * sage_probe_fp8_products runs one wave of the two E4M3 matrix products the
  * E4M3 variant uses (sage_shape.fp8), so that their lane layout and their
  * summation can be checked against exact products:

@@ -199,6 +199,7 @@ def test_probe_rejects_bad_arguments(lib):
     base = ctypes.addressof(buf)
     for blocks, iters, ptr in ((0, 1, base), (1, 0, base), (1, 1, None), (1, 1, base + 4)):
         assert lib.sage_probe_mfma_i8(blocks, iters, ptr, None) == bd.SAGE_EINVAL
+        assert lib.sage_probe_mfma_bf16(blocks, iters, ptr, None) == bd.SAGE_EINVAL
 
 
 def test_fp8_probe_rejects_bad_arguments(lib):

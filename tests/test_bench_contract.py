@@ -50,3 +50,19 @@ def test_sq_summary_derivation(tmp_path):
         assert abs(r["waves_waiting_on_dependency"] - 0.2) < 1e-12 and abs(r["waves_issuing"] - 0.3) < 1e-12
         assert abs(r["valu_per_64_pairs"] - 0.5 * 1024 * T / 4 / 16_777_216.0) < 1e-9
         assert r["mfma_per_64_pairs"] == 1.0 and r["exp_per_64_pairs"] == 2.0 and r["salu_per_64_pairs"] == 3.0
+
+
+def test_backward_roofline_prices_each_product_at_its_own_peak():
+    """d=128 N=8192 causal (B=2, H=16): 2^30 unmasked pairs, 8*128 INT8
+    operations and 2*128 BF16 flops per pair; at 5.0 POP/s and 2.5 PFLOP/s
+    the ideal time is 219.9 + 110.0 us, so the mixed ceiling is
+    5*2^38 ops / 329.9 us = 4166.7 TOP/s."""
+    sys.path.insert(0, ROOT)
+    import bench
+    from bit_trainable_attention_block_amd import workloads as wl
+    w = bench.bwd_work(wl.C3)
+    pairs = 2 * 16 * 8192 * 8192 / 2
+    assert w == {"int8_ops": 8 * 128 * pairs, "bf16_flops": 2 * 128 * pairs}
+    assert abs(bench.mixed_ceiling_tops(w) - 5 / (4 / 5000 + 1 / 2500)) < 1e-9
+    assert abs(bench.mixed_ceiling_tops(w) - 4166.67) < 0.01
+    assert bench.bwd_pre_algo_bytes(128) == 5.03125 and bench.QUANT_ALGO_BYTES == 11.0

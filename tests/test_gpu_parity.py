@@ -110,7 +110,9 @@ FULL = [
     (wl.C2_CAUSAL, [(1, 7)]),
     (wl.C3, [(0, 0), (1, 15)]),
     (wl.C4[0], [(0, 3)]),
+    (wl.C4[1], [(0, 12)]),
     (wl.C4[2], [(0, 17)]),
+    (wl.C4[3], [(0, 24)]),
     (wl.C4[4], [(0, 31)]),
     (wl.C5, [(0, 0), (0, 7)]),
     (wl.C5_QSMOOTH, [(0, 5)]),
@@ -137,7 +139,11 @@ def test_full_size_sampled(cfg, heads):
         dQ, dK, dV = gp.check_bwd(cfg, x, g, b, h, qz, kv_blocks, q_blocks)
         if k == 0:
             gp.report_vs_fpa(cfg, x, g, b, h, q_blocks, kv_blocks, {"O": O, "dQ": dQ, "dK": dK, "dV": dV})
-    # every head: codes of the first Q and K blocks (cheap, bit-exact) and finite outputs
+    # every head: all block scales, the means and the codes of the first Q, K
+    # and V blocks bit-exact (cheap), and finite outputs
+    for b in range(cfg.B):
+        for h in range(cfg.H):
+            gp.check_head_codes(cfg, x, g, b, h)
     for k in ("O", "L", "dQ", "dK", "dV"):
         assert np.all(np.isfinite(g[k])), k
 
