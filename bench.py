@@ -130,7 +130,7 @@ def measured_sq(kernel: str):
 
 # kernels of each C-ABI call (by name prefix in the counter output)
 CALL_KERNELS = {
-    "sage_quantize": ("zero_f64_kernel", "quant_v_ksum_kernel", "quant_q_kernel", "quant_k_kernel"),
+    "sage_quantize": ("quant_v_ksum_kernel", "kmean_kernel", "quant_q_kernel", "quant_k_kernel"),
     "sage_fwd": ("fwd_kernel",),
     "sage_bwd_pre": ("bwd_pre_kernel",),
     "sage_bwd": ("bwd_kernel", "dq_kernel"),

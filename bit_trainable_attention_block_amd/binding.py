@@ -170,7 +170,8 @@ def alloc_qtensors(sh: Shape, device="cuda") -> Dict[str, torch.Tensor]:
         "qk_bias": torch.empty((B, H, sh.Tm, N), **f32) if sh.q_smooth else None,
         "rq": torch.empty((B, H, N), **f32) if sh.qk_norm else None,
         "rk": torch.empty((B, H, N), **f32) if sh.qk_norm else None,
-        "ws": torch.empty((max(1, B * H * D),), dtype=torch.float64, device=device),
+        "ws": torch.empty((max(1, load().sage_quantize_workspace_bytes(ctypes.byref(sh.c())) // 8),),
+                          dtype=torch.float64, device=device),
     }
     return t
 

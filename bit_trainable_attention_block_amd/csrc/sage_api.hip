@@ -85,7 +85,7 @@ extern "C" {
 size_t sage_quantize_workspace_bytes(const sage_shape* shape) {
     sage::Dims d;
     if (check_shape(shape, d) != SAGE_OK) return 0;
-    return (size_t)d.B * d.H * d.D * sizeof(double);
+    return (size_t)d.B * d.H * d.Tn() * d.D * sizeof(double);
 }
 
 int sage_quantize(const sage_shape* shape, const void* Q, const void* K, const void* V,

@@ -212,20 +212,16 @@ __device__ __forceinline__ void store_r16h(const v4i (&raw)[Blk<R, D>::PER_T], u
 
 // ------------------------------------------------------------------ kernels
 
-__global__ void zero_f64_kernel(double* p, int n) {
-    int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) p[i] = 0.0;
-}
-
 // V blocks (64 rows): codes -> vt (C64P), scale -> sv, raw copy -> vr (R16H);
 // with dp_int8 the codes again, as R32 row tiles, -> vr instead of the copy.
-// K blocks (same rows): float64 column sums accumulated into ws[bh][D]
-// (exact: sums of 16-bit values fit float64 without rounding, so the order of
-// the atomic additions does not change the result).
+// K blocks (same rows): the block's float64 column sums -> kpart[bh][j][D]
+// (a fixed summation order inside the block; kmean_kernel adds the blocks in
+// order, so mu_K does not depend on scheduling even where the float64 sums
+// round, as they can for the QK-normed float32 rows).
 template <bool BF16, int D>
 __global__ __launch_bounds__(kThreads) void quant_v_ksum_kernel(
     const u16* __restrict__ K, const u16* __restrict__ V, int N, int8_t* __restrict__ vt,
-    float* __restrict__ sv, u16* __restrict__ vr, double* __restrict__ ws, int k_smooth, int dp_int8,
+    float* __restrict__ sv, u16* __restrict__ vr, double* __restrict__ kpart, int k_smooth, int dp_int8,
     int qk_norm, int fp8) {
     constexpr int R = 64;
     using B = Blk<R, D>;
@@ -268,8 +264,21 @@ __global__ __launch_bounds__(kThreads) void quant_v_ksum_kernel(
 #pragma unroll
             for (int e = 0; e < 8; ++e) part[e] += (double)y[k][e];
         block_colsum<R, D>(part, dred, dsum);
-        if (threadIdx.x < D) atomicAdd(ws + (size_t)bh * D + threadIdx.x, dsum[threadIdx.x]);
+        if (threadIdx.x < D) kpart[((size_t)bh * gridDim.x + j) * D + threadIdx.x] = dsum[threadIdx.x];
     }
+}
+
+// mu_K[bh][c] = f32(sum_j kpart[bh][j][c] / N), the Tn block sums added in
+// block order in float64 (one thread per channel; reads are coalesced across
+// the channels of a block).
+template <int D>
+__global__ __launch_bounds__(D) void kmean_kernel(const double* __restrict__ kpart, int Tn, int N,
+                                                  float* __restrict__ mu_k) {
+    const int bh = blockIdx.x, c = threadIdx.x;
+    const double* p = kpart + (size_t)bh * Tn * D + c;
+    double acc = 0.0;
+    for (int j = 0; j < Tn; ++j) acc += p[(size_t)j * D];
+    mu_k[(size_t)bh * D + c] = (float)(acc / (double)N);
 }
 
 // Q blocks (BQ rows): optional Q-smoothing (QS, mu_q set), codes -> q (R32)
@@ -340,7 +349,7 @@ __global__ __launch_bounds__(kThreads) void quant_q_kernel(const u16* __restrict
 template <bool BF16, int D, bool QS>
 __global__ __launch_bounds__(kThreads) void quant_k_kernel(
     const u16* __restrict__ K, int N, int8_t* __restrict__ k, int8_t* __restrict__ kt,
-    float* __restrict__ sk, float* __restrict__ mu_k, const double* __restrict__ ws, int k_smooth,
+    float* __restrict__ sk, const float* __restrict__ mu_k, int k_smooth,
     const float* __restrict__ mu_q, float* __restrict__ qk_bias, int Tm, double scale, float* __restrict__ rk,
     int fp8) {
     constexpr int R = 64;
@@ -356,14 +365,7 @@ __global__ __launch_bounds__(kThreads) void quant_k_kernel(
     // the block's rows are requested first; the mean arrives meanwhile
     v4i raw[B::PER_T];
     load_block<R, D>(K + head + (size_t)row0 * D, raw);
-    if (threadIdx.x < D) {
-        float mv = 0.f;
-        if (k_smooth) {
-            mv = (float)(ws[(size_t)bh * D + threadIdx.x] / (double)N);
-            if (j == 0) mu_k[(size_t)bh * D + threadIdx.x] = mv;
-        }
-        mu[threadIdx.x] = mv;
-    }
+    if (threadIdx.x < D) mu[threadIdx.x] = k_smooth ? mu_k[(size_t)bh * D + threadIdx.x] : 0.f;
     __syncthreads();
 
     float x[B::PER_T][8];
@@ -517,20 +519,17 @@ hipError_t quantize_impl(const Dims& d, const void* Q, const void* K, const void
                          const sage_qtensors& out, double* ws, hipStream_t s) {
     const int BH = d.BH();
     dim3 blk(kThreads);
-    if (d.k_smooth) {
-        int n = BH * d.D;
-        zero_f64_kernel<<<(n + 255) / 256, 256, 0, s>>>(ws, n);
-    }
     quant_v_ksum_kernel<BF16, D><<<dim3(d.Tn(), BH), blk, 0, s>>>(
         (const u16*)K, (const u16*)V, d.N, out.vt, out.sv, out.vr, ws, d.k_smooth ? 1 : 0, d.dp_int8 ? 1 : 0,
         d.qk_norm ? 1 : 0, d.fp8 ? 1 : 0);
+    if (d.k_smooth) kmean_kernel<D><<<dim3(BH), dim3(D), 0, s>>>(ws, d.Tn(), d.N, out.mu_k);
     auto qq = d.bq == 128 ? (d.q_smooth ? quant_q_kernel<BF16, D, 128, true> : quant_q_kernel<BF16, D, 128, false>)
                           : (d.q_smooth ? quant_q_kernel<BF16, D, 64, true> : quant_q_kernel<BF16, D, 64, false>);
     qq<<<dim3(d.Tm(), BH), blk, 0, s>>>((const u16*)Q, d.N, out.q, out.qt, out.sq, d.q_smooth ? out.mu_q : nullptr,
                                         d.qk_norm ? out.rq : nullptr, d.fp8 ? 1 : 0);
     auto kq = d.q_smooth ? quant_k_kernel<BF16, D, true> : quant_k_kernel<BF16, D, false>;
     kq<<<dim3(d.Tn(), BH), blk, 0, s>>>(
-        (const u16*)K, d.N, out.k, out.kt, out.sk, out.mu_k, ws, d.k_smooth ? 1 : 0,
+        (const u16*)K, d.N, out.k, out.kt, out.sk, out.mu_k, d.k_smooth ? 1 : 0,
         d.q_smooth ? out.mu_q : nullptr, d.q_smooth ? out.qk_bias : nullptr, d.Tm(), d.scale,
         d.qk_norm ? out.rk : nullptr, d.fp8 ? 1 : 0);
     return hipGetLastError();

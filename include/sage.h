@@ -144,7 +144,8 @@ typedef struct sage_dotensors {
     uint16_t* dor;    /* R16H, N*D*2: dO re-laid as 16-bit row tiles */
 } sage_dotensors;
 
-/* Bytes of workspace sage_quantize needs (float64 column sums of K). */
+/* Bytes of workspace sage_quantize needs: the float64 column sums of K of
+ * every bkv-row block, B*H*(N/bkv)*D*8 bytes (used with k_smooth only). */
 size_t sage_quantize_workspace_bytes(const sage_shape* shape);
 
 /*
@@ -161,7 +162,10 @@ size_t sage_quantize_workspace_bytes(const sage_shape* shape);
  * Q, K, V: [B,H,N,D] 16-bit inputs.  out: every pointer must be set, except
  * mu_q and qk_bias, which must be NULL unless q_smooth (and set if it is).
  * workspace: sage_quantize_workspace_bytes() bytes, 8-byte aligned, any
- * content (it is cleared on the stream first).
+ * content (every byte read is written first by the same call); may be NULL
+ * when k_smooth is 0.  mu_K is summed in a fixed order (each 64-row block's
+ * column sums, then the blocks in order, in float64), so repeated calls give
+ * identical bits.
  */
 int sage_quantize(const sage_shape* shape, const void* Q, const void* K, const void* V,
                   const sage_qtensors* out, void* workspace, sage_stream_t stream);

@@ -212,16 +212,22 @@ def test_autograd_wrapper_matches_the_oracle(causal, qk_norm, fp8):
                      rel_max=chain, cos_min=0.9999)
 
 
-@pytest.mark.parametrize("fp8", [False, True])
-def test_repeat_is_deterministic(fp8):
-    """Two runs on the same inputs give identical codes, scales, O, L, dQ, dK
-    and dV (no atomics anywhere: dQ is a separate pass with a fixed order)."""
-    cfg = wl.C2_CAUSAL.replace(B=1, H=4, fp8=fp8)
+@pytest.mark.parametrize("fp8,qk_norm", [(False, False), (True, False), (False, True)])
+def test_repeat_is_deterministic(fp8, qk_norm):
+    """Two runs on the same inputs give identical codes, scales, means, O, L,
+    dQ, dK and dV (no atomics anywhere: mu_K adds block sums in a fixed order,
+    dQ is a separate pass with a fixed order).  With QK-norm fused, the K-mean
+    summands are float32 rows spanning many binades, where a float64 sum in a
+    varying order would round differently."""
+    if qk_norm:
+        cfg = wl.C3_QKNORM_FUSED.replace(B=1, H=4, N=4096)
+    else:
+        cfg = wl.C2_CAUSAL.replace(B=1, H=4, fp8=fp8)
     x = wl.generate(cfg)
-    gp.say(f"[gpu] determinism fp8={fp8}")
+    gp.say(f"[gpu] determinism fp8={fp8} qk_norm={qk_norm}")
     g1 = gp.run_gpu(cfg, x)
     g2 = gp.run_gpu(cfg, x)
-    for k in ("q", "k", "vt", "sq", "sk", "sv"):
+    for k in ("q", "k", "vt", "sq", "sk", "sv", "mu_k") + (("rq", "rk") if qk_norm else ()):
         np.testing.assert_array_equal(g1["qt"][k], g2["qt"][k])
     for k in ("O_bits", "L", "dQ", "dK", "dV"):
         np.testing.assert_array_equal(g1[k], g2[k])
