@@ -17,7 +17,8 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsage.so")
 
-SAGE_OK, SAGE_EINVAL, SAGE_EUNSUPPORTED, SAGE_EHIP = 0, -1, -2, -3
+SAGE_OK, SAGE_EINVAL, SAGE_EUNSUPPORTED, SAGE_EHIP, SAGE_ESCRATCH = 0, -1, -2, -3, -4
+NOALLOC_SCRATCH_BYTES = 8 << 20   # SAGE_NOALLOC_SCRATCH_BYTES of include/sage.h
 SAGE_FP16, SAGE_BF16 = 0, 1
 
 
@@ -52,6 +53,7 @@ class c_dotensors(ctypes.Structure):
 SIGNATURES = {
     "sage_quantize_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(c_shape)]),
     "sage_quantize": (ctypes.c_int, [ctypes.POINTER(c_shape), _P, _P, _P, ctypes.POINTER(c_qtensors), _P, _P]),
+    "sage_quantize_noalloc": (ctypes.c_int, [ctypes.POINTER(c_shape), _P, _P, _P, ctypes.POINTER(c_qtensors), _P]),
     "sage_fwd": (ctypes.c_int, [ctypes.POINTER(c_shape), ctypes.POINTER(c_qtensors), _P, _P, _P]),
     "sage_bwd_pre": (ctypes.c_int, [ctypes.POINTER(c_shape), _P, _P, ctypes.POINTER(c_dotensors), _P]),
     "sage_bwd_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(c_shape)]),
@@ -200,6 +202,15 @@ def quantize(sh: Shape, Q, K, V, out: Optional[Dict[str, torch.Tensor]] = None, 
     cs = sh.c()
     _check(lib.sage_quantize(ctypes.byref(cs), _ptr(Q), _ptr(K), _ptr(V), ctypes.byref(_qstruct(out)),
                              _ptr(out["ws"]), _stream(stream)), "sage_quantize")
+    return out
+
+
+def quantize_noalloc(sh: Shape, Q, K, V, out: Dict[str, torch.Tensor], stream=None):
+    """sage_quantize_noalloc: sage_quantize with the library's own fixed device
+    scratch in place of the workspace (out["ws"] is not used)."""
+    cs = sh.c()
+    _check(load().sage_quantize_noalloc(ctypes.byref(cs), _ptr(Q), _ptr(K), _ptr(V), ctypes.byref(_qstruct(out)),
+                                        _stream(stream)), "sage_quantize_noalloc")
     return out
 
 

@@ -3,6 +3,7 @@
 // buffer and no device state, and the error paths run without a GPU.
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/sage_probe.h"
 #include "sage_internal.h"
@@ -10,6 +11,38 @@
 namespace {
 
 thread_local int g_last_hip_error = 0;
+
+// Device memory of sage_quantize_noalloc: the K-mean partial sums live here
+// instead of in a caller's workspace.  One copy per GPU, resident until the
+// process ends.  Host code never passes the array's name to a kernel (on the
+// host it is only a stand-in for the symbol): the device address comes from
+// hipGetSymbolAddress, once per device, in noalloc_scratch() below.
+constexpr size_t kScratchBytes = SAGE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device (looked up on the
+// first call per device), or nullptr with the HIP error in *err.
+void* noalloc_scratch(hipError_t* err) {
+    int dev = 0;
+    *err = hipGetDevice(&dev);
+    if (*err != hipSuccess) return nullptr;
+    if (dev < 0 || dev >= kMaxDevices) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* ptr = nullptr;
+        *err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (*err != hipSuccess) return nullptr;
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -101,6 +134,22 @@ int sage_quantize(const sage_shape* shape, const void* Q, const void* K, const v
                                         reinterpret_cast<hipStream_t>(stream)));
 }
 
+int sage_quantize_noalloc(const sage_shape* shape, const void* Q, const void* K, const void* V,
+                          const sage_qtensors* out, sage_stream_t stream) {
+    sage::Dims d;
+    int st = check_shape(shape, d);
+    if (st != SAGE_OK) return st;
+    if (empty(d)) return SAGE_OK;
+    if (!ptrs_ok(Q, K, V)) return SAGE_EINVAL;
+    if ((st = check_qtensors(d, out)) != SAGE_OK) return st;
+    if (d.k_smooth && sage_quantize_workspace_bytes(shape) > kScratchBytes) return SAGE_ESCRATCH;
+    hipError_t e = hipSuccess;
+    void* ws = noalloc_scratch(&e);
+    if (ws == nullptr) return finish(e);
+    return finish(sage::launch_quantize(d, Q, K, V, *out, static_cast<double*>(ws),
+                                        reinterpret_cast<hipStream_t>(stream)));
+}
+
 int sage_fwd(const sage_shape* shape, const sage_qtensors* qk, void* O, float* L, sage_stream_t stream) {
     sage::Dims d;
     int st = check_shape(shape, d);
@@ -172,6 +221,9 @@ const char* sage_status_str(int status) {
         case SAGE_EINVAL: return "invalid argument (NULL or misaligned pointer, negative size, bad flag)";
         case SAGE_EUNSUPPORTED: return "unsupported shape (D, block sizes, dtype, or N not a multiple of the blocks)";
         case SAGE_EHIP: return "HIP launch failed (see sage_last_hip_error)";
+        case SAGE_ESCRATCH:
+            return "problem too large for the no-alloc entry point's fixed device scratch "
+                   "(use sage_quantize with a workspace)";
         default: return "unknown status";
     }
 }

@@ -60,7 +60,9 @@ enum {
     SAGE_OK = 0,
     SAGE_EINVAL = -1,       /* NULL pointer, negative size, misaligned pointer */
     SAGE_EUNSUPPORTED = -2, /* D, block sizes, dtype or N outside what is built */
-    SAGE_EHIP = -3          /* a HIP launch failed; see sage_last_hip_error() */
+    SAGE_EHIP = -3,         /* a HIP launch failed; see sage_last_hip_error() */
+    SAGE_ESCRATCH = -4      /* sage_quantize_noalloc: the problem needs more than
+                               SAGE_NOALLOC_SCRATCH_BYTES of scratch */
 };
 
 enum { SAGE_FP16 = 0, SAGE_BF16 = 1 };
@@ -169,6 +171,26 @@ size_t sage_quantize_workspace_bytes(const sage_shape* shape);
  */
 int sage_quantize(const sage_shape* shape, const void* Q, const void* K, const void* V,
                   const sage_qtensors* out, void* workspace, sage_stream_t stream);
+
+/* Largest workspace sage_quantize_noalloc can stand in for (8 MiB). */
+#define SAGE_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+
+/*
+ * sage_quantize_noalloc — for callers that cannot allocate device memory
+ * (code being captured into a HIP graph, tight serving loops, harnesses that
+ * forbid hipMalloc): sage_quantize with its workspace taken from a fixed
+ * array of SAGE_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held
+ * until the process ends.  Same arguments, layouts, results (bit for bit)
+ * and errors as sage_quantize, without `workspace`; the call allocates
+ * nothing.  Problems whose sage_quantize_workspace_bytes() exceed the array
+ * return SAGE_ESCRATCH before anything is launched (with k_smooth 0 there is
+ * no limit).  The first call on a device looks up the array's device address
+ * (a HIP failure there returns SAGE_EHIP).  Every call on one GPU shares that
+ * GPU's array: calls that may overlap on one GPU (several streams, several
+ * host threads) race on it and must be ordered by the caller.
+ */
+int sage_quantize_noalloc(const sage_shape* shape, const void* Q, const void* K, const void* V,
+                          const sage_qtensors* out, sage_stream_t stream);
 
 /*
  * sage_fwd — forward steps (3)-(5): for each query block, the INT8 logits
