@@ -343,7 +343,7 @@ def sweep(steps, warmup):
         L = torch.empty(Q.shape[:3], dtype=torch.float32, device="cuda")
         dQ, dK, dV = (torch.empty(Q.shape, dtype=torch.float32, device="cuda") for _ in range(3))
         calls = (lambda: bd.quantize(sh, Q, K, V, out=qt), lambda: bd.fwd(sh, qt, O, L),
-                 lambda: bd.bwd_pre(sh, O, dO, out=dot), lambda: bd.bwd(sh, qt, dot, L, dQ, dK, dV, ws=bws))
+                 lambda: bd.bwd_pre(sh, O, dO, out=dot), lambda: bd.bwd(sh, qt, dot, V, dO, L, dQ, dK, dV, ws=bws))
         for _ in range(warmup):
             for c in calls:
                 c()
@@ -454,7 +454,7 @@ def main():
         bd.bwd_pre(sh, O, dO, out=dot)
         if ev is not None:
             ev[3].record(stream)
-        bd.bwd(sh, qt, dot, L, dQ, dK, dV, ws=bws)
+        bd.bwd(sh, qt, dot, V, dO, L, dQ, dK, dV, ws=bws)
         if ev is not None:
             ev[4].record(stream)
 
@@ -561,6 +561,9 @@ def main():
     variants = () if args.no_variants else (("ablation_dp_int8", {"dp_int8": True}), ("variant_fp8", {"fp8": True}))
     for key, sw in variants:
         sha = dataclasses.replace(sh, **sw)
+        # the INT8-dP ablation also writes and reads row-tile copies of V's and
+        # dO's codes, so each variant gets buffers of its own
+        qt, dot = bd.alloc_qtensors(sha), bd.alloc_dotensors(sha)
         ab_ms = []
         for k in range(args.warmup + max(3, args.steps // 4)):
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
@@ -571,7 +574,7 @@ def main():
             ev[2].record(stream)
             bd.bwd_pre(sha, O, dO, out=dot)
             ev[3].record(stream)
-            bd.bwd(sha, qt, dot, L, dQ, dK, dV, ws=bws)
+            bd.bwd(sha, qt, dot, V, dO, L, dQ, dK, dV, ws=bws)
             ev[4].record(stream)
             torch.cuda.synchronize()
             if k >= args.warmup:

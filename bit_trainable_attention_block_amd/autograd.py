@@ -5,10 +5,10 @@ forward steps (1)-(5), backward steps (1)-(7)).
     O = sage_attention(Q, K, V, causal=True)     # Q, K, V: [B, H, N, D] bf16/fp16 on the GPU
     O.backward(dO)                               # Q.grad, K.grad, V.grad in the input dtype
 
-Forward: sage_quantize then sage_fwd; the INT8 codes, scales and means, O and
-the logsumexp L are kept for the backward (about 3 bytes per element plus
-the 16-bit copy of V: the backward recomputes S and P from the codes, it
-does not keep them).  Backward: sage_bwd_pre on the incoming dO, then
+Forward: sage_quantize then sage_fwd; the INT8 codes, scales and means, V,
+O and the logsumexp L are kept for the backward (3 bytes of codes per element
+beside the 16-bit V: the backward recomputes S and P from the codes, it does
+not keep them, and forms dP from V's 16-bit values).  Backward: sage_bwd_pre on the incoming dO, then
 sage_bwd.  The library computes every step; this module only allocates the
 buffers and passes pointers and the current stream; sage_cast_grads rounds
 the float32 gradients to the input dtype.  Without libsage.so the calls
@@ -42,22 +42,22 @@ class SageAttentionFunction(torch.autograd.Function):
         qt = bd.quantize(sh, Q, K, V)
         O, L = bd.fwd(sh, qt)
         ctx.sh = sh
-        ctx.qt = qt          # codes, scales and means (and the 16-bit copy of V)
+        ctx.qt = qt          # codes, scales and means
         if qk_norm:
-            ctx.save_for_backward(O, L, Q, K)   # the norm's gradient needs the input rows
+            ctx.save_for_backward(O, L, V, Q, K)   # the norm's gradient needs the input rows
         else:
-            ctx.save_for_backward(O, L)
+            ctx.save_for_backward(O, L, V)
         return O
 
     @staticmethod
     def backward(ctx, dO):
-        O, L = ctx.saved_tensors[:2]
+        O, L, V = ctx.saved_tensors[:3]
         sh = ctx.sh
         dO = dO.to(O.dtype).contiguous()
         dot = bd.bwd_pre(sh, O, dO)
-        dQ, dK, dV = bd.bwd(sh, ctx.qt, dot, L)
+        dQ, dK, dV = bd.bwd(sh, ctx.qt, dot, V, dO, L)
         if sh.qk_norm:
-            Q, K = ctx.saved_tensors[2:]
+            Q, K = ctx.saved_tensors[3:]
             bd.qk_norm_bwd(sh, Q, K, ctx.qt, dQ, dK)
         ctx.qt = None
         dQ, dK, dV = bd.cast_grads(sh, dQ, dK, dV)   # float32 -> the input dtype, in the library

@@ -37,7 +37,7 @@ class c_shape(ctypes.Structure):
 
 
 _P = ctypes.c_void_p
-QT_FIELDS = ("q", "qt", "sq", "k", "kt", "sk", "vt", "sv", "vr", "mu_k", "mu_q", "qk_bias", "rq", "rk")
+QT_FIELDS = ("q", "sq", "k", "sk", "vt", "sv", "vr", "mu_k", "mu_q", "qk_bias", "rq", "rk")
 DO_FIELDS = ("delta", "dot", "sdo", "dor")
 
 
@@ -58,7 +58,7 @@ SIGNATURES = {
     "sage_bwd_pre": (ctypes.c_int, [ctypes.POINTER(c_shape), _P, _P, ctypes.POINTER(c_dotensors), _P]),
     "sage_bwd_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(c_shape)]),
     "sage_bwd": (ctypes.c_int, [ctypes.POINTER(c_shape), ctypes.POINTER(c_qtensors), ctypes.POINTER(c_dotensors),
-                                _P, _P, _P, _P, _P, _P]),
+                                _P, _P, _P, _P, _P, _P, _P, _P]),
     "sage_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "sage_last_hip_error": (ctypes.c_int, []),
     "sage_version": (ctypes.c_char_p, []),
@@ -161,12 +161,12 @@ def alloc_qtensors(sh: Shape, device="cuda") -> Dict[str, torch.Tensor]:
     i8 = dict(dtype=torch.int8, device=device)
     f32 = dict(dtype=torch.float32, device=device)
     t = {
-        "q": torch.empty((B, H, N * D), **i8), "qt": torch.empty((B, H, N * D), **i8),
+        "q": torch.empty((B, H, N * D), **i8),
         "sq": torch.empty((B, H, sh.Tm), **f32),
-        "k": torch.empty((B, H, N * D), **i8), "kt": torch.empty((B, H, N * D), **i8),
+        "k": torch.empty((B, H, N * D), **i8),
         "sk": torch.empty((B, H, sh.Tn), **f32),
         "vt": torch.empty((B, H, N * D), **i8), "sv": torch.empty((B, H, sh.Tn), **f32),
-        "vr": torch.empty((B, H, N * D), dtype=torch.int16, device=device),
+        "vr": torch.empty((B, H, N * D), **i8) if sh.dp_int8 else None,
         "mu_k": torch.zeros((B, H, D), **f32),
         "mu_q": torch.empty((B, H, sh.Tm, D), **f32) if sh.q_smooth else None,
         "qk_bias": torch.empty((B, H, sh.Tm, N), **f32) if sh.q_smooth else None,
@@ -184,7 +184,7 @@ def alloc_dotensors(sh: Shape, device="cuda") -> Dict[str, torch.Tensor]:
         "delta": torch.empty((B, H, N), dtype=torch.float32, device=device),
         "dot": torch.empty((B, H, N * D), dtype=torch.int8, device=device),
         "sdo": torch.empty((B, H, sh.Tm), dtype=torch.float32, device=device),
-        "dor": torch.empty((B, H, N * D), dtype=torch.int16, device=device),
+        "dor": torch.empty((B, H, N * D), dtype=torch.int8, device=device) if sh.dp_int8 else None,
     }
 
 
@@ -239,7 +239,8 @@ def bwd_workspace(sh: Shape, device="cuda") -> torch.Tensor:
     return torch.empty((max(n, 16),), dtype=torch.uint8, device=device)
 
 
-def bwd(sh: Shape, qt, dot, L, dQ=None, dK=None, dV=None, ws=None, stream=None):
+def bwd(sh: Shape, qt, dot, V, dO, L, dQ=None, dK=None, dV=None, ws=None, stream=None):
+    """sage_bwd: V and dO are the 16-bit tensors given to quantize and bwd_pre."""
     lib = load()
     dev = L.device
     ws = bwd_workspace(sh, dev) if ws is None else ws
@@ -248,8 +249,8 @@ def bwd(sh: Shape, qt, dot, L, dQ=None, dK=None, dV=None, ws=None, stream=None):
     dK = torch.empty(shape, dtype=torch.float32, device=dev) if dK is None else dK
     dV = torch.empty(shape, dtype=torch.float32, device=dev) if dV is None else dV
     cs = sh.c()
-    _check(lib.sage_bwd(ctypes.byref(cs), ctypes.byref(_qstruct(qt)), ctypes.byref(_dostruct(dot)), _ptr(L),
-                        _ptr(ws), _ptr(dQ), _ptr(dK), _ptr(dV), _stream(stream)), "sage_bwd")
+    _check(lib.sage_bwd(ctypes.byref(cs), ctypes.byref(_qstruct(qt)), ctypes.byref(_dostruct(dot)), _ptr(V),
+                        _ptr(dO), _ptr(L), _ptr(ws), _ptr(dQ), _ptr(dK), _ptr(dV), _stream(stream)), "sage_bwd")
     return dQ, dK, dV
 
 
@@ -299,7 +300,7 @@ def run(sh: Shape, Q, K, V, dO, stream=None):
     qt = quantize(sh, Q, K, V, stream=stream)
     O, L = fwd(sh, qt, stream=stream)
     dot = bwd_pre(sh, O, dO, stream=stream)
-    dQ, dK, dV = bwd(sh, qt, dot, L, stream=stream)
+    dQ, dK, dV = bwd(sh, qt, dot, V, dO, L, stream=stream)
     out = {"qt": qt, "O": O, "L": L, "dot": dot, "dQ": dQ, "dK": dK, "dV": dV}
     if sh.qk_norm:
         # dQ, dK above are w.r.t. the normalised rows; these w.r.t. Q and K
@@ -316,7 +317,7 @@ def _rows_cols(N, D):
 
 
 def layout_offsets(kind: str, N: int, D: int):
-    """[N, D] array of byte (element for R16H) offsets of element (row, col)."""
+    """[N, D] array of byte offsets of element (row, col)."""
     import numpy as np
     r, c = _rows_cols(N, D)
     r = np.broadcast_to(r, (N, D)); c = np.broadcast_to(c, (N, D))
@@ -327,11 +328,6 @@ def layout_offsets(kind: str, N: int, D: int):
         g = (rr // 4) % 4
         e = (rr // 16) * 4 + rr % 4
         return (r // 64) * (64 * D) + (g * D + c) * 16 + e
-    if kind == "C64N":
-        rr = r % 64
-        return (r // 64) * (64 * D) + ((rr // 16) * D + c) * 16 + rr % 16
-    if kind == "R16H":
-        return (r // 16) * (16 * D) + (((c // 8) * 16 + r % 16) * 8) + c % 8
     raise ValueError(kind)
 
 

@@ -90,16 +90,18 @@ bool ptrs_ok(P... p) {
 
 int check_qtensors(const sage::Dims& d, const sage_qtensors* t) {
     if (t == nullptr) return SAGE_EINVAL;
-    if (!ptrs_ok(t->q, t->qt, t->sq, t->k, t->kt, t->sk, t->vt, t->sv, t->vr)) return SAGE_EINVAL;
+    if (!ptrs_ok(t->q, t->sq, t->k, t->sk, t->vt, t->sv)) return SAGE_EINVAL;
+    if (d.dp_int8 && !ptrs_ok(t->vr)) return SAGE_EINVAL;
     if (d.k_smooth && !ptrs_ok(t->mu_k)) return SAGE_EINVAL;
     if (d.q_smooth && !ptrs_ok(t->mu_q, t->qk_bias)) return SAGE_EINVAL;
     if (d.qk_norm && !ptrs_ok(t->rq, t->rk)) return SAGE_EINVAL;
     return SAGE_OK;
 }
 
-int check_dotensors(const sage_dotensors* t) {
+int check_dotensors(const sage::Dims& d, const sage_dotensors* t) {
     if (t == nullptr) return SAGE_EINVAL;
-    if (!ptrs_ok(t->delta, t->dot, t->sdo, t->dor)) return SAGE_EINVAL;
+    if (!ptrs_ok(t->delta, t->dot, t->sdo)) return SAGE_EINVAL;
+    if (d.dp_int8 && !ptrs_ok(t->dor)) return SAGE_EINVAL;
     return SAGE_OK;
 }
 
@@ -167,7 +169,7 @@ int sage_bwd_pre(const sage_shape* shape, const void* O, const void* dO, const s
     if (st != SAGE_OK) return st;
     if (empty(d)) return SAGE_OK;
     if (!ptrs_ok(O, dO)) return SAGE_EINVAL;
-    if ((st = check_dotensors(out)) != SAGE_OK) return st;
+    if ((st = check_dotensors(d, out)) != SAGE_OK) return st;
     return finish(sage::launch_bwd_pre(d, O, dO, *out, reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -177,16 +179,18 @@ size_t sage_bwd_workspace_bytes(const sage_shape* shape) {
     return sage::bwd_workspace_bytes(d);
 }
 
-int sage_bwd(const sage_shape* shape, const sage_qtensors* qk, const sage_dotensors* dos,
-             const float* L, void* workspace, float* dQ, float* dK, float* dV, sage_stream_t stream) {
+int sage_bwd(const sage_shape* shape, const sage_qtensors* qk, const sage_dotensors* dos, const void* V,
+             const void* dO, const float* L, void* workspace, float* dQ, float* dK, float* dV,
+             sage_stream_t stream) {
     sage::Dims d;
     int st = check_shape(shape, d);
     if (st != SAGE_OK) return st;
     if (empty(d)) return SAGE_OK;
     if ((st = check_qtensors(d, qk)) != SAGE_OK) return st;
-    if ((st = check_dotensors(dos)) != SAGE_OK) return st;
-    if (!ptrs_ok(L, workspace, dQ, dK, dV)) return SAGE_EINVAL;
-    return finish(sage::launch_bwd(d, *qk, *dos, L, workspace, dQ, dK, dV, reinterpret_cast<hipStream_t>(stream)));
+    if ((st = check_dotensors(d, dos)) != SAGE_OK) return st;
+    if (!ptrs_ok(V, dO, L, workspace, dQ, dK, dV)) return SAGE_EINVAL;
+    return finish(sage::launch_bwd(d, *qk, *dos, V, dO, L, workspace, dQ, dK, dV,
+                                   reinterpret_cast<hipStream_t>(stream)));
 }
 
 int sage_qk_norm_bwd(const sage_shape* shape, const void* Q, const void* K, const sage_qtensors* qk, float* dQ,

@@ -113,19 +113,36 @@ template <int BQ, int D, bool DPI8>
 struct BwdStage {
     int8_t q[BQ * D];     // Q codes, R32
     int8_t dot[BQ * D];   // dO codes, C64P
-    int8_t dor[(DPI8 ? 1 : 2) * BQ * D];   // dO, R16H; with dp_int8 dO's codes, R32
+    int8_t dor[(DPI8 ? 1 : 2) * BQ * D];   // dO, 16-bit row tiles (R16H order); with dp_int8 dO's codes, R32
     float l2[BQ];         // L * log2 e
     float ndelta[BQ];     // -delta (the dP accumulation starts from it)
 };
 
+// The 16-bit dO sits in the stage in 16-row tiles: element (row, col) of a
+// 16-row group at ((col / 8) * 16 + row % 16) * 8 + col % 8, so that the dP
+// product's A operand (a row's 8 consecutive d per lane) is one 16-byte read
+// per lane with the 16 rows of a lane group on distinct banks.  The stage is
+// filled from the row-major dO: the wave's copy of stage bytes [off, off +
+// 1 KiB) reads, for lane l, the 16 bytes of row 16 grp + l % 16 at chunk
+// column rem0 / 16 + l / 16 (grp, rem0: the 16-row group and the chunk
+// offset in it of the copy's first chunk); the lane part is voff_dor.
+template <int D>
+__device__ __forceinline__ int r16h_src_off(int off) {
+    constexpr int G16 = 2 * D;   // 16-byte chunks per 16-row group
+    const int c0 = off >> 4;     // the copy's first chunk (a multiple of 64)
+    return (c0 / G16) * 16 * 2 * D + ((c0 % G16) >> 4) * 16;
+}
+
 // Asynchronous copy of query tile qbase (Q codes, dO codes, dO) into the
 // stage at LDS address `lds`; the Q codes land swizzled (qswz), which the
-// copy does by reading lane l's chunk from qswz(16 l) (voff_q).  The three regions are contiguous BQ*D, BQ*D
-// and 2*BQ*D byte runs (BQ*D for the third with dp_int8), laid out in the
-// same order in the stage; each wave instruction moves 1 KiB, and round u of
-// the eight waves moves the stage's u-th 8 KiB.  When a region is a whole
-// number of rounds (BQ*D a multiple of 8 KiB) the region of a round is known
-// at compile time.  voff = 16 * lane.
+// copy does by reading lane l's chunk from qswz(16 l) (voff_q), and the
+// 16-bit dO lands in its row-tile order (r16h_src_off, voff_dor).  The three
+// regions are BQ*D, BQ*D and 2*BQ*D bytes (BQ*D for the third with dp_int8:
+// dO's R32 codes, copied as they are), laid out in the same order in the
+// stage; each wave instruction moves 1 KiB, and round u of the eight waves
+// moves the stage's u-th 8 KiB.  When a region is a whole number of rounds
+// (BQ*D a multiple of 8 KiB) the region of a round is known at compile time.
+// voff = 16 * lane.
 template <int BQ, int D, bool DPI8>
 struct StagePlan {
     static constexpr int QB = BQ * D, TOT = (DPI8 ? 3 : 4) * QB, R = 8 * 1024;
@@ -138,23 +155,28 @@ struct StagePlan {
 template <int BQ, int D, bool DPI8>
 __device__ __forceinline__ void plan_query_tile(StagePlan<BQ, D, DPI8>& pl, unsigned lds, const int8_t* q,
                                                 const int8_t* dot, const int8_t* dorb, int w, unsigned voff,
-                                                unsigned voff_q) {
+                                                unsigned voff_q, unsigned voff_dor) {
     using P = StagePlan<BQ, D, DPI8>;
-    constexpr int QB = P::QB, TOT = P::TOT, R = P::R, ROUNDS = P::ROUNDS;
+    constexpr int QB = P::QB, R = P::R, ROUNDS = P::ROUNDS;
     const int8_t** src = pl.src;
     unsigned* dst = pl.dst;
     unsigned* vo = pl.vo;
+    // source of the dO region's bytes [off, off + 1 KiB)
+    auto dor_src = [&](int off) __attribute__((always_inline)) {
+        return DPI8 ? dorb + off : dorb + r16h_src_off<D>(off);
+    };
+    const unsigned vo_dor = DPI8 ? voff : voff_dor;
 #pragma unroll
     for (int u = 0; u < ROUNDS; ++u) {
         const int c0 = u * R + w * 1024;
         if constexpr (QB % R == 0) {
             constexpr int RQ = QB / R;   // rounds per 1-byte region
             const int off = (u % RQ) * R + w * 1024;
-            src[u] = u < RQ ? q + off : u < 2 * RQ ? dot + off : dorb + (u - 2 * RQ) * R + w * 1024;
-            vo[u] = u < RQ ? voff_q : voff;
+            src[u] = u < RQ ? q + off : u < 2 * RQ ? dot + off : dor_src((u - 2 * RQ) * R + w * 1024);
+            vo[u] = u < RQ ? voff_q : u < 2 * RQ ? voff : vo_dor;
         } else {
-            src[u] = c0 < QB ? q + c0 : c0 < 2 * QB ? dot + (c0 - QB) : dorb + (c0 - 2 * QB);
-            vo[u] = c0 < QB ? voff_q : voff;
+            src[u] = c0 < QB ? q + c0 : c0 < 2 * QB ? dot + (c0 - QB) : dor_src(c0 - 2 * QB);
+            vo[u] = c0 < QB ? voff_q : c0 < 2 * QB ? voff : vo_dor;
         }
         dst[u] = lds + c0;
     }
@@ -182,10 +204,11 @@ __device__ __forceinline__ void issue_round(const StagePlan<BQ, D, DPI8>& pl, in
 // The whole stage at once.
 template <int BQ, int D, bool DPI8>
 __device__ __forceinline__ void stage_query_tile(unsigned lds, const int8_t* q, const int8_t* dot,
-                                                 const int8_t* dorb, int w, unsigned voff, unsigned voff_q) {
+                                                 const int8_t* dorb, int w, unsigned voff, unsigned voff_q,
+                                                 unsigned voff_dor) {
     using P = StagePlan<BQ, D, DPI8>;
     StagePlan<BQ, D, DPI8> pl;
-    plan_query_tile<BQ, D, DPI8>(pl, lds, q, dot, dorb, w, voff, voff_q);
+    plan_query_tile<BQ, D, DPI8>(pl, lds, q, dot, dorb, w, voff, voff_q, voff_dor);
     copy16_rounds<P::FULL>(pl.src, pl.dst, pl.vo);
     if constexpr (P::FULL < P::ROUNDS) issue_round<BQ, D, DPI8>(pl, P::FULL, w);
 }
@@ -196,10 +219,11 @@ __device__ __forceinline__ void stage_query_tile(unsigned lds, const int8_t* q, 
 template <bool BF16, int D, int BQ, bool CAUSAL, bool QSMOOTH, bool DPI8, bool F8>
 __global__ __launch_bounds__(512, 1) void bwd_kernel(
     const int8_t* __restrict__ q, const float* __restrict__ sq, const int8_t* __restrict__ k,
-    const float* __restrict__ sk, const u16* __restrict__ vr, const float* __restrict__ sv,
-    const float* __restrict__ mu_q,
+    const float* __restrict__ sk, const u16* __restrict__ V, const int8_t* __restrict__ vr8,
+    const float* __restrict__ sv, const float* __restrict__ mu_q,
     const float* __restrict__ qk_bias, const float* __restrict__ delta, const int8_t* __restrict__ dot,
-    const float* __restrict__ sdo, const u16* __restrict__ dor, const float* __restrict__ L,
+    const float* __restrict__ sdo, const u16* __restrict__ dO16, const int8_t* __restrict__ dor8,
+    const float* __restrict__ L,
     int8_t* __restrict__ dsw, float* __restrict__ sds, float* __restrict__ dK, float* __restrict__ dV, int N,
     int BH, double scale) {
     constexpr int MB = BQ / 16;   // 16-query blocks per tile
@@ -224,6 +248,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int lane = tid & 63, n16 = lane & 15, g = lane >> 4;
     const unsigned voff = 16u * lane, voff_q = (unsigned)qswz(16 * lane);
+    const unsigned voff_dor = (unsigned)((lane & 15) * 2 * D + (lane >> 4) * 16);
     // this lane's Q chunk offsets in a stage (swizzled): the S product reads
     // row 16 mb + n16, chunk column 4 ks + g, at qa_lane[mb & 1] + (mb / 2)
     // 32 D + 2048 ks; the dK product's transposed reads take query row
@@ -254,9 +279,8 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
             kop[ks] = *reinterpret_cast<const v4i*>(k + head + off_r32(key, 64 * ks + 16 * g, D));
 #pragma unroll
         for (int ks = 0; ks < KSV; ++ks)
-            vop[ks] = DPI8 ? *reinterpret_cast<const v4i*>(reinterpret_cast<const int8_t*>(vr) + head +
-                                                           off_r32(key, 64 * ks + 16 * g, D))
-                           : *reinterpret_cast<const v4i*>(vr + head + off_r16h(key, 32 * ks + 8 * g, D));
+            vop[ks] = DPI8 ? *reinterpret_cast<const v4i*>(vr8 + head + off_r32(key, 64 * ks + 16 * g, D))
+                           : *reinterpret_cast<const v4i*>(V + head + (size_t)key * D + 32 * ks + 8 * g);
         skj = sk[(size_t)bh * Tn + j];
         if (DPI8) svj = sv[(size_t)bh * Tn + j];
     }
@@ -278,7 +302,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
     const int8_t* qh = q + head;
     const int8_t* doth = dot + head;
     constexpr int DOR_B = DPI8 ? 1 : 2;   // bytes per element of the dP operand copy of dO
-    const int8_t* dorh = reinterpret_cast<const int8_t*>(dor) + DOR_B * head;
+    const int8_t* dorh = DPI8 ? dor8 + head : reinterpret_cast<const int8_t*>(dO16 + head);
     // Q-smoothing bias of this lane's key for the current query tile, loaded
     // one tile ahead (a key past a ragged end reads nothing)
     float nbias = 0.f;
@@ -326,7 +350,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
         Plan pl;
         const int qnext = more ? qbase + BQ : qbase;
         plan_query_tile<BQ, D, DPI8>(pl, lds_addr(&nxt), qh + (size_t)qnext * D, doth + (size_t)qnext * D,
-                                     dorh + (size_t)DOR_B * qnext * D, w, voff, voff_q);
+                                     dorh + (size_t)DOR_B * qnext * D, w, voff, voff_q, voff_dor);
         auto issue_rounds_of_block = [&](int mb) __attribute__((always_inline)) {
 #pragma unroll
             for (int u = mb * Plan::ROUNDS / MB; u < (mb + 1) * Plan::ROUNDS / MB; ++u) issue_round<BQ, D, DPI8>(pl, u, w);
@@ -408,10 +432,10 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
             mfma_block(0, opa[0]);
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
+                const v4f l2 = *reinterpret_cast<const v4f*>(&cur.l2[16 * mb + 4 * g]);
                 if (mb + 2 < MB) read_block(mb + 2, opa[mb & 1]);
                 if (mb + 1 < MB) mfma_block(mb + 1, opa[(mb + 1) & 1]);
                 issue_rounds_of_block(mb);
-                const v4f l2 = *reinterpret_cast<const v4f*>(&cur.l2[16 * mb + 4 * g]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     float x = fmaf(acc_value(s[mb][r]), c2, -l2[r]);
@@ -450,6 +474,23 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
             tile_scales(pmax, dsmax, sP, sS);
             // hardware reciprocal (within an ulp): a code moves only where
             // P / s_P lies within about 1e-5 of a rounding boundary
+            struct OpsB {
+                v4i av[KQ];
+                v4i ak[KQ];
+            };
+            OpsB opb[2];
+            auto read_db = [&](int db, OpsB& o) __attribute__((always_inline)) {
+#pragma unroll
+                for (int kq = 0; kq < KQ; ++kq) {
+                    o.av[kq] = reinterpret_cast<const v4i*>(cur.dot)[kq * 4 * D + g * D + 16 * db + n16];
+                    const v2i r1 = lds_read_tr8(cur.q + tr_lane + kq * 64 * D + db * 512);
+                    const v2i r2 = lds_read_tr8(cur.q + tr_lane + kq * 64 * D + 32 * D + db * 512);
+                    o.ak[kq] = v4i{r1[0], r1[1], r2[0], r2[1]};
+                }
+            };
+            read_db(0, opb[0]);
+            if (DB > 1) read_db(1, opb[1]);
+            __builtin_amdgcn_sched_barrier(0);
             const float invP = sP > 0.f ? __builtin_amdgcn_rcpf(sP) : 0.f;
             const float invS = sS > 0.f ? __builtin_amdgcn_rcpf(sS) : 0.f;
             // ---- codes, query-contiguous per lane (4 queries per dword)
@@ -503,15 +544,11 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
             const float fv = sP * sdoi;
             const float fk = sS * sqi;
             Acc accv[DB], acck[DB];
-            auto mfma_db = [&](int db) __attribute__((always_inline)) {
-                v4i av[KQ], ak[KQ];
+            auto mfma_db = [&](int db, const OpsB& o) __attribute__((always_inline)) {
+                const v4i* av = o.av;
+                const v4i* ak = o.ak;
 #pragma unroll
                 for (int kq = 0; kq < KQ; ++kq) {
-                    av[kq] = reinterpret_cast<const v4i*>(cur.dot)[kq * 4 * D + g * D + 16 * db + n16];
-                    // Q^ transposed: rows = d (lane), k = queries 64 kq + 16 (e/4) + 4 g + e%4
-                    const v2i r1 = lds_read_tr8(cur.q + tr_lane + kq * 64 * D + db * 512);
-                    const v2i r2 = lds_read_tr8(cur.q + tr_lane + kq * 64 * D + 32 * D + db * 512);
-                    ak[kq] = v4i{r1[0], r1[1], r2[0], r2[1]};
                     if constexpr (!F8) {
                         accv[db] = mfma16_i8(av[kq], pop[kq], kq == 0 ? magic4 : accv[db]);
                         acck[db] = mfma16_i8(ak[kq], dsop[kq], kq == 0 ? magic4 : acck[db]);
@@ -529,15 +566,19 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
                 }
             };
             // one d-block of products ahead of the accumulation of the previous
-            mfma_db(0);
+            mfma_db(0, opb[0]);
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                if (db + 1 < DB) mfma_db(db + 1);
+                if (db + 2 < DB) read_db(db + 2, opb[db & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+                if (db + 1 < DB) mfma_db(db + 1, opb[(db + 1) & 1]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     dvt[db][r] = fmaf(acc_value(accv[db][r]), fv, dvt[db][r]);
                     dkt[db][r] = fmaf(acc_value(acck[db][r]), fk, dkt[db][r]);
                 }
+                settle(dvt[db]);
+                settle(dkt[db]);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -553,7 +594,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
 
     // ---- prologue: first query tile into st0
     stage_query_tile<BQ, D, DPI8>(lds_addr(&st[0]), qh + (size_t)istart * BQ * D, doth + (size_t)istart * BQ * D,
-                                  dorh + (size_t)DOR_B * istart * BQ * D, w, voff, voff_q);
+                                  dorh + (size_t)DOR_B * istart * BQ * D, w, voff, voff_q, voff_dor);
     if (tid < BQ) {
         st[0].l2[tid] = (float)((double)Lh[istart * BQ + tid] * kLog2e_d);
         st[0].ndelta[tid] = -dlh[istart * BQ + tid];
@@ -599,17 +640,19 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
 // dQ_i = scale * sum_j s_dS,ij s_K,j M(dS^_ij, K^_j), one workgroup per query
 // tile; wave w owns the BQ/4 dS positions [w BQ/4, (w+1) BQ/4) (queries
 // 16 mb + 4 w + r) and all D columns.  Each key tile (its dS codes and the
-// K codes, column tiles) streams through two alternating LDS stages filled
-// one tile ahead by asynchronous copies.
+// K codes) streams through two alternating LDS stages filled one tile ahead
+// by asynchronous copies.  K's codes arrive as R32 row tiles (swizzled as the
+// backward's Q codes are) and are read transposed: column d of a product's B
+// operand is two transpose reads of eight keys.
 template <int BQ, int D>
 struct DqStage {
     int8_t ds[BQ * 64];   // dS codes of one tile, key-major (workspace layout)
-    int8_t k[64 * D];     // K codes of the key block, C64N
+    int8_t k[64 * D];     // K codes of the key block, R32, qswz-swizzled
 };
 
 template <int D, int BQ, bool CAUSAL, bool F8>
 __global__ __launch_bounds__(256, 2) void dq_kernel(const int8_t* __restrict__ dsw, const float* __restrict__ sds,
-                                                   const int8_t* __restrict__ kt, const float* __restrict__ sk,
+                                                   const int8_t* __restrict__ k, const float* __restrict__ sk,
                                                    float* __restrict__ dQ, int N, int BH, double scale) {
     constexpr int QPW = BQ / 4;           // positions per wave
     constexpr int MBq = QPW / 16;
@@ -634,23 +677,29 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const int8_t* __restrict__ d
     const int lane = tid & 63, n16 = lane & 15, g = lane >> 4;
     const int jend = CAUSAL ? (i + 1) * BQ / 64 : Tn;
 
-    const unsigned voff = 16u * lane;
+    const unsigned voff = 16u * lane, voff_q = (unsigned)qswz(16 * lane);
+    // this lane's K transpose-read offsets (keys 16 g + 8 h + n16 / 2, bytes
+    // 8 (n16 % 2).. of chunk column 0); chunk column nb adds 512 nb, which
+    // the swizzle (bits 7 and 8) does not see
+    int tk[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) tk[h] = qswz(off_r32(16 * g + 8 * h + (n16 >> 1), 0, D)) + 8 * (n16 & 1);
     // the stage's ds and k regions are contiguous: round u fills its bytes
     // [4096 u, 4096 u + 4096)
     auto load = [&](int j, DqStage<BQ, D>& st) __attribute__((always_inline)) {
         const size_t t = (size_t)bh * tph + tile_index<BQ, CAUSAL>(i, j, Tn);
         const int8_t* s1 = dsw + t * DS_BYTES;
-        const int8_t* s2 = kt + head + (size_t)j * K_BYTES;
+        const int8_t* s2 = k + head + (size_t)j * K_BYTES;
         const unsigned base = lds_addr(&st);
         const int8_t* src[ROUNDS];
         unsigned dst[ROUNDS], vo[ROUNDS];
 #pragma unroll
         for (int u = 0; u < ROUNDS; ++u) {
             const int c0 = u * 4096 + w * 1024;
-            if constexpr (DS_BYTES % 4096 == 0) src[u] = u * 4096 < DS_BYTES ? s1 + c0 : s2 + (c0 - DS_BYTES);
-            else src[u] = c0 < DS_BYTES ? s1 + c0 : s2 + (c0 - DS_BYTES);
+            const bool is_ds = DS_BYTES % 4096 == 0 ? u * 4096 < DS_BYTES : c0 < DS_BYTES;
+            src[u] = is_ds ? s1 + c0 : s2 + (c0 - DS_BYTES);
             dst[u] = base + c0;
-            vo[u] = voff;
+            vo[u] = is_ds ? voff : voff_q;
         }
         copy16_rounds<ROUNDS>(src, dst, vo);
     };
@@ -666,7 +715,6 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const int8_t* __restrict__ d
         const size_t t = (size_t)bh * tph + tile_index<BQ, CAUSAL>(i, j, Tn);
         const float cj = (float)((double)sds[t] * (double)sk[(size_t)bh * Tn + j] * scale);
         if (j + 1 < jend) load(j + 1, nxt);
-        const v4i* lk = reinterpret_cast<const v4i*>(cur.k);
         // A = dS^ rows (positions), k = keys 16 g + e, read transposed from the
         // key-major rows: two transpose reads of eight keys each
         v4i av[MBq];
@@ -684,7 +732,10 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const int8_t* __restrict__ d
         }
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            const v4i bv = lk[g * D + 16 * nb + n16];   // K^ C64N: column d, k = key 16 g + e
+            // K^ column d = 16 nb + n16, k = key 16 g + e
+            const v2i b0 = lds_read_tr8(cur.k + tk[0] + 512 * nb);
+            const v2i b1 = lds_read_tr8(cur.k + tk[1] + 512 * nb);
+            const v4i bv = v4i{b0[0], b0[1], b1[0], b1[1]};
 #pragma unroll
             for (int mb = 0; mb < MBq; ++mb) {
                 if constexpr (F8) {
@@ -722,6 +773,8 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const int8_t* __restrict__ d
 struct BwdPtrs {
     const sage_qtensors* qk;
     const sage_dotensors* dos;
+    const u16* V;    // 16-bit V, row-major
+    const u16* dO;   // 16-bit dO, row-major
     const float* L;
     int8_t* dsw;
     float* sds;
@@ -739,10 +792,10 @@ hipError_t bwd_dispatch(const Dims& d, const BwdPtrs& p, hipStream_t s) {
                                           : bwd_kernel<BF16, D, BQ, CAUSAL, false, true, false>)
                             : (d.q_smooth ? bwd_kernel<BF16, D, BQ, CAUSAL, true, false, false>
                                           : bwd_kernel<BF16, D, BQ, CAUSAL, false, false, false>);
-    kern<<<grid, 512, 0, s>>>(qk.q, qk.sq, qk.k, qk.sk, qk.vr, qk.sv, qk.mu_q, qk.qk_bias, dos.delta, dos.dot,
-                              dos.sdo, dos.dor, p.L, p.dsw, p.sds, p.dK, p.dV, d.N, d.BH(), d.scale);
+    kern<<<grid, 512, 0, s>>>(qk.q, qk.sq, qk.k, qk.sk, p.V, qk.vr, qk.sv, qk.mu_q, qk.qk_bias, dos.delta,
+                              dos.dot, dos.sdo, p.dO, dos.dor, p.L, p.dsw, p.sds, p.dK, p.dV, d.N, d.BH(), d.scale);
     auto dq = d.fp8 ? dq_kernel<D, BQ, CAUSAL, true> : dq_kernel<D, BQ, CAUSAL, false>;
-    dq<<<dim3(d.Tm() * d.BH()), 256, 0, s>>>(p.dsw, p.sds, qk.kt, qk.sk, p.dQ, d.N, d.BH(), d.scale);
+    dq<<<dim3(d.Tm() * d.BH()), 256, 0, s>>>(p.dsw, p.sds, qk.k, qk.sk, p.dQ, d.N, d.BH(), d.scale);
     return hipGetLastError();
 }
 
@@ -765,11 +818,12 @@ size_t codes_bytes(const Dims& d) { return (total_tiles(d) * (size_t)d.bq * 64 +
 
 size_t bwd_workspace_bytes(const Dims& d) { return codes_bytes(d) + total_tiles(d) * sizeof(float); }
 
-hipError_t launch_bwd(const Dims& d, const sage_qtensors& qk, const sage_dotensors& dos, const float* L,
-                      void* workspace, float* dQ, float* dK, float* dV, hipStream_t s) {
+hipError_t launch_bwd(const Dims& d, const sage_qtensors& qk, const sage_dotensors& dos, const void* V,
+                      const void* dO, const float* L, void* workspace, float* dQ, float* dK, float* dV,
+                      hipStream_t s) {
     int8_t* dsw = static_cast<int8_t*>(workspace);
     float* sds = reinterpret_cast<float*>(dsw + codes_bytes(d));
-    const BwdPtrs p{&qk, &dos, L, dsw, sds, dQ, dK, dV};
+    const BwdPtrs p{&qk, &dos, static_cast<const u16*>(V), static_cast<const u16*>(dO), L, dsw, sds, dQ, dK, dV};
     if (d.bf16) return d.D == 128 ? bwd_dispatch_bq<true, 128>(d, p, s) : bwd_dispatch_bq<true, 64>(d, p, s);
     return d.D == 128 ? bwd_dispatch_bq<false, 128>(d, p, s) : bwd_dispatch_bq<false, 64>(d, p, s);
 }

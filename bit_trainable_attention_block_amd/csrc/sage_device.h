@@ -62,12 +62,7 @@ __device__ __forceinline__ int off_c64p(int row, int col, int D) {
     int e = ((r >> 4) << 2) | (r & 3);
     return (row >> 6) * (64 * D) + ((g * D + col) << 4) + e;
 }
-// C64N: 64-row group, (g, e) -> in-group row 16*g + e.
-__device__ __forceinline__ int off_c64n(int row, int col, int D) {
-    int r = row & 63;
-    return (row >> 6) * (64 * D) + ((((r >> 4) * D) + col) << 4) + (r & 15);
-}
-// R16H: element offset of 16-bit element (row, col).
+// 16-bit row tiles (the backward's dO stage): element offset of (row, col).
 __device__ __forceinline__ int off_r16h(int row, int col, int D) {
     return (row >> 4) * (16 * D) + ((((col >> 3) << 4) + (row & 15)) << 3) + (col & 7);
 }

@@ -31,8 +31,9 @@ hipError_t launch_bwd_pre(const Dims& d, const void* O, const void* dO, const sa
                           hipStream_t s);
 hipError_t launch_fwd(const Dims& d, const sage_qtensors& qk, void* O, float* L, hipStream_t s);
 size_t bwd_workspace_bytes(const Dims& d);
-hipError_t launch_bwd(const Dims& d, const sage_qtensors& qk, const sage_dotensors& dos,
-                      const float* L, void* workspace, float* dQ, float* dK, float* dV, hipStream_t s);
+hipError_t launch_bwd(const Dims& d, const sage_qtensors& qk, const sage_dotensors& dos, const void* V,
+                      const void* dO, const float* L, void* workspace, float* dQ, float* dK, float* dV,
+                      hipStream_t s);
 hipError_t launch_qk_norm_bwd(const Dims& d, const void* Q, const void* K, const float* rq, const float* rk,
                               float* dQ, float* dK, hipStream_t s);
 hipError_t launch_cast_grads(const Dims& d, const float* const src[3], void* const dst[3], hipStream_t s);

@@ -154,14 +154,10 @@ __device__ __forceinline__ void codes_to_lds(const float (&x)[Blk<R, D>::PER_T][
     }
 }
 
-enum Layout { R32, C64P, C64N };
+enum Layout { R32, C64P };
 
-// In-block row of byte e of output chunk (h|g) for the column layouts.
-template <Layout L>
-__device__ __forceinline__ int col_layout_row(int grp_part, int e) {
-    if constexpr (L == C64P) return 16 * (e >> 2) + 4 * grp_part + (e & 3);
-    return 16 * grp_part + e;  // C64N
-}
+// In-block row of byte e of output chunk g for the C64P column layout.
+__device__ __forceinline__ int c64p_row(int grp_part, int e) { return 16 * (e >> 2) + 4 * grp_part + (e & 3); }
 
 // Write the R x D codes held in LDS to dst (the block's region of the head,
 // laid out as L) with coalesced 16-byte stores.
@@ -185,7 +181,7 @@ __device__ __forceinline__ void store_codes(const uint8_t* codes, int8_t* __rest
                 uint32_t acc = 0;
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
-                    const int row = grp * GR + col_layout_row<L>(part, 4 * q + b);
+                    const int row = grp * GR + c64p_row(part, 4 * q + b);
                     acc |= (uint32_t)codes[row * CStride<D> + col] << (8 * b);
                 }
                 w[q] = acc;
@@ -196,24 +192,10 @@ __device__ __forceinline__ void store_codes(const uint8_t* codes, int8_t* __rest
     }
 }
 
-// Copy the raw 16-bit block into the R16H row-tile layout.
-template <int R, int D>
-__device__ __forceinline__ void store_r16h(const v4i (&raw)[Blk<R, D>::PER_T], u16* __restrict__ head,
-                                           int row0) {
-    using B = Blk<R, D>;
-    const int t = threadIdx.x;
-    const int cc = t % B::CPR;
-#pragma unroll
-    for (int k = 0; k < B::PER_T; ++k) {
-        int row = row0 + t / B::CPR + k * B::RSTEP;
-        *reinterpret_cast<v4i*>(head + off_r16h(row, cc * 8, D)) = raw[k];
-    }
-}
-
 // ------------------------------------------------------------------ kernels
 
-// V blocks (64 rows): codes -> vt (C64P), scale -> sv, raw copy -> vr (R16H);
-// with dp_int8 the codes again, as R32 row tiles, -> vr instead of the copy.
+// V blocks (64 rows): codes -> vt (C64P), scale -> sv; with dp_int8 the
+// codes again, as R32 row tiles, -> vr (the INT8-dP ablation's operand).
 // K blocks (same rows): the block's float64 column sums -> kpart[bh][j][D]
 // (a fixed summation order inside the block; kmean_kernel adds the blocks in
 // order, so mu_K does not depend on scheduling even where the float64 sums
@@ -221,7 +203,7 @@ __device__ __forceinline__ void store_r16h(const v4i (&raw)[Blk<R, D>::PER_T], u
 template <bool BF16, int D>
 __global__ __launch_bounds__(kThreads) void quant_v_ksum_kernel(
     const u16* __restrict__ K, const u16* __restrict__ V, int N, int8_t* __restrict__ vt,
-    float* __restrict__ sv, u16* __restrict__ vr, double* __restrict__ kpart, int k_smooth, int dp_int8,
+    float* __restrict__ sv, int8_t* __restrict__ vr, double* __restrict__ kpart, int k_smooth, int dp_int8,
     int qk_norm, int fp8) {
     constexpr int R = 64;
     using B = Blk<R, D>;
@@ -243,14 +225,13 @@ __global__ __launch_bounds__(kThreads) void quant_v_ksum_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[k][e]));
     }
-    if (!dp_int8) store_r16h<R, D>(raw, vr + head, row0);
     const float a = block_max(m, red);
     const float s = __fdiv_rn(a, qmax_of(fp8));
     codes_to_lds<R, D>(x, s, codes, fp8);
     if (threadIdx.x == 0) sv[(size_t)bh * (N / R) + j] = s;
     __syncthreads();
     store_codes<C64P, R, D>(codes, vt + head + (size_t)row0 * D);
-    if (dp_int8) store_codes<R32, R, D>(codes, reinterpret_cast<int8_t*>(vr) + head + (size_t)row0 * D);
+    if (dp_int8) store_codes<R32, R, D>(codes, vr + head + (size_t)row0 * D);
 
     if (k_smooth) {
         load_block<R, D>(K + head + (size_t)row0 * D, raw);
@@ -268,25 +249,36 @@ __global__ __launch_bounds__(kThreads) void quant_v_ksum_kernel(
     }
 }
 
-// mu_K[bh][c] = f32(sum_j kpart[bh][j][c] / N), the Tn block sums added in
-// block order in float64 (one thread per channel; reads are coalesced across
-// the channels of a block).
+// mu_K[bh][c] = f32(sum_j kpart[bh][j][c] / N) in float64, in a fixed order:
+// the Tn block sums of a head are split into G consecutive runs, thread
+// (run, channel) adds its run in block order, and the G run sums are added in
+// run order.  Reads are coalesced across the channels of a block.
 template <int D>
-__global__ __launch_bounds__(D) void kmean_kernel(const double* __restrict__ kpart, int Tn, int N,
-                                                  float* __restrict__ mu_k) {
-    const int bh = blockIdx.x, c = threadIdx.x;
+__global__ __launch_bounds__(512) void kmean_kernel(const double* __restrict__ kpart, int Tn, int N,
+                                                    float* __restrict__ mu_k) {
+    constexpr int G = 512 / D;
+    __shared__ double part[G][D];
+    const int bh = blockIdx.x, c = threadIdx.x % D, run = threadIdx.x / D;
     const double* p = kpart + (size_t)bh * Tn * D + c;
+    const int j0 = run * Tn / G, j1 = (run + 1) * Tn / G;
     double acc = 0.0;
-    for (int j = 0; j < Tn; ++j) acc += p[(size_t)j * D];
-    mu_k[(size_t)bh * D + c] = (float)(acc / (double)N);
+#pragma unroll 8
+    for (int j = j0; j < j1; ++j) acc += p[(size_t)j * D];
+    part[run][c] = acc;
+    __syncthreads();
+    if (run == 0) {
+        double sum = part[0][c];
+#pragma unroll
+        for (int r = 1; r < G; ++r) sum += part[r][c];
+        mu_k[(size_t)bh * D + c] = (float)(sum / (double)N);
+    }
 }
 
-// Q blocks (BQ rows): optional Q-smoothing (QS, mu_q set), codes -> q (R32)
-// and qt (C64P).  Only with QS does the block hold the column-sum scratch.
+// Q blocks (BQ rows): optional Q-smoothing (QS, mu_q set), codes -> q (R32).
+// Only with QS does the block hold the column-sum scratch.
 template <bool BF16, int D, int BQ, bool QS>
 __global__ __launch_bounds__(kThreads) void quant_q_kernel(const u16* __restrict__ Q, int N,
                                                            int8_t* __restrict__ q,
-                                                           int8_t* __restrict__ qt,
                                                            float* __restrict__ sq,
                                                            float* __restrict__ mu_q,
                                                            float* __restrict__ rq, int fp8) {
@@ -338,17 +330,16 @@ __global__ __launch_bounds__(kThreads) void quant_q_kernel(const u16* __restrict
     if (threadIdx.x == 0) sq[(size_t)bh * Tm + i] = s;
     __syncthreads();
     store_codes<R32, BQ, D>(codes, q + head + (size_t)row0 * D);
-    store_codes<C64P, BQ, D>(codes, qt + head + (size_t)row0 * D);
 }
 
-// K blocks (64 rows): mu_K = f32(sum / N); K_sm = f32(K - mu_K); codes -> k
-// (R32) and kt (C64N).  With Q-smoothing, also the logit bias of these keys
+// K blocks (64 rows): K_sm = f32(K - mu_K) (mu_K from kmean_kernel); codes
+// -> k (R32).  With Q-smoothing, also the logit bias of these keys
 // for every query block: bias[i][n] = scale * sum_c mu_Q[i][c] * K_sm[n][c]
 // (float64 accumulation, rounded once).  QS: Q-smoothing on (qk_bias set);
 // only then does the block hold its smoothed rows in LDS.
 template <bool BF16, int D, bool QS>
 __global__ __launch_bounds__(kThreads) void quant_k_kernel(
-    const u16* __restrict__ K, int N, int8_t* __restrict__ k, int8_t* __restrict__ kt,
+    const u16* __restrict__ K, int N, int8_t* __restrict__ k,
     float* __restrict__ sk, const float* __restrict__ mu_k, int k_smooth,
     const float* __restrict__ mu_q, float* __restrict__ qk_bias, int Tm, double scale, float* __restrict__ rk,
     int fp8) {
@@ -396,7 +387,6 @@ __global__ __launch_bounds__(kThreads) void quant_k_kernel(
     }
     __syncthreads();
     store_codes<R32, R, D>(codes, k + head + (size_t)row0 * D);
-    store_codes<C64N, R, D>(codes, kt + head + (size_t)row0 * D);
 
     if constexpr (QS) {
         // thread -> (key n = t % 64, query blocks i = t / 64 + 4 r + 32 pass,
@@ -427,15 +417,15 @@ __global__ __launch_bounds__(kThreads) void quant_k_kernel(
 }
 
 // Backward pre-pass on one BQ-row block: delta = rowsum(dO o O) (float64,
-// rounded once), dO codes -> dot (C64P), scale -> sdo, raw dO -> dor (R16H);
-// with dp_int8 the codes again, as R32 row tiles, -> dor instead of the copy.
+// rounded once), dO codes -> dot (C64P), scale -> sdo; with dp_int8 the codes
+// again, as R32 row tiles, -> dor (the INT8-dP ablation's operand).
 template <bool BF16, int D, int BQ>
 __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const u16* __restrict__ O,
                                                            const u16* __restrict__ dO, int N,
                                                            float* __restrict__ delta,
                                                            int8_t* __restrict__ dot,
                                                            float* __restrict__ sdo,
-                                                           u16* __restrict__ dor, int dp_int8, int fp8) {
+                                                           int8_t* __restrict__ dor, int dp_int8, int fp8) {
     using B = Blk<BQ, D>;
     __shared__ float red[4];
     __shared__ __align__(16) uint8_t codes[BQ * CStride<D>];
@@ -449,7 +439,6 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const u16* __restrict
     float x[B::PER_T][8];
     load_block<BQ, D>(dO + head + (size_t)row0 * D, raw);
     load_block<BQ, D>(O + head + (size_t)row0 * D, rawo);
-    if (!dp_int8) store_r16h<BQ, D>(raw, dor + head, row0);
     float m = 0.f;
 #pragma unroll
     for (int k = 0; k < B::PER_T; ++k) {
@@ -472,7 +461,7 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const u16* __restrict
     if (threadIdx.x == 0) sdo[(size_t)bh * Tm + i] = s;
     __syncthreads();
     store_codes<C64P, BQ, D>(codes, dot + head + (size_t)row0 * D);
-    if (dp_int8) store_codes<R32, BQ, D>(codes, reinterpret_cast<int8_t*>(dor) + head + (size_t)row0 * D);
+    if (dp_int8) store_codes<R32, BQ, D>(codes, dor + head + (size_t)row0 * D);
 }
 
 // Gradient through QK-norm, in place on one 64-row block of one head:
@@ -522,14 +511,14 @@ hipError_t quantize_impl(const Dims& d, const void* Q, const void* K, const void
     quant_v_ksum_kernel<BF16, D><<<dim3(d.Tn(), BH), blk, 0, s>>>(
         (const u16*)K, (const u16*)V, d.N, out.vt, out.sv, out.vr, ws, d.k_smooth ? 1 : 0, d.dp_int8 ? 1 : 0,
         d.qk_norm ? 1 : 0, d.fp8 ? 1 : 0);
-    if (d.k_smooth) kmean_kernel<D><<<dim3(BH), dim3(D), 0, s>>>(ws, d.Tn(), d.N, out.mu_k);
+    if (d.k_smooth) kmean_kernel<D><<<dim3(BH), dim3(512), 0, s>>>(ws, d.Tn(), d.N, out.mu_k);
     auto qq = d.bq == 128 ? (d.q_smooth ? quant_q_kernel<BF16, D, 128, true> : quant_q_kernel<BF16, D, 128, false>)
                           : (d.q_smooth ? quant_q_kernel<BF16, D, 64, true> : quant_q_kernel<BF16, D, 64, false>);
-    qq<<<dim3(d.Tm(), BH), blk, 0, s>>>((const u16*)Q, d.N, out.q, out.qt, out.sq, d.q_smooth ? out.mu_q : nullptr,
+    qq<<<dim3(d.Tm(), BH), blk, 0, s>>>((const u16*)Q, d.N, out.q, out.sq, d.q_smooth ? out.mu_q : nullptr,
                                         d.qk_norm ? out.rq : nullptr, d.fp8 ? 1 : 0);
     auto kq = d.q_smooth ? quant_k_kernel<BF16, D, true> : quant_k_kernel<BF16, D, false>;
     kq<<<dim3(d.Tn(), BH), blk, 0, s>>>(
-        (const u16*)K, d.N, out.k, out.kt, out.sk, out.mu_k, d.k_smooth ? 1 : 0,
+        (const u16*)K, d.N, out.k, out.sk, out.mu_k, d.k_smooth ? 1 : 0,
         d.q_smooth ? out.mu_q : nullptr, d.q_smooth ? out.qk_bias : nullptr, d.Tm(), d.scale,
         d.qk_norm ? out.rk : nullptr, d.fp8 ? 1 : 0);
     return hipGetLastError();

@@ -31,17 +31,14 @@
  *   - No exception, abort or exit crosses this interface.
  *
  * Quantised-tensor layouts (element (row, col) of a [N, D] head; a "group"
- * is 16, 32 or 64 consecutive rows; each layout is [B, H, N/group, ...]):
+ * is 32 or 64 consecutive rows; each layout is [B, H, N/group, ...]):
  *   R32   row tiles:  byte (row, col) at group row/32, offset
  *         ((col/16) * 32 + row%32) * 16 + col%16.
  *   C64P  column tiles, 64-row groups, permuted: offset (g * D + col) * 16 + e,
  *         with in-group row r = 16*(e/4) + 4*g + e%4  (g in [0,4)).
- *   C64N  column tiles, 64-row groups, natural order: offset
- *         (g * D + col) * 16 + e with r = 16*g + e.
- *   R16H  16-bit row tiles: element (row, col) at group row/16, element
- *         offset ((col/8) * 16 + row%16) * 8 + col%8.
- * These orders are the operand orders of the gfx950 INT8 / 16-bit matrix
- * instructions the kernels use, so tiles move into LDS as plain copies.
+ * These orders are the operand orders of the gfx950 INT8 matrix instruction
+ * the kernels use, so tiles move into LDS as plain copies; the other operand
+ * orders are read out of the same tiles with the LDS transpose read.
  */
 #ifndef SAGE_H
 #define SAGE_H
@@ -81,11 +78,10 @@ typedef struct sage_shape {
                            1 = ablation (SageAttention3 write-up, Table 1c
                            compares it with FP16): dP from the per-block INT8
                            codes of dO and V, dP = f32(dO^ V^^T) * f32(s_dO * s_V).
-                           Then sage_quantize stores V's codes (R32, N*D bytes
-                           per head, heads consecutive) at the start of `vr`,
-                           sage_bwd_pre stores dO's codes (R32, likewise) at
-                           the start of `dor`, and sage_bwd reads them; the
-                           three calls must agree on it. */
+                           Then sage_quantize also stores V's codes as row
+                           tiles in `vr`, sage_bwd_pre dO's in `dor`, and
+                           sage_bwd reads them; the three calls must agree
+                           on it. */
     int32_t p_static;   /* 0 = the method: the forward's P codes per token,
                            s_P = exp(rowmax(S_ij) - m_ij) / 127 (Eq. 8).
                            1 = ablation (the SageAttention3 write-up names it
@@ -103,7 +99,7 @@ typedef struct sage_shape {
     int32_t fp8;        /* 0 = the method: INT8 codes, s = max|X| / 127.
                            1 = E4M3 variant (the SageAttention3 write-up's
                            INT8-versus-FP8 training comparison): every code
-                           tensor (q, qt, k, kt, vt, dot and the dS workspace)
+                           tensor (q, k, vt, dot and the dS workspace)
                            holds E4M3 bytes (OCP: sign, 4 exponent bits with
                            bias 7, 3 mantissa bits, largest finite 448), the
                            scales use 448 in place of 127 (block s =
@@ -121,14 +117,13 @@ typedef struct sage_shape {
  * for one head, T_m = N/bq, T_n = N/bkv. */
 typedef struct sage_qtensors {
     int8_t* q;        /* R32,  N*D:   codes of Q (of Q - mu_Q with q_smooth) */
-    int8_t* qt;       /* C64P, N*D:   the same codes, column tiles */
     float* sq;        /* T_m floats:  Q block scales */
     int8_t* k;        /* R32,  N*D:   codes of K - mu_K (K if !k_smooth) */
-    int8_t* kt;       /* C64N, N*D:   the same codes, column tiles */
     float* sk;        /* T_n floats:  K block scales */
     int8_t* vt;       /* C64P, N*D:   codes of V, column tiles */
     float* sv;        /* T_n floats:  V block scales */
-    uint16_t* vr;     /* R16H, N*D*2: V re-laid as 16-bit row tiles */
+    int8_t* vr;       /* R32,  N*D:   dp_int8 only: V's codes again, as row
+                         tiles (the ablation's dP operand); else NULL */
     float* mu_k;      /* D floats:    K token mean (written if k_smooth) */
     float* mu_q;      /* T_m*D floats: Q block means (q_smooth; else NULL) */
     float* qk_bias;   /* T_m*N floats: sm_scale * mu_Qi . (K_n - mu_K)
@@ -143,7 +138,8 @@ typedef struct sage_dotensors {
     float* delta;     /* N floats per head: rowsum(dO o O) */
     int8_t* dot;      /* C64P, N*D: codes of dO, bq-row blocks */
     float* sdo;       /* T_m floats: dO block scales */
-    uint16_t* dor;    /* R16H, N*D*2: dO re-laid as 16-bit row tiles */
+    int8_t* dor;      /* R32, N*D: dp_int8 only: dO's codes again, as row
+                         tiles (the ablation's dP operand); else NULL */
 } sage_dotensors;
 
 /* Bytes of workspace sage_quantize needs: the float64 column sums of K of
@@ -161,8 +157,9 @@ size_t sage_quantize_workspace_bytes(const sage_shape* shape);
  *   per block: s = f32(max|X| / 127); code = clamp(rint(f32(x / s)), +-127),
  *   half-to-even; a block of zeros gets s = 0 and zero codes.
  * Codes and scales are bit-identical to that definition.
- * Q, K, V: [B,H,N,D] 16-bit inputs.  out: every pointer must be set, except
- * mu_q and qk_bias, which must be NULL unless q_smooth (and set if it is).
+ * Q, K, V: [B,H,N,D] 16-bit inputs.  out: q, sq, k, sk, vt and sv must be
+ * set; mu_k with k_smooth; mu_q and qk_bias with q_smooth; rq and rk with
+ * qk_norm; vr with dp_int8 (each may be NULL otherwise).
  * workspace: sage_quantize_workspace_bytes() bytes, 8-byte aligned, any
  * content (every byte read is written first by the same call); may be NULL
  * when k_smooth is 0.  mu_K is summed in a fixed order (each 64-row block's
@@ -207,7 +204,8 @@ int sage_fwd(const sage_shape* shape, const sage_qtensors* qk, void* O, float* L
 /*
  * sage_bwd_pre — backward step (1): D_i = rowsum(dO o O) over the stored O
  * (summed exactly in float64, rounded once to float32), and per-block (bq
- * rows) INT8 quantisation of dO exactly as in sage_quantize.
+ * rows) INT8 quantisation of dO exactly as in sage_quantize.  out: delta, dot
+ * and sdo must be set; dor with dp_int8 (may be NULL otherwise).
  */
 int sage_bwd_pre(const sage_shape* shape, const void* O, const void* dO,
                  const sage_dotensors* out, sage_stream_t stream);
@@ -226,13 +224,15 @@ size_t sage_bwd_workspace_bytes(const sage_shape* shape);
  * dS = P o (dP - D); quantise dS per tile; dK += M(dS^T, Q^) s_dS s_Q
  * (+ (dS^T 1) mu_Q^T with q_smooth); then, in a second query-outer pass over
  * the stored dS codes, dQ += M(dS^, K^) s_dS s_K.  dQ and dK include
- * sm_scale.  dQ, dK, dV: [B,H,N,D] float32 outputs, each written exactly
- * once (no atomics, no clearing).  L is sage_fwd's output; dos is
- * sage_bwd_pre's.  workspace: sage_bwd_workspace_bytes() bytes, 16-byte
- * aligned, any content.
+ * sm_scale.  qk is sage_quantize's output, dos sage_bwd_pre's, L sage_fwd's.
+ * V, dO: the [B,H,N,D] 16-bit tensors given to sage_quantize and
+ * sage_bwd_pre (dP is formed from their values).  dQ, dK, dV: [B,H,N,D]
+ * float32 outputs, each written exactly once (no atomics, no clearing).
+ * workspace: sage_bwd_workspace_bytes() bytes, 16-byte aligned, any content.
  */
-int sage_bwd(const sage_shape* shape, const sage_qtensors* qk, const sage_dotensors* dos,
-             const float* L, void* workspace, float* dQ, float* dK, float* dV, sage_stream_t stream);
+int sage_bwd(const sage_shape* shape, const sage_qtensors* qk, const sage_dotensors* dos, const void* V,
+             const void* dO, const float* L, void* workspace, float* dQ, float* dK, float* dV,
+             sage_stream_t stream);
 
 /*
  * sage_qk_norm_bwd — the gradient through QK-norm (shape->qk_norm = 1), in

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_struct_layouts_match_header():
     assert ctypes.sizeof(bd.c_shape) == 15 * 4
-    assert ctypes.sizeof(bd.c_qtensors) == 14 * 8
+    assert ctypes.sizeof(bd.c_qtensors) == 12 * 8
     assert ctypes.sizeof(bd.c_dotensors) == 4 * 8
 
 
@@ -97,7 +97,8 @@ def test_bad_shapes_rejected_by_every_call(lib, kw, code):
     assert lib.sage_quantize(ctypes.byref(s), FAKE, FAKE, FAKE, ctypes.byref(qt), FAKE, None) == code
     assert lib.sage_fwd(ctypes.byref(s), ctypes.byref(qt), FAKE, FAKE, None) == code
     assert lib.sage_bwd_pre(ctypes.byref(s), FAKE, FAKE, ctypes.byref(dot), None) == code
-    assert lib.sage_bwd(ctypes.byref(s), ctypes.byref(qt), ctypes.byref(dot), FAKE, FAKE, FAKE, FAKE, FAKE, None) == code
+    assert lib.sage_bwd(ctypes.byref(s), ctypes.byref(qt), ctypes.byref(dot), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                        FAKE, None) == code
     assert lib.sage_cast_grads(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == code
     assert lib.sage_quantize_workspace_bytes(ctypes.byref(s)) == 0
     assert lib.sage_bwd_workspace_bytes(ctypes.byref(s)) == 0
@@ -109,7 +110,7 @@ def test_null_shape(lib):
 
 @pytest.mark.parametrize("field", bd.QT_FIELDS)
 def test_missing_or_misaligned_qtensor(lib, field):
-    s = _shape(q_smooth=1, qk_norm=1)   # every field required
+    s = _shape(q_smooth=1, qk_norm=1, dp_int8=1)   # every field required
     for bad in (None, FAKE + 4):
         qt = _qt(**{field: bad})
         assert lib.sage_fwd(ctypes.byref(s), ctypes.byref(qt), FAKE, FAKE, None) == bd.SAGE_EINVAL
@@ -126,11 +127,19 @@ def test_qsmooth_buffers_only_needed_with_qsmooth(lib):
 
 @pytest.mark.parametrize("field", bd.DO_FIELDS)
 def test_missing_dotensor(lib, field):
-    s = _shape()
+    s = _shape(dp_int8=1)   # every field required (dor only with the INT8-dP ablation)
     dot = _dot(**{field: None})
     assert lib.sage_bwd_pre(ctypes.byref(s), FAKE, FAKE, ctypes.byref(dot), None) == bd.SAGE_EINVAL
-    assert lib.sage_bwd(ctypes.byref(s), ctypes.byref(_qt()), ctypes.byref(dot), FAKE, FAKE, FAKE, FAKE, FAKE,
-                        None) == bd.SAGE_EINVAL
+    assert lib.sage_bwd(ctypes.byref(s), ctypes.byref(_qt()), ctypes.byref(dot), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                        FAKE, None) == bd.SAGE_EINVAL
+
+
+def test_ablation_buffers_required_only_with_dp_int8(lib):
+    """vr and dor hold the INT8-dP ablation's row-tile codes: with dp_int8 a
+    missing one is refused on the host (the method's path never reads them)."""
+    s = _shape(dp_int8=1)
+    assert lib.sage_fwd(ctypes.byref(s), ctypes.byref(_qt(vr=None)), FAKE, FAKE, None) == bd.SAGE_EINVAL
+    assert lib.sage_bwd_pre(ctypes.byref(s), FAKE, FAKE, ctypes.byref(_dot(dor=None)), None) == bd.SAGE_EINVAL
 
 
 def test_io_pointers_checked(lib):
@@ -141,8 +150,14 @@ def test_io_pointers_checked(lib):
     assert lib.sage_quantize(ctypes.byref(s), FAKE, FAKE, FAKE, qt, FAKE + 4, None) == bd.SAGE_EINVAL
     assert lib.sage_fwd(ctypes.byref(s), qt, FAKE + 2, FAKE, None) == bd.SAGE_EINVAL
     assert lib.sage_fwd(ctypes.byref(s), qt, FAKE, None, None) == bd.SAGE_EINVAL
-    assert lib.sage_bwd(ctypes.byref(s), qt, ctypes.byref(_dot()), FAKE, None, FAKE, FAKE, FAKE, None) == bd.SAGE_EINVAL
-    assert lib.sage_bwd(ctypes.byref(s), qt, ctypes.byref(_dot()), FAKE, FAKE, None, FAKE, FAKE, None) == bd.SAGE_EINVAL
+    dot = ctypes.byref(_dot())
+    # sage_bwd(shape, qk, dos, V, dO, L, workspace, dQ, dK, dV, stream): each pointer checked
+    for k in range(7):
+        args = [FAKE] * 7
+        args[k] = None
+        assert lib.sage_bwd(ctypes.byref(s), qt, dot, *args, None) == bd.SAGE_EINVAL, k
+        args[k] = FAKE + 2
+        assert lib.sage_bwd(ctypes.byref(s), qt, dot, *args, None) == bd.SAGE_EINVAL, k
 
 
 def test_empty_problem_is_a_no_op(lib):
@@ -152,7 +167,7 @@ def test_empty_problem_is_a_no_op(lib):
         assert lib.sage_quantize(ctypes.byref(s), None, None, None, None, None, None) == bd.SAGE_OK
         assert lib.sage_fwd(ctypes.byref(s), None, None, None, None) == bd.SAGE_OK
         assert lib.sage_bwd_pre(ctypes.byref(s), None, None, None, None) == bd.SAGE_OK
-        assert lib.sage_bwd(ctypes.byref(s), None, None, None, None, None, None, None, None) == bd.SAGE_OK
+        assert lib.sage_bwd(ctypes.byref(s), None, None, None, None, None, None, None, None, None, None) == bd.SAGE_OK
 
 
 def test_cast_grads_checks(lib):
@@ -189,7 +204,7 @@ def test_workspace_size_and_strings(lib):
 
 def test_layout_offsets_are_permutations():
     import numpy as np
-    for kind in ("R32", "C64P", "C64N", "R16H"):
+    for kind in ("R32", "C64P"):
         for N, D in ((64, 64), (128, 128), (192, 64)):
             off = bd.layout_offsets(kind, N, D)
             assert np.array_equal(np.sort(off.ravel()), np.arange(N * D)), (kind, N, D)
