@@ -334,21 +334,31 @@ __global__ __launch_bounds__(kThreads) void quant_q_kernel(const u16* __restrict
 
 // K blocks (64 rows): K_sm = f32(K - mu_K) (mu_K from kmean_kernel); codes
 // -> k (R32).  With Q-smoothing, also the logit bias of these keys
-// for every query block: bias[i][n] = scale * sum_c mu_Q[i][c] * K_sm[n][c]
-// (float64 accumulation, rounded once).  QS: Q-smoothing on (qk_bias set);
-// only then does the block hold its smoothed rows in LDS.
+// for every query block that sees them: bias[i][n] = scale * sum_c mu_Q[i][c]
+// * K_sm[n][c] (exact float64 products and float64 sums, rounded once).  QS:
+// Q-smoothing on (qk_bias set); only then does the block hold its smoothed
+// rows in LDS.
 template <bool BF16, int D, bool QS>
 __global__ __launch_bounds__(kThreads) void quant_k_kernel(
     const u16* __restrict__ K, int N, int8_t* __restrict__ k,
     float* __restrict__ sk, const float* __restrict__ mu_k, int k_smooth,
     const float* __restrict__ mu_q, float* __restrict__ qk_bias, int Tm, double scale, float* __restrict__ rk,
-    int fp8) {
+    int fp8, int causal) {
     constexpr int R = 64;
     using B = Blk<R, D>;
     __shared__ float red[4];
     __shared__ __align__(16) uint8_t codes[R * CStride<D>];
     __shared__ float mu[D];
-    __shared__ float ksm[QS ? R : 1][QS ? D + 1 : 1];
+    // K_sm rows; once each wave holds its keys' values in registers, the
+    // same LDS takes two stages of a 16-row tile of mu_Q (Q-smoothing bias),
+    // whose padding puts the A-operand reads (16 rows x 4 consecutive
+    // channels per instruction) on 64 distinct banks
+    constexpr int KSM_FLOATS = QS ? R * (D + 1) : 1;
+    constexpr int MUQ_FLOATS = QS ? 2 * 16 * (D + 4) : 1;
+    static_assert(MUQ_FLOATS <= KSM_FLOATS, "the mu_Q stages reuse the K_sm rows");
+    __shared__ __align__(16) float ksm_raw[KSM_FLOATS];
+    auto ksm = reinterpret_cast<float(*)[QS ? D + 1 : 1]>(ksm_raw);
+    auto muq = reinterpret_cast<float(*)[16][QS ? D + 4 : 1]>(ksm_raw);
     const int j = blockIdx.x, bh = blockIdx.y;
     const size_t head = (size_t)bh * N * D;
     const int row0 = j * R;
@@ -389,29 +399,79 @@ __global__ __launch_bounds__(kThreads) void quant_k_kernel(
     store_codes<R32, R, D>(codes, k + head + (size_t)row0 * D);
 
     if constexpr (QS) {
-        // thread -> (key n = t % 64, query blocks i = t / 64 + 4 r + 32 pass,
-        // r = 0..7): eight independent float64 sums per thread, each taken over
-        // c in order; the wave's mu_Q rows are wave-uniform reads
-        constexpr int RB = 8;
-        const int n = threadIdx.x & 63;
+        // The bias tile mu_Q (query blocks x D) . K_sm^T (D x the block's 64
+        // keys) on the float64 matrix cores (v_mfma_f64_16x16x4_f64: exact
+        // products, float64 sums).  Wave w owns keys 16 w .. 16 w + 15, whose
+        // K_sm values stay in registers as the B operands of all D / 4
+        // contraction steps (lane l: key 16 w + l % 16, channels 4 k + l / 16).
+        // The workgroup walks the query blocks 16 at a time; each tile of mu_Q
+        // rows goes through LDS (two stages, the next tile's coalesced loads
+        // in flight during this tile's products) and gives the A operands
+        // (lane l: query block i0 + l % 16, the same channels).  Result
+        // register r of lane l is query block i0 + l / 16 + 4 r, key
+        // 16 w + l % 16 (the float64 product's row order: rows interleave over
+        // the lane groups).  Under causal masking only the query blocks from
+        // the first one that sees a key of the block's 128-key pair on are
+        // computed (the backward takes its key blocks in pairs from that
+        // query block on); no kernel reads the others.
+        constexpr int KS = D / 4;
+        constexpr int TL = 16 * D / 4 / kThreads;   // float4 loads per thread per tile
+        static_assert(TL >= 1 && 16 * D / 4 == TL * kThreads, "mu_Q tile shape");
+        const int lane = threadIdx.x & 63;
         const int wq = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-        for (int i0 = wq; i0 < Tm; i0 += 4 * RB) {
-            const float* mq[RB];
+        const int cl = lane >> 4, rl = lane & 15;
+        double bk[KS];
 #pragma unroll
-            for (int r = 0; r < RB; ++r) {
-                const int i = i0 + 4 * r < Tm ? i0 + 4 * r : i0;   // rows past the end repeat i0, not stored
-                mq[r] = mu_q + ((size_t)bh * Tm + i) * D;
+        for (int kk = 0; kk < KS; ++kk) bk[kk] = (double)ksm[16 * wq + rl][4 * kk + cl];
+        const int bq = N / Tm;
+        const int i_first = causal ? ((row0 >> 7) << 7) / bq : 0;
+        const int ntiles = (Tm - i_first + 15) / 16;
+        typedef double v4d __attribute__((ext_vector_type(4)));
+        const float* mqh = mu_q + (size_t)bh * Tm * D;
+        // thread t's share of a tile: float4 number t + kThreads u, i.e. row
+        // (t + kThreads u) / (D / 4), channels 4 ((t + kThreads u) % (D / 4))..
+        auto fetch = [&](int i0, v4f (&buf)[TL]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int u = 0; u < TL; ++u) {
+                const int f = threadIdx.x + kThreads * u;
+                const int row = i0 + f / (D / 4);
+                buf[u] = row < Tm ? *reinterpret_cast<const v4f*>(mqh + (size_t)row * D + 4 * (f % (D / 4)))
+                                  : v4f{0.f, 0.f, 0.f, 0.f};
             }
-            double acc[RB] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
-#pragma unroll 8
-            for (int c = 0; c < D; ++c) {
-                const double kv = (double)ksm[n][c];
+        };
+        auto put = [&](int stage, const v4f (&buf)[TL]) __attribute__((always_inline)) {
 #pragma unroll
-                for (int r = 0; r < RB; ++r) acc[r] += (double)mq[r][c] * kv;
+            for (int u = 0; u < TL; ++u) {
+                const int f = threadIdx.x + kThreads * u;
+                *reinterpret_cast<v4f*>(&muq[stage][f / (D / 4)][4 * (f % (D / 4))]) = buf[u];
             }
+        };
+        v4f pre[TL];
+        if (ntiles > 0) fetch(i_first, pre);
+        __syncthreads();   // every wave holds its K_sm values: the rows' LDS takes the mu_Q stages
+        if (ntiles > 0) put(0, pre);
+        __syncthreads();
+        for (int t = 0; t < ntiles; ++t) {
+            const int i0 = i_first + 16 * t;
+            if (t + 1 < ntiles) fetch(i0 + 16, pre);
+            // four independent accumulation chains over the contraction
+            // steps (kk % 4), added at the end: the products of one chain
+            // wait for each other, those of different chains do not
+            v4d acc4[4];
 #pragma unroll
-            for (int r = 0; r < RB; ++r)
-                if (i0 + 4 * r < Tm) qk_bias[((size_t)bh * Tm + i0 + 4 * r) * N + row0 + n] = (float)(acc[r] * scale);
+            for (int c4 = 0; c4 < 4; ++c4) acc4[c4] = v4d{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk)
+                acc4[kk & 3] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)muq[t & 1][rl][4 * kk + cl], bk[kk],
+                                                                     acc4[kk & 3], 0, 0, 0);
+            const v4d acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = i0 + cl + 4 * r;
+                if (i < Tm) qk_bias[((size_t)bh * Tm + i) * N + row0 + 16 * wq + rl] = (float)(acc[r] * scale);
+            }
+            if (t + 1 < ntiles) put((t + 1) & 1, pre);
+            __syncthreads();   // the next tile is in LDS; this one may be overwritten
         }
     }
 }
@@ -520,7 +580,7 @@ hipError_t quantize_impl(const Dims& d, const void* Q, const void* K, const void
     kq<<<dim3(d.Tn(), BH), blk, 0, s>>>(
         (const u16*)K, d.N, out.k, out.sk, out.mu_k, d.k_smooth ? 1 : 0,
         d.q_smooth ? out.mu_q : nullptr, d.q_smooth ? out.qk_bias : nullptr, d.Tm(), d.scale,
-        d.qk_norm ? out.rk : nullptr, d.fp8 ? 1 : 0);
+        d.qk_norm ? out.rk : nullptr, d.fp8 ? 1 : 0, d.causal ? 1 : 0);
     return hipGetLastError();
 }
 

@@ -127,7 +127,9 @@ typedef struct sage_qtensors {
     float* mu_k;      /* D floats:    K token mean (written if k_smooth) */
     float* mu_q;      /* T_m*D floats: Q block means (q_smooth; else NULL) */
     float* qk_bias;   /* T_m*N floats: sm_scale * mu_Qi . (K_n - mu_K)
-                         (q_smooth; else NULL) */
+                         (q_smooth; else NULL).  Causal: written only for
+                         query blocks i >= 128 floor(n / 128) / bq, the ones
+                         the attention kernels read; the rest is left as is */
     float* rq;        /* N floats: QK-norm factor r of each Q row (qk_norm;
                          else NULL) */
     float* rk;        /* N floats: the same for K (qk_norm; else NULL) */

@@ -174,7 +174,14 @@ def check_quantize(cfg, inputs, g, b, h):
         np.testing.assert_array_equal(qt["mu_q"][b, h], qz.mu_q.astype(np.float32))
         bias = np.stack([sage.qsmooth_bias(qz, i, j, shp) for i in range(shp.Tm) for j in range(shp.Tn)])
         bias = bias.reshape(shp.Tm, shp.Tn, cfg.bkv).reshape(shp.Tm, cfg.N)
-        np.testing.assert_allclose(qt["qk_bias"][b, h], bias, rtol=2e-6, atol=1e-6)
+        got = qt["qk_bias"][b, h]
+        if cfg.causal:
+            # written for query blocks from the first one that sees the key's
+            # 128-key pair on (include/sage.h)
+            first = (np.arange(cfg.N) // 128 * 128) // cfg.bq
+            keep = np.arange(shp.Tm)[:, None] >= first[None, :]
+            got, bias = got[keep], bias[keep]
+        np.testing.assert_allclose(got, bias, rtol=2e-6, atol=1e-6)
     return qz
 
 
