@@ -233,7 +233,9 @@ __global__ __launch_bounds__(64 * kWaves, 4) void fwd_kernel(
                 // logits are one positive scale times the integer sums, so the
                 // maximum is taken on the accumulator bits (which order like the
                 // sums); masked keys never win it.
-                float bias2[4][4];
+                // with Q-smoothing: the biased logits x = S c2 + bias log2 e,
+                // formed once and kept for the codes
+                float xq[4][4];
                 if (QSMOOTH) {
                     const float* brow = cur.bias[(16 * w) / bq];
                     rm = -INFINITY;
@@ -243,9 +245,8 @@ __global__ __launch_bounds__(64 * kWaves, 4) void fwd_kernel(
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             const int key = k0 + 16 * kb + 4 * g + r;
-                            bias2[kb][r] = (float)((double)b4[r] * kLog2e_d);
-                            const float v = fmaf(acc_value(s[kb][r]), c2, bias2[kb][r]);
-                            if (!(MASK && key > query)) rm = fmaxf(rm, v);
+                            xq[kb][r] = fmaf(acc_value(s[kb][r]), c2, b4[r] * kLog2e);
+                            if (!(MASK && key > query)) rm = fmaxf(rm, xq[kb][r]);
                         }
                     }
                     rm = qmax4(rm);
@@ -281,8 +282,7 @@ __global__ __launch_bounds__(64 * kWaves, 4) void fwd_kernel(
                     float ev[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        float x = QSMOOTH ? fmaf(acc_value(s[kb][r]), c2, bias2[kb][r] - shift)
-                                          : fmaf(acc_value(s[kb][r]), c2, -shift);
+                        float x = QSMOOTH ? xq[kb][r] - shift : fmaf(acc_value(s[kb][r]), c2, -shift);
                         if (MASK) {
                             const int key = k0 + 16 * kb + 4 * g + r;
                             if (key > query) x = -INFINITY;
