@@ -640,8 +640,10 @@ __global__ __launch_bounds__(512, 1) void bwd_kernel(
 // dQ_i = scale * sum_j s_dS,ij s_K,j M(dS^_ij, K^_j), one workgroup per query
 // tile; wave w owns the BQ/4 dS positions [w BQ/4, (w+1) BQ/4) (queries
 // 16 mb + 4 w + r) and all D columns.  Each key tile (its dS codes and the
-// K codes) streams through two alternating LDS stages filled one tile ahead
-// by asynchronous copies.  K's codes arrive as R32 row tiles (swizzled as the
+// K codes) streams through a ring of three LDS stages filled two tiles ahead
+// by asynchronous copies; the dS codes, read once, are copied with the
+// non-temporal hint so that they do not push the K codes (read again by every
+// query tile of the head) out of L2.  K's codes arrive as R32 row tiles (swizzled as the
 // backward's Q codes are) and are read transposed: column d of a product's B
 // operand is two transpose reads of eight keys.
 template <int BQ, int D>
@@ -662,7 +664,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const int8_t* __restrict__ d
     constexpr int K_BYTES = 64 * D;
     constexpr int ROUNDS = (DS_BYTES + K_BYTES) / 4096;
     static_assert((DS_BYTES + K_BYTES) % 4096 == 0 && DS_BYTES % 1024 == 0, "stage shape");
-    __shared__ __align__(16) DqStage<BQ, D> st[2];
+    __shared__ __align__(16) DqStage<BQ, D> st[3];
     using Stage = DqStage<BQ, D>;
     static_assert(offsetof(Stage, k) == DS_BYTES, "stage layout");
 
@@ -701,7 +703,11 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const int8_t* __restrict__ d
             dst[u] = base + c0;
             vo[u] = is_ds ? voff : voff_q;
         }
-        copy16_rounds<ROUNDS>(src, dst, vo);
+#pragma unroll
+        for (int u = 0; u < ROUNDS; ++u) {
+            if (u * 4096 + 4096 <= DS_BYTES) copy16x1_nt_to_lds(src[u], dst[u], vo[u]);
+            else copy16x1_to_lds(src[u], dst[u], vo[u]);
+        }
     };
 
     v4f acc[MBq][NB];
@@ -714,7 +720,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const int8_t* __restrict__ d
     auto step = [&](int j, DqStage<BQ, D>& cur, DqStage<BQ, D>& nxt) __attribute__((always_inline)) {
         const size_t t = (size_t)bh * tph + tile_index<BQ, CAUSAL>(i, j, Tn);
         const float cj = (float)((double)sds[t] * (double)sk[(size_t)bh * Tn + j] * scale);
-        if (j + 1 < jend) load(j + 1, nxt);
+        if (j + 2 < jend) load(j + 2, nxt);
         // A = dS^ rows (positions), k = keys 16 g + e, read transposed from the
         // key-major rows: two transpose reads of eight keys each
         v4i av[MBq];
@@ -749,14 +755,29 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const int8_t* __restrict__ d
                 }
             }
         }
-        wait_vmem();       // the asynchronous copies are not seen by the compiler's waits
-        __syncthreads();   // next tile landed for every wave; `cur` may be overwritten
+        // tile j + 1 has landed once only tile j + 2's copies (ROUNDS per
+        // wave, the only vector memory operations of the loop) may be in
+        // flight; the compiler's own waits do not see these copies
+        if (j + 2 < jend) wait_vmem_leave<ROUNDS>();
+        else wait_vmem();
+        __syncthreads();   // tile j + 1 landed for every wave; stage j may be overwritten
     };
 
     load(0, st[0]);
-    wait_vmem();       // the asynchronous copies are not seen by the compiler's waits
+    if (1 < jend) {
+        load(1, st[1]);
+        wait_vmem_leave<ROUNDS>();
+    } else {
+        wait_vmem();
+    }
     __syncthreads();
-    for (int j = 0; j < jend; ++j) step(j, st[j & 1], st[(j & 1) ^ 1]);
+    // stage of tile j: j mod 3; tile j + 2 goes to the stage tile j - 1 used
+    int cur = 0, ahead = 2;
+    for (int j = 0; j < jend; ++j) {
+        step(j, st[cur], st[ahead]);
+        cur = cur == 2 ? 0 : cur + 1;
+        ahead = ahead == 2 ? 0 : ahead + 1;
+    }
     // position p = QPW w + 16 mb + 4 g + r  ->  query 64 mb + 16 g + 4 w + r
     float* out = dQ + head + (size_t)(i * BQ) * D;
 #pragma unroll

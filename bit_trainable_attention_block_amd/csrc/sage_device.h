@@ -134,6 +134,14 @@ __device__ __forceinline__ void copy16_to_lds(const void* src, void* lds_wave) {
         : "memory");
 }
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N vector memory operations of this wave are in flight
+// (they complete in issue order for this count): with N the copies of the
+// newest tile, every older tile has landed.
+template <int N>
+__device__ __forceinline__ void wait_vmem_leave() {
+    static_assert(N >= 0 && N < 64, "vmcnt field");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // LDS byte address of a __shared__ object (the value M0 takes for a copy).
 template <typename T>
@@ -150,6 +158,19 @@ __device__ __forceinline__ void copy16x1_to_lds(const void* s0, unsigned l0, uns
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
         "s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %3, %2\n\ts_nop 0\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(l0), "s"(s0), "v"(voff)
+        : "memory");
+}
+// copy16x1_to_lds with the non-temporal hint, for data read exactly once (the
+// backward's dS workspace): its lines then leave L2 first and do not push out
+// operands that other workgroups read again.
+__device__ __forceinline__ void copy16x1_nt_to_lds(const void* s0, unsigned l0, unsigned voff) {
+    unsigned saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %3, %2 nt\n\ts_nop 0\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
         : "s"(l0), "s"(s0), "v"(voff)
