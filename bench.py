@@ -61,20 +61,37 @@ def measured_traffic(call: str):
 
 SQ_FILE = os.path.join(ROOT, "profiles", "sq_utilisation.json")
 SQ_KERNELS = ("fwd_kernel", "bwd_kernel", "dq_kernel")
+# VALU instruction classes counted separately on gfx950 (a third counter run)
+SQ_VALU_CLASSES = ("SQ_INSTS_VALU_ADD_F32", "SQ_INSTS_VALU_MUL_F32", "SQ_INSTS_VALU_FMA_F32",
+                   "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_VALU_CVT", "SQ_INSTS_VALU_INT32", "SQ_INSTS_VALU_INT64")
+HEADLINE_WORKLOAD = "d128_n8k_causal_qknorm"
 
 
-def sq_from(directory, out_path=SQ_FILE):
+def full_size_workloads():
+    """The full-size workloads of the sweep, by name."""
+    from bit_trainable_attention_block_amd import workloads as wl
+    return {c.name: c for c in (wl.C2, wl.C2_CAUSAL, wl.C3, *wl.C4, wl.C5, wl.C5_QSMOOTH)}
+
+
+def sq_file(workload):
+    return SQ_FILE if workload == HEADLINE_WORKLOAD else os.path.join(ROOT, "profiles", f"sq_utilisation_{workload}.json")
+
+
+def sq_from(directory, workload=HEADLINE_WORKLOAD, out_path=None):
     """Write profiles/sq_utilisation.json (or out_path; and print its table rows) from
     rocprofv3 --pmc runs of one bench step under `directory` holding the SQ
     counters below.  Derived per kernel, with T = GRBM_GUI_ACTIVE / 8 (the
     counter is summed over the eight XCDs), 1024 SIMDs and 256 CUs: VALU issue
     busy = 4 cycles x SQ_INSTS_VALU (MFMA included) per SIMD over T; MFMA busy
     = SQ_VALU_MFMA_BUSY_CYCLES per SIMD over T; LDS busy = SQ_LDS_IDX_ACTIVE
-    per CU over T; instructions per 64 unmasked (query, key) pairs of the
-    d=128 N=8192 causal workload."""
+    per CU over T; resident waves per SIMD = 4 SQ_WAVE_CYCLES / (1024 T)
+    (the counter advances once per four cycles of each resident wave: the
+    backward's two-wave workgroups read 1.84, its launch limit being 2);
+    instructions per 64 unmasked (query, key) pairs of `workload` (one
+    bench step of it), with the VALU classes of SQ_VALU_CLASSES when a run
+    holds them ("other" = VALU minus MFMA minus those classes)."""
     import csv
     import glob
-    from bit_trainable_attention_block_amd import workloads as wl
     sums = {}
     for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
         for r in csv.DictReader(open(path)):
@@ -83,7 +100,8 @@ def sq_from(directory, out_path=SQ_FILE):
             if name in SQ_KERNELS:
                 d = sums.setdefault(name, {})
                 d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
-    cfg = wl.C3
+    cfg = full_size_workloads()[workload]
+    out_path = out_path or sq_file(workload)
     pairs64 = cfg.attention_ops()[0] / (4 * cfg.D) / 64
     out = {}
     for k in SQ_KERNELS:
@@ -101,8 +119,13 @@ def sq_from(directory, out_path=SQ_FILE):
             "mfma_per_64_pairs": v["SQ_INSTS_MFMA"] / pairs64,
             "exp_per_64_pairs": v["SQ_INSTS_VALU_TRANS_F32"] / pairs64,
             "salu_per_64_pairs": v["SQ_INSTS_SALU"] / pairs64,
+            "resident_waves_per_simd": 4 * v["SQ_WAVE_CYCLES"] / (1024 * T),
         }
-    doc = {"source_hash": kernel_source_hash(), "workload": "d128_n8k_causal_qknorm", "kernels": out}
+        if all(c in v for c in SQ_VALU_CLASSES):
+            cls = {c[len("SQ_INSTS_VALU_"):]: v[c] / pairs64 for c in SQ_VALU_CLASSES}
+            cls["other"] = out[k]["valu_per_64_pairs"] - sum(cls.values())
+            out[k]["valu_classes_per_64_pairs"] = cls
+    doc = {"source_hash": kernel_source_hash(), "workload": workload, "kernels": out}
     os.makedirs(os.path.dirname(out_path), exist_ok=True)
     with open(out_path, "w") as f:
         json.dump(doc, f, indent=1)
@@ -110,7 +133,10 @@ def sq_from(directory, out_path=SQ_FILE):
         print(f"| `{k}` | {d['cycles']/1e6:.3f} | {d['valu_issue_busy']:.0%} | {d['mfma_busy']:.1%} | "
               f"{d['mfma_valu_coexec']:.1%} | {d['lds_busy']:.1%} | {d['waves_waiting_on_dependency']:.0%} | "
               f"{d['waves_issuing']:.0%} | {d['valu_per_64_pairs']:.1f} | {d['mfma_per_64_pairs']:.2f} | "
-              f"{d['exp_per_64_pairs']:.2f} | {d['salu_per_64_pairs']:.1f} |")
+              f"{d['exp_per_64_pairs']:.2f} | {d['salu_per_64_pairs']:.1f} | {d['resident_waves_per_simd']:.2f} |")
+    for k, d in out.items():
+        if "valu_classes_per_64_pairs" in d:
+            print(f"| `{k}` | " + " | ".join(f"{n} {x:.2f}" for n, x in d["valu_classes_per_64_pairs"].items()) + " |")
     return doc
 
 
@@ -319,7 +345,7 @@ def copy_gbps(mib=512, reps=5):
     return 2 * n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
 
-def sweep(steps, warmup):
+def sweep(steps, warmup, only=None):
     """One JSON line per full-size workload (not the default headline line):
     the four calls' mean times (HIP events on the launch stream) and the
     forward, backward and whole-step TOPS in the FlashAttention convention."""
@@ -332,7 +358,9 @@ def sweep(steps, warmup):
         sys.exit(1)
     bd.load()
     stream = torch.cuda.current_stream()
-    for cfg in (wl.C2, wl.C2_CAUSAL, wl.C3, *wl.C4, wl.C5, wl.C5_QSMOOTH):
+    for name, cfg in full_size_workloads().items():
+        if only and name != only:
+            continue
         sh = bd.Shape.of(cfg)
         x = wl.generate(cfg)
         Q, K, V, dO = (torch.from_numpy(x[n]["bits"].view(np.int16)).to("cuda").view(sh.torch_dtype)
@@ -384,6 +412,9 @@ def main():
                          "profiles/sq_utilisation.json (no GPU needed) and exit")
     ap.add_argument("--sweep", action="store_true",
                     help="one JSON line of call times and TOPS per full-size workload, then exit")
+    ap.add_argument("--workload", default="",
+                    help="with --sweep: only this full-size workload (a profiler run of its kernels); "
+                         "with --sq-from: the workload the counter runs were taken on")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run one plain device-to-device copy of this many MiB (the known-size "
                          "reference that scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -392,10 +423,13 @@ def main():
         traffic_from(args.traffic_from, 1024 << 20)
         return
     if args.sq_from:
-        sq_from(args.sq_from)
+        sq_from(args.sq_from, args.workload or HEADLINE_WORKLOAD)
         return
     if args.sweep and args.gpus == 1:
-        sweep(args.steps, args.warmup)
+        if args.workload and args.workload not in full_size_workloads():
+            print(f"bench.py: unknown workload {args.workload}", file=sys.stderr)
+            sys.exit(2)
+        sweep(args.steps, args.warmup, args.workload or None)
         return
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
