@@ -14,7 +14,8 @@
 //   code = clamp(rint(f32(x / s)), -127, 127), ties to even;
 // in the E4M3 variant s = f32(max|x| / 448) and the code is the nearest E4M3
 // value of f32(x / s), ties to even (v_cvt_pk_fp8_f32 rounds that way).
-// Hence __fdiv_rn / __fsub_rn and no fast-math anywhere in this file.
+// Hence __fdiv_rn / __fsub_rn, the exact float64 form of f32(x / s) in
+// codes_to_lds, and no fast-math anywhere in this file.
 #include "sage_device.h"
 #include "sage_internal.h"
 
@@ -133,6 +134,17 @@ __device__ __forceinline__ void codes_to_lds(const float (&x)[Blk<R, D>::PER_T][
     using B = Blk<R, D>;
     const int t = threadIdx.x;
     const int cc = t % B::CPR;
+    // x / s correctly rounded to float32 without a division per element.
+    // With r = RN64(1/s) (one division per block), RN64(x r) lies within
+    // 2^-52 (relative) of x / s.  A quotient of two float32 values is never
+    // within 2^-49 of a float32 rounding midpoint: a midpoint m has 25
+    // significant bits, so x - m s is a nonzero multiple of a power of two no
+    // smaller than 2^-49 |x|.  Rounding RN64(x r) to float32 is therefore
+    // RN32(x / s) exactly.  A zero block (s = 0) gets r = 0 and zero codes.
+    const double r = s > 0.f ? __ddiv_rn(1.0, (double)s) : 0.0;
+    auto quot = [r](float v) __attribute__((always_inline)) {
+        return __double2float_rn(__dmul_rn((double)v, r));
+    };
 #pragma unroll
     for (int k = 0; k < B::PER_T; ++k) {
         int row = t / B::CPR + k * B::RSTEP;
@@ -140,13 +152,13 @@ __device__ __forceinline__ void codes_to_lds(const float (&x)[Blk<R, D>::PER_T][
         if (fp8) {
             float v[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = s > 0.f ? __fdiv_rn(x[k][e], s) : 0.f;
+            for (int e = 0; e < 8; ++e) v[e] = quot(x[k][e]);
             w.x = (uint32_t)pack_e4m3(v[0], v[1], v[2], v[3]);
             w.y = (uint32_t)pack_e4m3(v[4], v[5], v[6], v[7]);
         } else {
             int c[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) c[e] = s > 0.f ? code_i8(__fdiv_rn(x[k][e], s)) : 0;
+            for (int e = 0; e < 8; ++e) c[e] = code_i8(quot(x[k][e]));
             w.x = pack4(c[0], c[1], c[2], c[3]);
             w.y = pack4(c[4], c[5], c[6], c[7]);
         }
