@@ -246,17 +246,26 @@ def _cpu_head(args):
     return t1 - t0, t2 - t1, start, end
 
 
-def cpu_baseline(cfg):
+def sample_heads(cfg, n):
+    """n (batch, head) pairs spread evenly over the workload's B*H heads."""
+    total = cfg.B * cfg.H
+    n = min(n, total)
+    return [divmod(k * total // n, cfg.H) for k in range(n)]
+
+
+def cpu_baseline(cfg, heads=None):
     """The oracle as it stands on whole heads of the workload, one head per
     worker process (single BLAS thread each), the workers started before
     anything touches the GPU.  value = attention ops of the sampled heads
     over the wall-clock span from the first worker's start to the last
-    worker's end of that work (input generation and imports excluded)."""
+    worker's end of that work (input generation and imports excluded).
+    heads: the (batch, head) pairs to time; by default the fixed sample of
+    the d=128 N=8192 causal workload, as many as there are workers."""
     import multiprocessing as mp
 
     cpus = len(os.sched_getaffinity(0))
     workers = max(1, min(CPU_WORKERS_MAX, cpus))
-    heads = CPU_HEADS[:workers]
+    heads = CPU_HEADS[:workers] if heads is None else heads[:workers]
     fwd_ops, bwd_ops = (v / (cfg.B * cfg.H) for v in cfg.attention_ops())
     with mp.get_context("spawn").Pool(workers) as pool:
         pool.map(abs, range(workers))          # interpreters up
@@ -271,6 +280,19 @@ def cpu_baseline(cfg):
             "fwd_tops_per_core": fwd_ops * n / tf / 1e12, "bwd_tops_per_core": bwd_ops * n / tb / 1e12,
             "fwd_cpu_s": round(tf, 2), "bwd_cpu_s": round(tb, 2),
             "host_cpus": os.cpu_count(), "affinity_cpus": cpus, "blas_threads": 1}
+
+
+def cpu_sweep():
+    """One JSON line per workload configuration (tiny, d=64 N=2048, d=128
+    N=8192 causal, the sigma=1 member of the sigma sweep, N=32768 causal):
+    the oracle's whole chain on up to CPU_WORKERS_MAX heads spread over the
+    workload, fwd (quantize + fwd) and bwd (bwd_pre + bwd) CPU seconds and
+    TOPS in the same convention as the GPU figures."""
+    from bit_trainable_attention_block_amd import workloads as wl
+    for cfg in (wl.C1, wl.C2, wl.C3, wl.C4[0], wl.C5):
+        r = cpu_baseline(cfg, sample_heads(cfg, CPU_WORKERS_MAX))
+        print(json.dumps({"workload": cfg.name, "B": cfg.B, "H": cfg.H, "N": cfg.N, "D": cfg.D,
+                          "causal": cfg.causal, **r}), flush=True)
 
 
 def mfma_probe(kind="i8", iters=4000):
@@ -412,6 +434,9 @@ def main():
                          "profiles/sq_utilisation.json (no GPU needed) and exit")
     ap.add_argument("--sweep", action="store_true",
                     help="one JSON line of call times and TOPS per full-size workload, then exit")
+    ap.add_argument("--cpu-sweep", action="store_true",
+                    help="the oracle's CPU baseline on a bounded sample of heads of each of the five "
+                         "workload configurations (one JSON line each; no GPU needed), then exit")
     ap.add_argument("--workload", default="",
                     help="with --sweep: only this full-size workload (a profiler run of its kernels); "
                          "with --sq-from: the workload the counter runs were taken on")
@@ -424,6 +449,9 @@ def main():
         return
     if args.sq_from:
         sq_from(args.sq_from, args.workload or HEADLINE_WORKLOAD)
+        return
+    if args.cpu_sweep:
+        cpu_sweep()
         return
     if args.sweep and args.gpus == 1:
         if args.workload and args.workload not in full_size_workloads():

@@ -107,3 +107,17 @@ def test_backward_roofline_prices_each_product_at_its_own_peak():
     assert abs(bench.mixed_ceiling_tops(w) - 5 / (4 / 5000 + 1 / 2500)) < 1e-9
     assert abs(bench.mixed_ceiling_tops(w) - 4166.67) < 0.01
     assert bench.bwd_pre_algo_bytes(128) == 5.03125 and bench.QUANT_ALGO_BYTES == 11.0
+
+
+def test_cpu_sweep_head_sample_is_spread_and_valid():
+    """The CPU sweep's head sample: distinct (batch, head) pairs inside the
+    workload, evenly spread, all heads when there are fewer than asked."""
+    sys.path.insert(0, ROOT)
+    import bench
+    from bit_trainable_attention_block_amd import workloads as wl
+    for cfg in (wl.C1, wl.C2, wl.C3, wl.C4[0], wl.C5):
+        hs = bench.sample_heads(cfg, 16)
+        assert len(hs) == min(16, cfg.B * cfg.H) == len(set(hs))
+        assert all(0 <= b < cfg.B and 0 <= h < cfg.H for b, h in hs)
+    assert bench.sample_heads(wl.C2, 16)[:5] == [(0, 0), (0, 4), (0, 8), (0, 12), (1, 0)]   # 64 heads, step 4
+    assert bench.sample_heads(wl.C5, 16) == [(0, h) for h in range(8)]                        # all 8
