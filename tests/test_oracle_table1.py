@@ -12,8 +12,8 @@ non-causal, K-smoothing on, Q-smoothing off) is run here at a reduced size
 
 At sigma = 1 the per-tile quantisation of P and dS in the backward pass (one
 scale per 128 x 64 tile) dominates dQ, dK and dV; those errors come out about
-3x the table's, so the survey's "O tracks dV" holds here only from sigma = 3
-on.  tests/test_oracle_granularity.py pins the account: the same backward
+3x the table's, so "O tracks dV" (the table's pattern at every sigma) holds
+here only from sigma = 3 on.  tests/test_oracle_granularity.py pins the account: the same backward
 with per-row P and dS scales reproduces the table's sigma = 1 row, and
 smaller tiles close the gap monotonically while O stays put.
 """
