@@ -288,7 +288,7 @@ __global__ __launch_bounds__(512) void kmean_kernel(const double* __restrict__ k
 
 // Q blocks (BQ rows): optional Q-smoothing (QS, mu_q set), codes -> q (R32).
 // Only with QS does the block hold the column-sum scratch.
-template <bool BF16, int D, int BQ, bool QS>
+template <bool BF16, int D, int BQ, bool QS, bool QKN>
 __global__ __launch_bounds__(kThreads) void quant_q_kernel(const u16* __restrict__ Q, int N,
                                                            int8_t* __restrict__ q,
                                                            float* __restrict__ sq,
@@ -310,7 +310,7 @@ __global__ __launch_bounds__(kThreads) void quant_q_kernel(const u16* __restrict
     load_block<BQ, D>(Q + head + (size_t)row0 * D, raw);
 #pragma unroll
     for (int k = 0; k < B::PER_T; ++k) unpack8<BF16>(raw[k], x[k]);
-    if (rq != nullptr) rms_normalize<BQ, D>(x, rq + (size_t)bh * N, row0);
+    if constexpr (QKN) rms_normalize<BQ, D>(x, rq + (size_t)bh * N, row0);
 
     if constexpr (QS) {
         double part[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -584,8 +584,16 @@ hipError_t quantize_impl(const Dims& d, const void* Q, const void* K, const void
         (const u16*)K, (const u16*)V, d.N, out.vt, out.sv, out.vr, ws, d.k_smooth ? 1 : 0, d.dp_int8 ? 1 : 0,
         d.qk_norm ? 1 : 0, d.fp8 ? 1 : 0);
     if (d.k_smooth) kmean_kernel<D><<<dim3(BH), dim3(512), 0, s>>>(ws, d.Tn(), d.N, out.mu_k);
-    auto qq = d.bq == 128 ? (d.q_smooth ? quant_q_kernel<BF16, D, 128, true> : quant_q_kernel<BF16, D, 128, false>)
-                          : (d.q_smooth ? quant_q_kernel<BF16, D, 64, true> : quant_q_kernel<BF16, D, 64, false>);
+    // fused QK-norm as a template switch: its float64 row sums would
+    // otherwise set the register count (and the occupancy) of every launch
+    auto qq = d.qk_norm ? (d.bq == 128 ? (d.q_smooth ? quant_q_kernel<BF16, D, 128, true, true>
+                                                    : quant_q_kernel<BF16, D, 128, false, true>)
+                                       : (d.q_smooth ? quant_q_kernel<BF16, D, 64, true, true>
+                                                     : quant_q_kernel<BF16, D, 64, false, true>))
+                        : (d.bq == 128 ? (d.q_smooth ? quant_q_kernel<BF16, D, 128, true, false>
+                                                    : quant_q_kernel<BF16, D, 128, false, false>)
+                                       : (d.q_smooth ? quant_q_kernel<BF16, D, 64, true, false>
+                                                     : quant_q_kernel<BF16, D, 64, false, false>));
     qq<<<dim3(d.Tm(), BH), blk, 0, s>>>((const u16*)Q, d.N, out.q, out.sq, d.q_smooth ? out.mu_q : nullptr,
                                         d.qk_norm ? out.rq : nullptr, d.fp8 ? 1 : 0);
     auto kq = d.q_smooth ? quant_k_kernel<BF16, D, true> : quant_k_kernel<BF16, D, false>;
