@@ -105,6 +105,25 @@ def test_degenerate_zero_blocks():
     gp.check_full_chain(cfg, x, g)
 
 
+def test_largest_head_count():
+    """B*H = 65535, the most heads the library takes (the quantisation grids
+    put the heads on their second dimension): small causal heads (N = 64,
+    d = 64), so every launch runs at its largest grid.  The first, a middle and
+    the last head against the oracle, and every output finite."""
+    cfg = small("heads65535_n64_d64_bq64_causal", 64, 64, 64, True, B=5, H=13107)
+    assert cfg.B * cfg.H == 65535
+    gp.say(f"[gpu] largest head count B={cfg.B} H={cfg.H} N={cfg.N} D={cfg.D} (input generation takes ~30 s)")
+    gp.CURRENT_CASE[0] = cfg.name
+    x = wl.generate(cfg)
+    g = gp.run_gpu(cfg, x)
+    for b, h in ((0, 0), (2, 6553), (4, 13106)):
+        qz = gp.check_quantize(cfg, x, g, b, h)
+        gp.check_fwd(cfg, x, g, b, h, qz, [0])
+        gp.check_bwd(cfg, x, g, b, h, qz, [0], [0])
+    for k in ("O", "L", "dQ", "dK", "dV"):
+        assert np.all(np.isfinite(g[k])), k
+
+
 FULL = [
     (wl.C2, [(0, 0), (3, 15)]),
     (wl.C2_CAUSAL, [(1, 7)]),
