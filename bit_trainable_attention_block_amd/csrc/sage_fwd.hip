@@ -296,7 +296,6 @@ __global__ __launch_bounds__(64 * kWaves, 4) void fwd_kernel(
                     }
                     pc[kb] = F8 ? pack_e4m3(ev[0], ev[1], ev[2], ev[3]) : (int)word;
                 }
-                sum = qsum4(sum);
             };
             // Diagonal tiles (some key after some query) take the masked
             // instantiation; every other tile runs without a compare.
@@ -318,6 +317,9 @@ __global__ __launch_bounds__(64 * kWaves, 4) void fwd_kernel(
 #pragma unroll
                 for (int db = 0; db < DB; ++db) o[db] *= alpha;
             }
+            // l is kept per lane group (this lane's 16 keys of each tile): sP
+            // and alpha are the same for the four groups of a query, so their
+            // shares are added once, after the last tile
             l = fmaf(sum, sP, l);
             m = m_new;
             const float beta = sP * sv[(size_t)bh * Tn + j];
@@ -340,18 +342,19 @@ __global__ __launch_bounds__(64 * kWaves, 4) void fwd_kernel(
 
     // O^T block db holds rows d = 16 db + 4 g + r of column (query) n
     if (active) {
+        const float lq = qsum4(l);   // the row sum: the four lane groups' shares
         u16* O = Out + head + (size_t)query * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
             u16 h[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) h[r] = from_f32<BF16>(__fdiv_rn(o[db][r], l));
+            for (int r = 0; r < 4; ++r) h[r] = from_f32<BF16>(__fdiv_rn(o[db][r], lq));
             uint2 pk;
             pk.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
             pk.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
             *reinterpret_cast<uint2*>(O + 16 * db + 4 * g) = pk;
         }
-        if (g == 0) L[(size_t)bh * N + query] = (m + (log2f(l) - kLog2Qmax)) * kLn2;
+        if (g == 0) L[(size_t)bh * N + query] = (m + (log2f(lq) - kLog2Qmax)) * kLn2;
     }
 }
 
